@@ -1,0 +1,162 @@
+"""Oracle page pool: the allocation policy the host library must reproduce exactly.
+
+The pages fix the structure (fixed-size blocks mapped through a per-sequence
+block table, copy-on-write sharing -- page "CacheFlow：基于 llama.cpp 的多请求 LLM
+推理优化引擎", section 2; a per-sequence page mapping plus true length -- page
+"面向多并发长上下文的 llama.cpp 分页式 KV Cache 与计算加速优化", section 作品简介;
+read-only shared prefixes with private suffixes and accounting over the union of
+physical cells -- page "面向边缘智能体推理的 llama.cpp KV Cache 共享与复用优化",
+section 主要功能与技术路线).  They leave the choice of *which* free page to use
+open; this model fixes it so block tables are unique:
+
+* the free list is a stack; initially ``free_order[0]`` is on top, so pages are
+  handed out in ``free_order`` order;
+* a page whose reference count drops to 0 is pushed on top (freed in logical
+  page order);
+* append fills the last page before taking a new one; if the last page is
+  shared (refcount > 1) and partially filled, appending first gives the
+  sequence a private copy of it (copy-on-write) and reports the (src, dst) pair;
+* fork shares every page of the source (refcount + 1 each);
+* cow of a logical page takes one new page, repoints the table entry, and drops
+  the old page's refcount; it is an error on an unshared page;
+* sequence ids are the smallest non-negative integer not in use;
+* a failing call leaves the pool unchanged.
+
+Pinned by invariants (page conservation, sharing only under refcount > 1,
+free-all restores every page, page counts with and without sharing) in
+tests/test_oracle.py.
+"""
+from __future__ import annotations
+
+from typing import Dict, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+
+class PoolError(Exception):
+    status = -1
+
+
+class InvalidError(PoolError):
+    status = -1
+
+
+class NoPagesError(PoolError):
+    status = -3
+
+
+class StateError(PoolError):
+    status = -4
+
+
+class AllocatorModel:
+    def __init__(self, num_pages: int, page_size: int, free_order: Optional[Sequence[int]] = None):
+        if num_pages < 1 or page_size < 1:
+            raise InvalidError("bad pool size")
+        order = list(range(num_pages)) if free_order is None else [int(x) for x in free_order]
+        if sorted(order) != list(range(num_pages)):
+            raise InvalidError("free_order must be a permutation of 0..N-1")
+        self.num_pages = num_pages
+        self.page_size = page_size
+        self.free: List[int] = order[::-1]          # top of stack = end of list
+        self.ref = [0] * num_pages
+        self.pages: Dict[int, List[int]] = {}
+        self.length: Dict[int, int] = {}
+
+    # -- helpers
+    def _pop(self) -> int:
+        return self.free.pop()
+
+    def _alive(self, seq: int):
+        if seq not in self.pages:
+            raise StateError(f"sequence {seq} is not live")
+
+    # -- API mirror
+    def seq_new(self) -> int:
+        sid = 0
+        while sid in self.pages:
+            sid += 1
+        self.pages[sid] = []
+        self.length[sid] = 0
+        return sid
+
+    def seq_append(self, seq: int, n_new: int) -> Tuple[np.ndarray, Optional[Tuple[int, int]]]:
+        self._alive(seq)
+        if n_new < 0:
+            raise InvalidError("n_new < 0")
+        P = self.page_size
+        L = self.length[seq]
+        pages = self.pages[seq]
+        if n_new == 0:
+            return np.zeros(0, dtype=np.int32), None
+        cow = bool(L % P) and self.ref[pages[-1]] > 1
+        need = (L + n_new + P - 1) // P - (L + P - 1) // P + (1 if cow else 0)
+        if need > len(self.free):
+            raise NoPagesError("pool exhausted")
+        pair = None
+        if cow:
+            src = pages[-1]
+            dst = self._pop()
+            self.ref[src] -= 1
+            self.ref[dst] = 1
+            pages[-1] = dst
+            pair = (src, dst)
+        slots = np.empty(n_new, dtype=np.int32)
+        for j in range(n_new):
+            t = L + j
+            if t % P == 0:
+                p = self._pop()
+                self.ref[p] = 1
+                pages.append(p)
+            slots[j] = pages[t // P] * P + t % P
+        self.length[seq] = L + n_new
+        return slots, pair
+
+    def seq_fork(self, src: int) -> int:
+        self._alive(src)
+        dst = self.seq_new()
+        self.pages[dst] = list(self.pages[src])
+        self.length[dst] = self.length[src]
+        for p in self.pages[dst]:
+            self.ref[p] += 1
+        return dst
+
+    def seq_cow(self, seq: int, logical_page: int) -> Tuple[int, int]:
+        self._alive(seq)
+        pages = self.pages[seq]
+        if logical_page < 0 or logical_page >= len(pages):
+            raise InvalidError("logical page out of range")
+        src = pages[logical_page]
+        if self.ref[src] < 2:
+            raise StateError("page is not shared")
+        if not self.free:
+            raise NoPagesError("pool exhausted")
+        dst = self._pop()
+        self.ref[src] -= 1
+        self.ref[dst] = 1
+        pages[logical_page] = dst
+        return src, dst
+
+    def seq_free(self, seq: int) -> None:
+        self._alive(seq)
+        for p in self.pages[seq]:
+            self.ref[p] -= 1
+            if self.ref[p] == 0:
+                self.free.append(p)
+        del self.pages[seq]
+        del self.length[seq]
+
+    def block_tables(self, seqs: Sequence[int], max_pages: int):
+        for s in seqs:
+            self._alive(s)
+            if len(self.pages[s]) > max_pages:
+                raise InvalidError("max_pages too small")
+        bt = np.full((len(seqs), max_pages), -1, dtype=np.int32)
+        kv = np.zeros(len(seqs), dtype=np.int32)
+        for i, s in enumerate(seqs):
+            bt[i, :len(self.pages[s])] = self.pages[s]
+            kv[i] = self.length[s]
+        return bt, kv
+
+    def stats(self):
+        return len(self.free), np.asarray(self.ref, dtype=np.int32)

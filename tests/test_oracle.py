@@ -1,0 +1,485 @@
+"""Pins for the CPU oracle (no GPU).
+
+The pages print no worked example, so each oracle function is pinned to
+something other than itself: a pure-Python brute force that walks the physical
+pool through inverted block tables, torch's float64 CPU attention on inputs
+that need no paging, hand-derived fixtures, closed forms and invariants.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+
+GOLD = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+# ----------------------------------------------------------------- brute force
+
+def brute_force(q, k_pool, v_pool, block_tables, token_row, token_kv_len, token_pos, scale):
+    """Scalar definition.  Inverts the block tables (physical cell -> (row, logical
+    position)) instead of gathering, then loops with math.fsum / math.exp."""
+    _, n_kv, P, D = k_pool.shape
+    T, n_q, _ = q.shape
+    G = n_q // n_kv
+    owner = {}
+    for r, row in enumerate(np.asarray(block_tables)):
+        for j, page in enumerate(row):
+            if page >= 0:
+                for s in range(P):
+                    owner.setdefault((int(page), s), []).append((r, j * P + s))
+    sc = float(np.float32(scale))
+    out = np.zeros((T, n_q, D))
+    for i in range(T):
+        r = int(token_row[i])
+        if r < 0:
+            continue
+        n = min(int(token_kv_len[i]), int(token_pos[i]) + 1)
+        cells = sorted((t, page, s) for (page, s), lst in owner.items()
+                       for (rr, t) in lst if rr == r and t < n)
+        assert [c[0] for c in cells] == list(range(n))
+        for h in range(n_q):
+            g = h // G
+            qv = [float(x) for x in q[i, h]]
+            z = [sc * math.fsum(qv[d] * float(k_pool[p, g, s, d]) for d in range(D))
+                 for (_, p, s) in cells]
+            m = max(z)
+            w = [math.exp(x - m) for x in z]
+            den = math.fsum(w)
+            for d in range(D):
+                out[i, h, d] = math.fsum(w[c] * float(v_pool[cells[c][1], g, d, cells[c][2]])
+                                         for c in range(n)) / den
+    return out
+
+
+def _small_prefill(seed=7, order="round_robin"):
+    rng = np.random.default_rng(seed)
+    case = W.make_prefill_case(rng, "small", 4, 2, 32, 16, 24, [20, 33, 5], [6, 4, 7], order)
+    k, v = oracle.reshape_and_cache(case.k_pool, case.v_pool, case.k_new, case.v_new,
+                                    case.slot_mapping)
+    return case, k, v
+
+
+def test_brute_force_tiny_decode():
+    c = W.tiny_decode()
+    got = oracle.paged_decode(c.q, c.k_pool, c.v_pool, c.block_tables, c.kv_lens, c.scale)
+    ref = brute_force(c.q, c.k_pool, c.v_pool, c.block_tables, np.arange(2), c.kv_lens,
+                      c.kv_lens - 1, c.scale)
+    assert np.all(np.isfinite(got))
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("order", ["round_robin", "grouped"])
+def test_brute_force_small_prefill(order):
+    c, k, v = _small_prefill(order=order)
+    got = oracle.paged_attention(c.q, k, v, c.block_tables, c.token_row, c.token_kv_len,
+                                 c.token_pos, c.scale)
+    ref = brute_force(c.q, k, v, c.block_tables, c.token_row, c.token_kv_len, c.token_pos,
+                      c.scale)
+    assert np.all(np.isfinite(got))
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-13)
+
+
+def test_brute_force_shared_pages():
+    """Two rows whose tables share their first page (a forked prefix)."""
+    rng = np.random.default_rng(11)
+    N, Hkv, P, D = 8, 1, 4, 16
+    k = rng.standard_normal((N, Hkv, P, D)).astype(np.float16)
+    v = rng.standard_normal((N, Hkv, D, P)).astype(np.float16)
+    bt = np.array([[6, 1, -1], [6, 3, 0]], dtype=np.int32)
+    q = rng.standard_normal((2, 2, D)).astype(np.float32)
+    lens = np.array([7, 10], dtype=np.int32)
+    got = oracle.paged_decode(q, k, v, bt, lens, 0.25)
+    ref = brute_force(q, k, v, bt, np.arange(2), lens, lens - 1, 0.25)
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-13)
+
+
+# ------------------------------------------------------------ golden fixtures
+
+def _hand_pool(g):
+    pool = g["pool"]
+    k, v = W.nan_pools(pool["num_pages"], pool["n_kv_heads"], pool["page_size"], pool["head_dim"])
+    for c in pool["cells"]:
+        for h in range(pool["n_kv_heads"]):
+            k[c["page"], h, c["slot"], :] = c["k"][h]
+            v[c["page"], h, :, c["slot"]] = c["v"][h]
+    return k, v, np.array(pool["block_table"], dtype=np.int32)
+
+
+def test_golden_attention_hand():
+    g = json.load(open(os.path.join(GOLD, "attention_hand.json")))
+    k, v, bt = _hand_pool(g)
+    for case in g["cases"]:
+        T = len(case["token_row"])
+        q = np.array([g["queries"]] * T, dtype=np.float32)
+        got = oracle.paged_attention(q, k, v, bt, case["token_row"], case["token_kv_len"],
+                                     case["token_pos"], g["scale"])
+        np.testing.assert_allclose(got, np.array(case["expected"], dtype=np.float64),
+                                   rtol=1e-15, atol=1e-15, err_msg=case["name"])
+
+
+# ------------------------------------------------------- torch float64 SDPA
+
+def _sdpa(q, K, V, G, scale, mask):
+    """q [T][Hq][D], K/V [n][Hkv][D] float64; mask bool [T][n] (True = visible)."""
+    qt = torch.from_numpy(q.astype(np.float64)).permute(1, 0, 2)[None]
+    kt = torch.from_numpy(K).permute(1, 0, 2).repeat_interleave(G, dim=0)[None]
+    vt = torch.from_numpy(V).permute(1, 0, 2).repeat_interleave(G, dim=0)[None]
+    o = torch.nn.functional.scaled_dot_product_attention(
+        qt, kt, vt, attn_mask=torch.from_numpy(mask), scale=float(np.float32(scale)))
+    return o[0].permute(1, 0, 2).numpy()
+
+
+@pytest.mark.parametrize("Hq,Hkv,D,L", [(4, 2, 64, 37), (8, 8, 32, 16), (32, 8, 128, 100)])
+def test_sdpa_single_page(Hq, Hkv, D, L):
+    """One sequence in one page (P >= L): no paging, so torch's attention applies."""
+    rng = np.random.default_rng(L)
+    P = 128
+    k = rng.standard_normal((3, Hkv, P, D)).astype(np.float16)
+    v = rng.standard_normal((3, Hkv, D, P)).astype(np.float16)
+    bt = np.array([[2]], dtype=np.int32)
+    T = 5
+    q = rng.standard_normal((T, Hq, D)).astype(np.float32)
+    pos = np.array([L - 1, L - 2, 0, L - 5, L - 1], dtype=np.int32)
+    got = oracle.paged_attention(q, k, v, bt, np.zeros(T, np.int32), np.full(T, L, np.int32),
+                                 pos, 1.0 / math.sqrt(D))
+    K = k[2, :, :L, :].transpose(1, 0, 2).astype(np.float64)
+    V = v[2, :, :, :L].transpose(2, 0, 1).astype(np.float64)
+    mask = np.arange(L)[None, :] <= pos[:, None]
+    ref = _sdpa(q, K, V, Hq // Hkv, 1.0 / math.sqrt(D), mask)
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-13)
+
+
+# ---------------------------------------------------------------- closed forms
+
+def _one_seq(rng, L, Hq=4, Hkv=2, D=16, P=8, N=12):
+    case = W.make_decode_case(rng, "cf", Hq, Hkv, D, P, [L], N)
+    return case
+
+
+def test_closed_form_single_key():
+    c = _one_seq(np.random.default_rng(1), 1)
+    out = oracle.paged_decode(c.q, c.k_pool, c.v_pool, c.block_tables, c.kv_lens, c.scale)
+    page = c.block_tables[0, 0]
+    for h in range(4):
+        np.testing.assert_array_equal(out[0, h], c.v_pool[page, h // 2, :, 0].astype(np.float64))
+
+
+def test_closed_form_zero_query_is_mean():
+    c = _one_seq(np.random.default_rng(2), 29)
+    q = np.zeros_like(c.q)
+    out = oracle.paged_decode(q, c.k_pool, c.v_pool, c.block_tables, c.kv_lens, c.scale)
+    # independent computation of the mean from the physical pool
+    P = 8
+    vals = np.stack([c.v_pool[c.block_tables[0, t // P], :, :, t % P] for t in range(29)])
+    for h in range(4):
+        np.testing.assert_allclose(out[0, h], vals[:, h // 2, :].astype(np.float64).mean(0),
+                                   rtol=1e-13, atol=1e-14)
+
+
+def test_closed_form_identical_keys_is_mean_and_constant_v():
+    rng = np.random.default_rng(3)
+    c = _one_seq(rng, 21)
+    valid = c.valid_cells
+    k = c.k_pool.copy()
+    # every valid cell of KV head g gets the same key row
+    for g in range(2):
+        row = rng.standard_normal(16).astype(np.float16)
+        kg = k[:, g]                                        # [N][P][D]
+        kg[valid] = row
+    out = oracle.paged_decode(c.q, k, c.v_pool, c.block_tables, c.kv_lens, c.scale)
+    vals = np.stack([c.v_pool[c.block_tables[0, t // 8], :, :, t % 8] for t in range(21)])
+    for h in range(4):
+        np.testing.assert_allclose(out[0, h], vals[:, h // 2].astype(np.float64).mean(0),
+                                   rtol=1e-13, atol=1e-14)
+    # constant V (value depends on the KV head) -> that constant, whatever the keys
+    v = c.v_pool.copy()
+    for g in range(2):
+        vg = v[:, g].transpose(0, 2, 1)                     # view [N][P][D]
+        vg[valid] = np.float16(0.5 * (g + 1))
+    out = oracle.paged_decode(c.q, c.k_pool, v, c.block_tables, c.kv_lens, c.scale)
+    for h in range(4):
+        np.testing.assert_allclose(out[0, h], 0.5 * (h // 2 + 1), rtol=1e-14)
+
+
+def test_gqa_equals_mha_with_repeated_kv_heads():
+    rng = np.random.default_rng(4)
+    c = W.make_decode_case(rng, "g", 8, 2, 16, 8, [13, 30], 16)
+    out = oracle.paged_decode(c.q, c.k_pool, c.v_pool, c.block_tables, c.kv_lens, c.scale)
+    G = 4
+    k_rep = np.repeat(c.k_pool, G, axis=1)
+    v_rep = np.repeat(c.v_pool, G, axis=1)
+    out_mha = oracle.paged_decode(c.q, k_rep, v_rep, c.block_tables, c.kv_lens, c.scale)
+    # BLAS may block a 4-row product differently from 1-row products: rounding only
+    np.testing.assert_allclose(out, out_mha, rtol=1e-13, atol=1e-15)
+
+
+# ------------------------------------------------------------------ invariants
+
+def test_page_permutation_bitwise():
+    c = W.tiny_decode()
+    out = oracle.paged_decode(c.q, c.k_pool, c.v_pool, c.block_tables, c.kv_lens, c.scale)
+    pi = np.random.default_rng(5).permutation(c.num_pages)   # old page p -> new id pi[p]
+    k2 = np.empty_like(c.k_pool)
+    v2 = np.empty_like(c.v_pool)
+    k2[pi] = c.k_pool
+    v2[pi] = c.v_pool
+    bt2 = np.where(c.block_tables >= 0, pi[np.maximum(c.block_tables, 0)], -1)
+    out2 = oracle.paged_decode(c.q, k2, v2, bt2, c.kv_lens, c.scale)
+    np.testing.assert_array_equal(out, out2)
+
+
+def test_nan_poison_does_not_change_output():
+    c = W.tiny_decode()
+    out = oracle.paged_decode(c.q, c.k_pool, c.v_pool, c.block_tables, c.kv_lens, c.scale)
+    assert np.all(np.isfinite(out))
+    # replace every poisoned cell by finite garbage; the output must not move
+    rng = np.random.default_rng(6)
+    k = c.k_pool.copy()
+    v = c.v_pool.copy()
+    k[np.isnan(k)] = rng.standard_normal(int(np.isnan(k).sum())).astype(np.float16) * 100
+    v[np.isnan(v)] = rng.standard_normal(int(np.isnan(v).sum())).astype(np.float16) * 100
+    out2 = oracle.paged_decode(c.q, k, v, c.block_tables, c.kv_lens, c.scale)
+    np.testing.assert_array_equal(out, out2)
+    # and the poisoned case really is poisoned: free pages and padding are NaN
+    n_nan_pages = int(np.all(np.isnan(c.k_pool.reshape(c.num_pages, -1)), axis=1).sum())
+    assert n_nan_pages == c.num_pages - 16
+
+
+@pytest.mark.parametrize("part", [16, 32, 48, 64, 200, 1000])
+def test_lse_split_identity(part):
+    c = W.tiny_decode()
+    out = oracle.paged_decode(c.q, c.k_pool, c.v_pool, c.block_tables, c.kv_lens, c.scale)
+    out2, m, l, acc = oracle.partitioned_decode(c.q, c.k_pool, c.v_pool, c.block_tables,
+                                                c.kv_lens, c.scale, part)
+    np.testing.assert_allclose(out2, out, rtol=1e-12, atol=1e-13)
+    n_part = m.shape[-1]
+    assert n_part == max(1, -(-200 // part))
+    # partitions beyond sequence 0's length are empty
+    used0 = -(-37 // part)
+    assert np.all(np.isneginf(m[0, :, used0:])) and np.all(l[0, :, used0:] == 0)
+
+
+def test_decode_is_ua_special_case():
+    c = W.tiny_decode()
+    a = oracle.paged_decode(c.q, c.k_pool, c.v_pool, c.block_tables, c.kv_lens, c.scale)
+    # the same two queries presented as a ubatch in reverse order with a padding token
+    q = np.stack([c.q[1], np.zeros_like(c.q[0]), c.q[0]])
+    b = oracle.paged_attention(q, c.k_pool, c.v_pool, c.block_tables, [1, -1, 0],
+                               [200, 0, 37], [199, 0, 36], c.scale)
+    np.testing.assert_array_equal(b[0], a[1])
+    np.testing.assert_array_equal(b[2], a[0])
+    assert np.all(b[1] == 0)
+
+
+def test_oracle_reads_only_needed_pages():
+    """Pages past ceil(n/P) may be garbage ids; the oracle must not touch them."""
+    c = W.tiny_decode()
+    bt = c.block_tables.copy()
+    bt[0, 3:] = 10 ** 6
+    a = oracle.paged_decode(c.q, c.k_pool, c.v_pool, c.block_tables, c.kv_lens, c.scale)
+    b = oracle.paged_decode(c.q, c.k_pool, c.v_pool, bt, c.kv_lens, c.scale)
+    np.testing.assert_array_equal(a, b)
+
+
+# --------------------------------------------------------------- cache ops
+
+def test_f16_rounding_golden():
+    g = json.load(open(os.path.join(GOLD, "f16_rounding.json")))
+    bits = np.array([int(c[0], 16) for c in g["cases"]], dtype=np.uint32)
+    want = np.array([int(c[1], 16) for c in g["cases"]], dtype=np.uint16)
+    n = len(bits)
+    src = np.zeros((n, 1, 1), dtype=np.float32)
+    src[:, 0, 0] = bits.view(np.float32)
+    k, v = W.nan_pools(n, 1, 1, 1)
+    with np.errstate(over="ignore"):
+        k2, v2 = oracle.reshape_and_cache(k, v, src, src, np.arange(n, dtype=np.int32))
+    np.testing.assert_array_equal(k2.view(np.uint16).ravel(), want)
+    np.testing.assert_array_equal(v2.view(np.uint16).ravel(), want)
+    nb = np.array([int(x, 16) for x in g["nan"]], dtype=np.uint32).view(np.float32)
+    k, v = W.nan_pools(len(nb), 1, 1, 1)
+    k.view(np.uint16)[...] = 0
+    k3, _ = oracle.reshape_and_cache(k, v, nb.reshape(-1, 1, 1), nb.reshape(-1, 1, 1),
+                                     np.arange(len(nb), dtype=np.int32))
+    assert np.all(np.isnan(k3))
+
+
+def test_reshape_and_cache_touches_only_addressed_cells():
+    rng = np.random.default_rng(8)
+    N, Hkv, P, D = 10, 3, 8, 16
+    k = rng.standard_normal((N, Hkv, P, D)).astype(np.float16)
+    v = rng.standard_normal((N, Hkv, D, P)).astype(np.float16)
+    T = 7
+    kn = rng.standard_normal((T, Hkv, D)).astype(np.float16)
+    vn = rng.standard_normal((T, Hkv, D)).astype(np.float16)
+    slots = np.array([3, 17, -1, 79, 40, -5, 8], dtype=np.int32)
+    k2, v2 = oracle.reshape_and_cache(k, v, kn, vn, slots)
+    kb, k2b = k.view(np.uint16), k2.view(np.uint16)
+    vb, v2b = v.view(np.uint16), v2.view(np.uint16)
+    touched = np.zeros((N, P), dtype=bool)
+    for i, s in enumerate(slots):
+        if s < 0:
+            continue
+        p, o = divmod(int(s), P)
+        touched[p, o] = True
+        for h in range(Hkv):
+            for d in range(D):
+                assert k2b[p, h, o, d] == kn[i, h, d].view(np.uint16)
+                assert v2b[p, h, d, o] == vn[i, h, d].view(np.uint16)
+    for p in range(N):
+        for o in range(P):
+            if not touched[p, o]:
+                assert np.array_equal(k2b[p, :, o, :], kb[p, :, o, :])
+                assert np.array_equal(v2b[p, :, :, o], vb[p, :, :, o])
+    with pytest.raises(ValueError):
+        oracle.reshape_and_cache(k, v, kn[:2], vn[:2], np.array([5, 5], np.int32))
+
+
+def test_copy_blocks():
+    rng = np.random.default_rng(9)
+    N = 9
+    ks = [rng.standard_normal((N, 2, 4, 8)).astype(np.float16) for _ in range(3)]
+    vs = [rng.standard_normal((N, 2, 8, 4)).astype(np.float16) for _ in range(3)]
+    pairs = [(1, 5), (1, 7), (2, 0)]
+    k2, v2 = oracle.copy_blocks(ks, vs, pairs)
+    for layer in range(3):
+        for p in range(N):
+            src = {5: 1, 7: 1, 0: 2}.get(p, p)
+            assert np.array_equal(k2[layer][p].view(np.uint16), ks[layer][src].view(np.uint16))
+            assert np.array_equal(v2[layer][p].view(np.uint16), vs[layer][src].view(np.uint16))
+    with pytest.raises(ValueError):
+        oracle.copy_blocks(ks, vs, [(1, 5), (2, 5)])
+    with pytest.raises(ValueError):
+        oracle.copy_blocks(ks, vs, [(1, 5), (5, 6)])
+
+
+# ---------------------------------------------------------------- allocator
+
+def run_pool_script(make_pool, script):
+    """Drive a pool object through the golden script; shared by the oracle model
+    test and the C library test.  ``make_pool(N, P, free_order)`` returns an
+    object with the AllocatorModel method names."""
+    pool = make_pool(script["num_pages"], script["page_size"], script["free_order"])
+    err_types = {"state": oracle.StateError, "no_pages": oracle.NoPagesError,
+                 "invalid": oracle.InvalidError}
+    for st in script["steps"]:
+        op = st["op"]
+        if "expect_error" in st:
+            before = (pool.stats()[0], pool.stats()[1].tolist())
+            with pytest.raises(err_types[st["expect_error"]]):
+                if op == "cow":
+                    pool.seq_cow(st["seq"], st["logical_page"])
+                elif op == "append":
+                    pool.seq_append(st["seq"], st["n"])
+                elif op == "free":
+                    pool.seq_free(st["seq"])
+            assert (pool.stats()[0], pool.stats()[1].tolist()) == before, st
+            continue
+        if op == "seq_new":
+            assert pool.seq_new() == st["expect_seq"]
+        elif op == "append":
+            slots, cow = pool.seq_append(st["seq"], st["n"])
+            assert list(slots) == st["expect_slots"], st
+            assert (None if cow is None else list(cow)) == st["expect_cow"], st
+        elif op == "fork":
+            assert pool.seq_fork(st["seq"]) == st["expect_seq"]
+        elif op == "cow":
+            assert list(pool.seq_cow(st["seq"], st["logical_page"])) == st["expect_pair"]
+        elif op == "free":
+            pool.seq_free(st["seq"])
+        elif op == "tables":
+            bt, kv = pool.block_tables(st["seqs"], st["max_pages"])
+            assert bt.tolist() == st["expect_bt"] and kv.tolist() == st["expect_len"]
+        elif op == "stats":
+            nf, ref = pool.stats()
+            assert nf == st["expect_free"] and list(ref) == st["expect_ref"]
+        else:
+            raise AssertionError(op)
+    return pool
+
+
+def test_allocator_golden_script():
+    script = json.load(open(os.path.join(GOLD, "pool_script.json")))
+    run_pool_script(oracle.AllocatorModel, script)
+
+
+def _check_invariants(pool: oracle.AllocatorModel):
+    n_free, ref = pool.stats()
+    used = set()
+    count = {}
+    for s, pages in pool.pages.items():
+        assert len(pages) == -(-pool.length[s] // pool.page_size)
+        for p in pages:
+            used.add(p)
+            count[p] = count.get(p, 0) + 1
+    assert n_free + len(used) == pool.num_pages
+    assert set(pool.free).isdisjoint(used)
+    for p in range(pool.num_pages):
+        assert ref[p] == count.get(p, 0)
+
+
+def test_allocator_random_invariants():
+    rng = np.random.default_rng(10)
+    pool = oracle.AllocatorModel(40, 4, rng.permutation(40))
+    live = []
+    for _ in range(400):
+        op = rng.integers(0, 5)
+        try:
+            if op == 0 or not live:
+                live.append(pool.seq_new())
+            elif op == 1:
+                pool.seq_append(live[rng.integers(len(live))], int(rng.integers(0, 9)))
+            elif op == 2:
+                live.append(pool.seq_fork(live[rng.integers(len(live))]))
+            elif op == 3:
+                s = live[rng.integers(len(live))]
+                if pool.pages[s]:
+                    pool.seq_cow(s, int(rng.integers(len(pool.pages[s]))))
+            else:
+                s = live.pop(rng.integers(len(live)))
+                pool.seq_free(s)
+        except (oracle.NoPagesError, oracle.StateError):
+            pass
+        _check_invariants(pool)
+    for s in live:
+        pool.seq_free(s)
+    assert pool.stats()[0] == 40 and not np.any(pool.stats()[1])
+
+
+def test_sharing_page_count():
+    """16 sequences sharing a 64-page prefix with 8 private pages each use
+    64 + 16*8 = 192 pages; without sharing 16*72 = 1152."""
+    pool = oracle.AllocatorModel(2048, 128)
+    s0 = pool.seq_new()
+    pool.seq_append(s0, 8192)
+    seqs = [s0] + [pool.seq_fork(s0) for _ in range(15)]
+    for s in seqs:
+        _, cow = pool.seq_append(s, 1024)
+        assert cow is None          # 8192 is page aligned: no partial shared page
+    assert 2048 - pool.stats()[0] == 192
+    # copy-on-write of the last shared page for four sequences: four more pages
+    pairs = [pool.seq_cow(s, 63) for s in seqs[:4]]
+    assert len({p[0] for p in pairs}) == 1 and 2048 - pool.stats()[0] == 196
+    flat = oracle.AllocatorModel(2048, 128)
+    for _ in range(16):
+        flat.seq_append(flat.seq_new(), 9216)
+    assert 2048 - flat.stats()[0] == 1152
+
+
+def test_append_cow_of_partial_shared_page():
+    """P=16, a 37-token prefix shared by a fork: the first append to either side
+    copies the partial page, the second side then writes in place."""
+    pool = oracle.AllocatorModel(16, 16)
+    a = pool.seq_new()
+    pool.seq_append(a, 37)
+    b = pool.seq_fork(a)
+    slots, cow = pool.seq_append(b, 3)
+    assert cow is not None and cow[0] == pool.pages[a][2] and cow[1] == pool.pages[b][2]
+    assert list(slots) == [cow[1] * 16 + 5, cow[1] * 16 + 6, cow[1] * 16 + 7]
+    slots2, cow2 = pool.seq_append(a, 1)
+    assert cow2 is None and list(slots2) == [pool.pages[a][2] * 16 + 5]
