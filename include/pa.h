@@ -1,0 +1,223 @@
+/*
+ * pa.h -- C ABI of libpa: paged attention over a block-table KV cache on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes is fixed by three pages:
+ *   [UA]  "面向多并发长上下文的 llama.cpp 分页式 KV Cache 与计算加速优化",
+ *         section 作品简介: the cache keeps a page mapping and a true KV length
+ *         per sequence; for a ubatch, the page table and true length are
+ *         expanded per query token in token order, and each query reads only
+ *         the valid pages of its own sequence (UA-PagedAttention).
+ *   [CF]  "CacheFlow：基于 llama.cpp 的多请求 LLM 推理优化引擎", section 2
+ *         (fixed-size blocks behind a block table; copy-on-write sharing of
+ *         blocks) and section 3 (one-pass and partition-plus-reduce paged
+ *         attention kernels; reshape-and-cache; block copy).
+ *   [RS]  "面向边缘智能体推理的 llama.cpp KV Cache 共享与复用优化", section
+ *         主要功能与技术路线: a shared prefix is read-only, each request's
+ *         private suffix is allocated separately.
+ *
+ * Conventions used by every entry point
+ *   - Every call returns pa_status (0 = PA_OK, negative = error).  On error,
+ *     pa_last_error() returns a message for the calling thread.  No C++
+ *     exception crosses this boundary.
+ *   - Cache storage for one layer is two device arrays of IEEE binary16:
+ *       K cache  [num_pages][n_kv_heads][page_size][head_dim]
+ *       V cache  [num_pages][n_kv_heads][head_dim][page_size]
+ *     Cell (page p, slot s) of KV head h holds one token's key row
+ *     K[p][h][s][:] and value column V[p][h][:][s].  A slot id is
+ *     page * page_size + slot.
+ *   - Query head h reads KV head h / (n_q_heads / n_kv_heads).
+ *   - Device pointers are pa_dev pointers; the caller allocates and owns every
+ *     device buffer.  Device calls are asynchronous on `stream` (a hipStream_t;
+ *     NULL is the default stream) and only launch kernels: they do not
+ *     allocate, copy host memory to the device, or synchronize.
+ *   - Host pointers are read during the call only.
+ *   - Supported shapes: head_dim in {64, 128}; page_size a multiple of 16 in
+ *     [16, 1024]; n_q_heads a multiple of n_kv_heads with group size
+ *     G = n_q_heads / n_kv_heads in {1, 2, 4, 8, 16}.  Other shapes return
+ *     PA_ERR_UNSUPPORTED before anything is launched.
+ *   - Block-table entries and slots are not range-checked on the device: an
+ *     out-of-range page id is undefined behaviour.  Setting the environment
+ *     variable PA_VALIDATE=1 makes the host check every host-visible table
+ *     first (decode: kv_lens_host; prefill: all host copies).
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    PA_OK = 0,
+    PA_ERR_INVALID = -1,      /* bad argument or shape; nothing was changed or launched */
+    PA_ERR_UNSUPPORTED = -2,  /* shape outside the supported set */
+    PA_ERR_NO_PAGES = -3,     /* page pool exhausted; the pool is unchanged */
+    PA_ERR_STATE = -4,        /* call not valid in the current pool state; pool unchanged */
+    PA_ERR_HIP = -5,          /* the HIP runtime reported an error at launch */
+    PA_ERR_WORKSPACE = -6     /* workspace missing or smaller than required */
+} pa_status;
+
+typedef void* pa_stream;      /* a hipStream_t */
+
+/* Text describing the last failing call on this thread ("" if none). */
+const char* pa_last_error(void);
+
+/* Library version, as major*10000 + minor*100 + patch. */
+int32_t pa_version(void);
+
+/* ===================================================================== */
+/* Host page pool and block tables ([CF] section 2; [UA] 作品简介; [RS]).  */
+/* Host memory only; never touches the device.  Not thread-safe: one     */
+/* thread at a time per pool.                                            */
+/* ===================================================================== */
+
+typedef struct pa_pool pa_pool;   /* opaque; created and freed by the library */
+
+/* Create a pool of `num_pages` pages of `page_size` cells.  `free_order`
+ * (nullable; else a permutation of 0..num_pages-1) is the order in which
+ * free pages are handed out; NULL means 0, 1, 2, ...  The free list is a
+ * stack: a page whose reference count falls to 0 is handed out next. */
+pa_status pa_pool_create(int32_t num_pages, int32_t page_size, const int32_t* free_order,
+                         pa_pool** out);
+void      pa_pool_destroy(pa_pool* pool);
+
+/* New empty sequence; its id is the smallest non-negative id not in use. */
+pa_status pa_seq_new(pa_pool* pool, int32_t* seq_out);
+
+/* Reserve cells for `n_new` more tokens of `seq`.  Fills the last page
+ * before taking new pages.  Writes slot_mapping_out[i] = page*page_size +
+ * slot for token i.  If the last page is shared (reference count > 1) and
+ * partly filled, the sequence first gets a private copy of it: the pair
+ * (source page, destination page) is written to cow_pair_out and *n_cow_out
+ * is set to 1 (else 0).  The caller must run pa_copy_blocks on that pair
+ * before writing the new tokens with pa_reshape_and_cache.  Fails with
+ * PA_ERR_NO_PAGES, leaving the pool unchanged, if too few pages are free. */
+pa_status pa_seq_append(pa_pool* pool, int32_t seq, int32_t n_new, int32_t* slot_mapping_out,
+                        int32_t cow_pair_out[2], int32_t* n_cow_out);
+
+/* New sequence sharing every page of `src` (reference counts + 1): the
+ * read-only shared prefix of [RS]; later appends copy on write ([CF] §2). */
+pa_status pa_seq_fork(pa_pool* pool, int32_t src_seq, int32_t* dst_seq_out);
+
+/* Give `seq` a private copy of its logical page `logical_page`, which must be
+ * shared (else PA_ERR_STATE).  Writes (source page, new page) to pair_out;
+ * the caller copies it with pa_copy_blocks. */
+pa_status pa_seq_cow(pa_pool* pool, int32_t seq, int32_t logical_page, int32_t pair_out[2]);
+
+/* Release `seq`; its pages' reference counts drop by one and pages that reach
+ * zero return to the free stack in logical order.  PA_ERR_STATE if `seq` is
+ * not live. */
+pa_status pa_seq_free(pa_pool* pool, int32_t seq);
+
+/* Export the block tables and true lengths of `n` live sequences:
+ * bt_out[i][j] = page of logical page j of seqs[i], -1 past its last page
+ * (row-major [n][max_pages]); kv_len_out[i] = its number of tokens.
+ * PA_ERR_INVALID if a sequence has more than max_pages pages. */
+pa_status pa_block_tables(const pa_pool* pool, const int32_t* seqs, int32_t n, int32_t max_pages,
+                          int32_t* bt_out, int32_t* kv_len_out);
+
+/* Number of free pages, and (nullable) the reference count of every page
+ * into refcount_out[num_pages]. */
+pa_status pa_pool_stats(const pa_pool* pool, int32_t* n_free_out, int32_t* refcount_out);
+
+/* ===================================================================== */
+/* Device operations.                                                    */
+/* ===================================================================== */
+
+typedef struct {
+    int32_t num_pages;
+    int32_t page_size;
+    int32_t n_kv_heads;
+    int32_t head_dim;
+} pa_cache_desc;
+
+/* Reshape-and-cache ([CF] section 3): write new tokens' keys and values into
+ * their cells.  k_new, v_new: device [n_tokens][n_kv_heads][head_dim], binary16
+ * (src_is_f32 = 0) or IEEE binary32 (src_is_f32 = 1, rounded to nearest even
+ * on store).  slot_mapping: device int32 [n_tokens]; a negative slot skips the
+ * token.  Live slots must be distinct and < num_pages*page_size.  Bits are
+ * copied exactly for binary16 input. */
+pa_status pa_reshape_and_cache(const pa_cache_desc* desc, void* k_cache, void* v_cache,
+                               const void* k_new, const void* v_new, int32_t src_is_f32,
+                               const int32_t* slot_mapping, int32_t n_tokens, pa_stream stream);
+
+/* Block copy for copy-on-write ([CF] sections 2 and 3): for every layer l and
+ * pair i, copy page pairs_host[2i] onto page pairs_host[2i+1] in both
+ * k_caches_host[l] and v_caches_host[l].  Pairs are validated on the host:
+ * ids in range, no destination repeated, no destination that is also a
+ * source (PA_ERR_INVALID otherwise).  k_caches_host / v_caches_host are host
+ * arrays of n_layers device pointers.  Bits are copied exactly. */
+pa_status pa_copy_blocks(const pa_cache_desc* desc, void* const* k_caches_host,
+                         void* const* v_caches_host, int32_t n_layers, const int32_t* pairs_host,
+                         int32_t n_pairs, pa_stream stream);
+
+/* Workspace bytes pa_decode needs for these arguments (0 if it needs none).
+ * Same meaning of arguments as pa_decode. */
+size_t pa_decode_workspace_bytes(const pa_cache_desc* desc, int32_t n_seqs, int32_t n_q_heads,
+                                 int32_t max_pages, const int32_t* kv_lens_host,
+                                 int32_t partition_tokens);
+
+/* Paged decode attention ([UA] 作品简介; [CF] section 3): one query token per
+ * sequence at position kv_len-1, reading only the sequence's first kv_len
+ * cells through its block-table row.
+ *   q            device fp32 [n_seqs][n_q_heads][head_dim]
+ *   out          device fp32 [n_seqs][n_q_heads][head_dim]
+ *   block_tables device int32 [n_seqs][max_pages]; only the first
+ *                ceil(kv_len/page_size) entries of a row are read
+ *   kv_lens      device int32 [n_seqs]; each in [1, max_pages*page_size]
+ *   kv_lens_host host copy of kv_lens or NULL; used only to size the split
+ *   scale        softmax scale (e.g. 1/sqrt(head_dim))
+ *   partition_tokens  0 = choose; -1 = one pass per sequence (no split);
+ *                >0 = split every sequence into partitions of this many
+ *                tokens (a multiple of 256), combined by a log-sum-exp reduce.
+ * The result does not depend on the physical page ids, and cells past a
+ * sequence's length are never used, whatever they hold. */
+pa_status pa_decode(const pa_cache_desc* desc, const void* k_cache, const void* v_cache,
+                    const float* q, float* out, const int32_t* block_tables,
+                    const int32_t* kv_lens, const int32_t* kv_lens_host, int32_t n_seqs,
+                    int32_t max_pages, int32_t n_q_heads, float scale, int32_t partition_tokens,
+                    void* workspace, size_t workspace_bytes, pa_stream stream);
+
+/* Workspace bytes pa_prefill needs for these arguments. */
+size_t pa_prefill_workspace_bytes(const pa_cache_desc* desc, int32_t n_tokens, int32_t n_q_heads,
+                                  const int32_t* token_row_host, const int32_t* token_kv_len_host,
+                                  const int32_t* token_pos_host, int32_t kv_splits);
+
+/* UA paged prefill ([UA] 作品简介): attention for one ubatch whose tokens may
+ * come from several sequences in any order.  Token i carries its sequence's
+ * block-table row token_row[i] (-1 = padding token: its output row is set to
+ * 0), the sequence's true KV length token_kv_len[i] (K/V of this ubatch
+ * already written) and its position token_pos[i]; it attends to cells
+ * t < min(token_kv_len[i], token_pos[i] + 1) of that row.
+ *   q            device fp32 [n_tokens][n_q_heads][head_dim]; rounded to
+ *                binary16 (nearest even) for the matrix products, which
+ *                accumulate in fp32
+ *   out          device fp32 [n_tokens][n_q_heads][head_dim]
+ *   block_tables device int32 [n_rows][max_pages]
+ *   token_row, token_kv_len, token_pos   device int32 [n_tokens]
+ *   token_row_host, token_kv_len_host, token_pos_host   host copies of the
+ *                same arrays, used to plan the work (grouping tokens by
+ *                sequence); they must equal the device arrays
+ *   kv_splits    0 = choose; >= 1 = split each tile's KV range into at most
+ *                this many parts combined by a log-sum-exp reduce
+ * Each row's tokens are grouped into tiles in ubatch order; a tile's work
+ * ends at its last token's visible length, so tokens of a row should appear
+ * in increasing position for efficiency (not for correctness). */
+pa_status pa_prefill(const pa_cache_desc* desc, const void* k_cache, const void* v_cache,
+                     const float* q, float* out, const int32_t* block_tables,
+                     const int32_t* token_row, const int32_t* token_kv_len,
+                     const int32_t* token_pos, const int32_t* token_row_host,
+                     const int32_t* token_kv_len_host, const int32_t* token_pos_host,
+                     int32_t n_tokens, int32_t n_rows, int32_t max_pages, int32_t n_q_heads,
+                     float scale, int32_t kv_splits, void* workspace, size_t workspace_bytes,
+                     pa_stream stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

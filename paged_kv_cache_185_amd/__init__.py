@@ -1,0 +1,307 @@
+"""Paged attention over a block-table KV cache for AMD MI355X (gfx950).
+
+Thin Python binding of libpa.so; every entry point has the name of its C
+function in include/pa.h.  This layer only marshals arguments: torch tensors
+supply device pointers and the current HIP stream, numpy arrays supply host
+arrays.  All computation happens in the library's HIP kernels; if the library
+is missing, every call raises.
+
+Cache layout (one layer), binary16:
+    K cache [num_pages][n_kv_heads][page_size][head_dim]
+    V cache [num_pages][n_kv_heads][head_dim][page_size]
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Sequence
+
+import numpy as np
+
+from . import _lib
+from ._lib import CacheDesc
+
+__all__ = [
+    "PaError", "InvalidError", "UnsupportedError", "NoPagesError", "StateError", "HipError",
+    "WorkspaceError", "CacheDesc", "cache_desc", "pa_version", "pa_last_error", "Pool",
+    "pa_reshape_and_cache", "pa_copy_blocks", "pa_decode_workspace_bytes", "pa_decode",
+    "pa_prefill_workspace_bytes", "pa_prefill", "library_path",
+]
+
+
+class PaError(RuntimeError):
+    status = None
+
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"[{status}] {msg}")
+        self.status = status
+
+
+class InvalidError(PaError):
+    pass
+
+
+class UnsupportedError(PaError):
+    pass
+
+
+class NoPagesError(PaError):
+    pass
+
+
+class StateError(PaError):
+    pass
+
+
+class HipError(PaError):
+    pass
+
+
+class WorkspaceError(PaError):
+    pass
+
+
+_ERR = {-1: InvalidError, -2: UnsupportedError, -3: NoPagesError, -4: StateError, -5: HipError,
+        -6: WorkspaceError}
+
+
+def library_path() -> str:
+    return _lib.LIB_PATH
+
+
+def _L():
+    return _lib.load()
+
+
+def _check(status: int):
+    if status != 0:
+        msg = _L().pa_last_error().decode(errors="replace")
+        raise _ERR.get(status, PaError)(status, msg)
+
+
+def pa_version() -> int:
+    return int(_L().pa_version())
+
+
+def pa_last_error() -> str:
+    return _L().pa_last_error().decode(errors="replace")
+
+
+# ---------------------------------------------------------------- helpers
+
+def _host_i32(x) -> np.ndarray:
+    a = np.ascontiguousarray(np.asarray(x, dtype=np.int32))
+    return a
+
+
+def _i32p(a: Optional[np.ndarray]):
+    if a is None:
+        return None
+    return a.ctypes.data_as(_lib.c_i32_p)
+
+
+def _stream_ptr(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dev(t, dtype, name, ndim=None):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor on the GPU")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must live on the GPU (got {t.device})")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims (got {t.dim()})")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def cache_desc(k_cache, v_cache=None) -> CacheDesc:
+    """Descriptor of a K cache [N][Hkv][P][D] (checked against V [N][Hkv][D][P])."""
+    N, H, P, D = (int(x) for x in k_cache.shape)
+    if v_cache is not None and tuple(v_cache.shape) != (N, H, D, P):
+        raise ValueError(f"V cache shape {tuple(v_cache.shape)} does not match K cache {N, H, P, D}")
+    return CacheDesc(N, P, H, D)
+
+
+# ---------------------------------------------------------------- host pool
+
+class Pool:
+    """Host page pool / block tables (pa_pool_*)."""
+
+    def __init__(self, num_pages: int, page_size: int, free_order: Optional[Sequence[int]] = None):
+        fo = None if free_order is None else _host_i32(free_order)
+        h = ctypes.c_void_p()
+        _check(_L().pa_pool_create(int(num_pages), int(page_size), _i32p(fo), ctypes.byref(h)))
+        self._h = h
+        self.num_pages = int(num_pages)
+        self.page_size = int(page_size)
+
+    def close(self):
+        if getattr(self, "_h", None) is not None and self._h.value:
+            _L().pa_pool_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def seq_new(self) -> int:
+        s = ctypes.c_int32()
+        _check(_L().pa_seq_new(self._h, ctypes.byref(s)))
+        return s.value
+
+    def seq_append(self, seq: int, n_new: int):
+        slots = np.empty(max(int(n_new), 0), dtype=np.int32)
+        pair = np.zeros(2, dtype=np.int32)
+        ncow = ctypes.c_int32(0)
+        _check(_L().pa_seq_append(self._h, int(seq), int(n_new), _i32p(slots), _i32p(pair),
+                                  ctypes.byref(ncow)))
+        return slots, ((int(pair[0]), int(pair[1])) if ncow.value else None)
+
+    def seq_fork(self, src: int) -> int:
+        s = ctypes.c_int32()
+        _check(_L().pa_seq_fork(self._h, int(src), ctypes.byref(s)))
+        return s.value
+
+    def seq_cow(self, seq: int, logical_page: int):
+        pair = np.zeros(2, dtype=np.int32)
+        _check(_L().pa_seq_cow(self._h, int(seq), int(logical_page), _i32p(pair)))
+        return int(pair[0]), int(pair[1])
+
+    def seq_free(self, seq: int) -> None:
+        _check(_L().pa_seq_free(self._h, int(seq)))
+
+    def block_tables(self, seqs: Sequence[int], max_pages: int):
+        s = _host_i32(seqs)
+        bt = np.empty((len(s), int(max_pages)), dtype=np.int32)
+        kv = np.empty(len(s), dtype=np.int32)
+        _check(_L().pa_block_tables(self._h, _i32p(s), len(s), int(max_pages), _i32p(bt), _i32p(kv)))
+        return bt, kv
+
+    def stats(self):
+        n = ctypes.c_int32()
+        ref = np.empty(self.num_pages, dtype=np.int32)
+        _check(_L().pa_pool_stats(self._h, ctypes.byref(n), _i32p(ref)))
+        return n.value, ref
+
+
+# ---------------------------------------------------------------- device ops
+
+def pa_reshape_and_cache(k_cache, v_cache, k_new, v_new, slot_mapping, stream=None) -> None:
+    """Write new tokens' K/V ([T][Hkv][D], float16 or float32) into their cells."""
+    import torch
+    desc = cache_desc(k_cache, v_cache)
+    _dev(k_cache, torch.float16, "k_cache", 4)
+    _dev(v_cache, torch.float16, "v_cache", 4)
+    T = int(slot_mapping.shape[0])
+    if k_new.dtype not in (torch.float16, torch.float32) or v_new.dtype != k_new.dtype:
+        raise TypeError("k_new/v_new must both be float16 or both float32")
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        if tuple(t.shape) != (T, desc.n_kv_heads, desc.head_dim):
+            raise ValueError(f"{name} must be [{T}][{desc.n_kv_heads}][{desc.head_dim}]")
+    _check(_L().pa_reshape_and_cache(
+        ctypes.byref(desc), _dev(k_cache, torch.float16, "k_cache"),
+        _dev(v_cache, torch.float16, "v_cache"), _dev(k_new, k_new.dtype, "k_new"),
+        _dev(v_new, v_new.dtype, "v_new"), 1 if k_new.dtype == torch.float32 else 0,
+        _dev(slot_mapping, torch.int32, "slot_mapping", 1), T, _stream_ptr(stream)))
+
+
+def pa_copy_blocks(k_caches, v_caches, pairs, stream=None) -> None:
+    """Copy pages src -> dst (pairs: host [n][2]) in every layer's K and V cache."""
+    import torch
+    if len(k_caches) != len(v_caches) or not k_caches:
+        raise ValueError("need the same non-zero number of K and V caches")
+    desc = cache_desc(k_caches[0], v_caches[0])
+    for k, v in zip(k_caches, v_caches):
+        if tuple(k.shape) != tuple(k_caches[0].shape) or tuple(v.shape) != tuple(v_caches[0].shape):
+            raise ValueError("all layers must have the same cache shape")
+        _dev(k, torch.float16, "k_cache", 4)
+        _dev(v, torch.float16, "v_cache", 4)
+    p = _host_i32(pairs).reshape(-1, 2)
+    n_layers = len(k_caches)
+    kp = (ctypes.c_void_p * n_layers)(*[k.data_ptr() for k in k_caches])
+    vp = (ctypes.c_void_p * n_layers)(*[v.data_ptr() for v in v_caches])
+    _check(_L().pa_copy_blocks(ctypes.byref(desc), kp, vp, n_layers, _i32p(p), p.shape[0],
+                               _stream_ptr(stream)))
+
+
+def pa_decode_workspace_bytes(desc: CacheDesc, n_seqs: int, n_q_heads: int, max_pages: int,
+                              kv_lens_host=None, partition_tokens: int = 0) -> int:
+    kl = None if kv_lens_host is None else _host_i32(kv_lens_host)
+    return int(_L().pa_decode_workspace_bytes(ctypes.byref(desc), int(n_seqs), int(n_q_heads),
+                                              int(max_pages), _i32p(kl), int(partition_tokens)))
+
+
+def pa_decode(q, k_cache, v_cache, block_tables, kv_lens, scale: float, kv_lens_host=None,
+              partition_tokens: int = 0, out=None, workspace=None, stream=None):
+    """Paged decode attention; q fp32 [S][Hq][D] -> out fp32 [S][Hq][D]."""
+    import torch
+    desc = cache_desc(k_cache, v_cache)
+    S, Hq, D = (int(x) for x in q.shape)
+    if D != desc.head_dim:
+        raise ValueError("q head_dim does not match the cache")
+    max_pages = int(block_tables.shape[1])
+    kl = None if kv_lens_host is None else _host_i32(kv_lens_host)
+    if out is None:
+        out = torch.empty_like(q)
+    need = pa_decode_workspace_bytes(desc, S, Hq, max_pages, kl, partition_tokens)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(_L().pa_decode(
+        ctypes.byref(desc), _dev(k_cache, torch.float16, "k_cache", 4),
+        _dev(v_cache, torch.float16, "v_cache", 4), _dev(q, torch.float32, "q", 3),
+        _dev(out, torch.float32, "out", 3), _dev(block_tables, torch.int32, "block_tables", 2),
+        _dev(kv_lens, torch.int32, "kv_lens", 1), _i32p(kl), S, max_pages, Hq, float(scale),
+        int(partition_tokens), ws_ptr, ws_bytes, _stream_ptr(stream)))
+    return out
+
+
+def pa_prefill_workspace_bytes(desc: CacheDesc, n_q_heads: int, token_row_host, token_kv_len_host,
+                               token_pos_host, kv_splits: int = 0) -> int:
+    r = _host_i32(token_row_host)
+    k = _host_i32(token_kv_len_host)
+    p = _host_i32(token_pos_host)
+    return int(_L().pa_prefill_workspace_bytes(ctypes.byref(desc), len(r), int(n_q_heads), _i32p(r),
+                                               _i32p(k), _i32p(p), int(kv_splits)))
+
+
+def pa_prefill(q, k_cache, v_cache, block_tables, token_row, token_kv_len, token_pos,
+               scale: float, token_row_host=None, token_kv_len_host=None, token_pos_host=None,
+               kv_splits: int = 0, out=None, workspace=None, stream=None):
+    """UA paged prefill; q fp32 [T][Hq][D] -> out fp32 [T][Hq][D].
+
+    The host copies of the token arrays are taken from the device tensors if
+    not given (a synchronizing copy; pass them to avoid it)."""
+    import torch
+    desc = cache_desc(k_cache, v_cache)
+    T, Hq, D = (int(x) for x in q.shape)
+    if D != desc.head_dim:
+        raise ValueError("q head_dim does not match the cache")
+    rh = _host_i32(token_row.cpu().numpy() if token_row_host is None else token_row_host)
+    kh = _host_i32(token_kv_len.cpu().numpy() if token_kv_len_host is None else token_kv_len_host)
+    ph = _host_i32(token_pos.cpu().numpy() if token_pos_host is None else token_pos_host)
+    if out is None:
+        out = torch.empty_like(q)
+    need = pa_prefill_workspace_bytes(desc, Hq, rh, kh, ph, kv_splits)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    n_rows, max_pages = (int(x) for x in block_tables.shape)
+    _check(_L().pa_prefill(
+        ctypes.byref(desc), _dev(k_cache, torch.float16, "k_cache", 4),
+        _dev(v_cache, torch.float16, "v_cache", 4), _dev(q, torch.float32, "q", 3),
+        _dev(out, torch.float32, "out", 3), _dev(block_tables, torch.int32, "block_tables", 2),
+        _dev(token_row, torch.int32, "token_row", 1), _dev(token_kv_len, torch.int32, "token_kv_len", 1),
+        _dev(token_pos, torch.int32, "token_pos", 1), _i32p(rh), _i32p(kh), _i32p(ph), T, n_rows,
+        max_pages, Hq, float(scale), int(kv_splits), ws_ptr, ws_bytes, _stream_ptr(stream)))
+    return out

@@ -1,0 +1,407 @@
+// C-ABI entry points for the device operations: argument validation, work
+// planning (partition sizes for decode, token tiles and KV splits for
+// prefill) and kernel launches on the caller's stream.  No device memory is
+// allocated here and nothing is copied from the host to the device.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "pa.h"
+#include "pa_internal.h"
+
+namespace pa {
+
+static thread_local std::string g_error;
+
+void set_error(const std::string& msg) { g_error = msg; }
+
+namespace {
+
+constexpr double kLog2e = 1.4426950408889634;
+
+pa_status fail(pa_status st, const std::string& msg) {
+    set_error(msg);
+    return st;
+}
+
+pa_status hip_fail(const char* where, hipError_t e) {
+    return fail(PA_ERR_HIP, std::string(where) + ": " + hipGetErrorString(e));
+}
+
+bool validate_env() {
+    const char* v = std::getenv("PA_VALIDATE");
+    return v && v[0] && v[0] != '0';
+}
+
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+pa_status check_desc(const char* fn, const pa_cache_desc* d) {
+    if (!d) return fail(PA_ERR_INVALID, std::string(fn) + ": desc is null");
+    if (d->num_pages < 1 || d->n_kv_heads < 1 || d->page_size < 1 || d->head_dim < 1)
+        return fail(PA_ERR_INVALID, std::string(fn) + ": cache dimensions must be >= 1");
+    if (d->head_dim != 64 && d->head_dim != 128)
+        return fail(PA_ERR_UNSUPPORTED, std::string(fn) + ": head_dim must be 64 or 128");
+    if (d->page_size % 16 != 0 || d->page_size > 1024)
+        return fail(PA_ERR_UNSUPPORTED,
+                    std::string(fn) + ": page_size must be a multiple of 16 in [16, 1024]");
+    if ((int64_t)d->num_pages * d->page_size > INT32_MAX)
+        return fail(PA_ERR_INVALID, std::string(fn) + ": num_pages * page_size overflows int32 slots");
+    return PA_OK;
+}
+
+pa_status check_heads(const char* fn, const pa_cache_desc* d, int32_t n_q_heads) {
+    if (n_q_heads < 1 || n_q_heads % d->n_kv_heads != 0)
+        return fail(PA_ERR_INVALID, std::string(fn) + ": n_q_heads must be a multiple of n_kv_heads");
+    const int G = n_q_heads / d->n_kv_heads;
+    if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16)
+        return fail(PA_ERR_UNSUPPORTED, std::string(fn) + ": GQA group size must be 1, 2, 4, 8 or 16");
+    return PA_OK;
+}
+
+// ---------------------------------------------------------------- decode plan
+
+struct DecodePlan {
+    int32_t partition_tokens = 0;
+    int32_t n_part = 1;
+    size_t m_off = 0, l_off = 0, acc_off = 0, bytes = 0;
+};
+
+pa_status plan_decode(const pa_cache_desc* d, int32_t n_seqs, int32_t n_q_heads, int32_t max_pages,
+                      const int32_t* kv_lens_host, int32_t partition_tokens, DecodePlan* plan) {
+    if (n_seqs < 0 || max_pages < 1)
+        return fail(PA_ERR_INVALID, "pa_decode: n_seqs must be >= 0 and max_pages >= 1");
+    const int64_t cap = (int64_t)max_pages * d->page_size;
+    int64_t total = (int64_t)n_seqs * cap, longest = cap;
+    if (kv_lens_host) {
+        total = 0;
+        longest = 1;
+        for (int32_t i = 0; i < n_seqs; ++i) {
+            const int64_t L = kv_lens_host[i];
+            if (L < 1 || L > cap)
+                return fail(PA_ERR_INVALID, "pa_decode: kv_len must be in [1, max_pages*page_size]");
+            total += L;
+            longest = std::max(longest, L);
+        }
+    }
+    const int64_t Q = kDecodePartitionQuantum;
+    int64_t T;
+    if (partition_tokens == -1) {
+        T = round_up(longest, Q);
+    } else if (partition_tokens > 0) {
+        if (partition_tokens % Q != 0)
+            return fail(PA_ERR_INVALID, "pa_decode: partition_tokens must be a multiple of 256");
+        T = partition_tokens;
+    } else if (partition_tokens == 0) {
+        // aim for about four workgroups per compute unit (256 CUs)
+        const int64_t work = total * d->n_kv_heads;
+        T = std::max<int64_t>(Q, round_up((work + 1023) / 1024, Q));
+        if (T >= longest) T = round_up(longest, Q);
+    } else {
+        return fail(PA_ERR_INVALID, "pa_decode: partition_tokens must be -1, 0 or a positive multiple of 256");
+    }
+    plan->partition_tokens = (int32_t)std::min<int64_t>(T, INT32_MAX / 2);
+    plan->n_part = (int32_t)((longest + T - 1) / T);
+    if (plan->n_part > 1) {
+        const size_t rows = (size_t)n_seqs * n_q_heads * plan->n_part;
+        plan->m_off = 0;
+        plan->l_off = align256(rows * 4);
+        plan->acc_off = plan->l_off + align256(rows * 4);
+        plan->bytes = plan->acc_off + align256(rows * (size_t)d->head_dim * 4);
+    }
+    return PA_OK;
+}
+
+// --------------------------------------------------------------- prefill plan
+
+struct PrefillPlan {
+    std::vector<PrefillTile> tiles;
+    int32_t split_tokens = 0;
+    int32_t max_splits = 1;
+    bool has_padding = false;
+    size_t m_off = 0, l_off = 0, acc_off = 0, bytes = 0;
+};
+
+pa_status plan_prefill(const pa_cache_desc* d, int32_t n_tokens, int32_t n_q_heads, int32_t n_rows,
+                       int32_t max_pages, const int32_t* row, const int32_t* kv_len,
+                       const int32_t* pos, int32_t kv_splits, PrefillPlan* plan) {
+    if (n_tokens < 0) return fail(PA_ERR_INVALID, "pa_prefill: n_tokens < 0");
+    if (n_tokens > 0 && (!row || !kv_len || !pos))
+        return fail(PA_ERR_INVALID, "pa_prefill: host token arrays are required");
+    if (kv_splits < 0) return fail(PA_ERR_INVALID, "pa_prefill: kv_splits < 0");
+    const int G = n_q_heads / d->n_kv_heads;
+    const int tpt = prefill_tokens_per_tile(G);
+    const int64_t cap = max_pages > 0 ? (int64_t)max_pages * d->page_size : INT64_MAX;
+    std::vector<int32_t> order;
+    order.reserve(n_tokens);
+    for (int32_t i = 0; i < n_tokens; ++i) {
+        if (row[i] < 0) {
+            plan->has_padding = true;
+            continue;
+        }
+        if (n_rows >= 0 && row[i] >= n_rows)
+            return fail(PA_ERR_INVALID, "pa_prefill: token_row out of range");
+        if (pos[i] < 0 || kv_len[i] < 1 || (int64_t)kv_len[i] > cap)
+            return fail(PA_ERR_INVALID, "pa_prefill: need pos >= 0 and kv_len in [1, max_pages*page_size]");
+        order.push_back(i);
+    }
+    std::stable_sort(order.begin(), order.end(),
+                     [&](int32_t x, int32_t y) { return row[x] < row[y]; });
+    int64_t sum_kv = 0, max_kv = 0;
+    for (size_t b = 0; b < order.size();) {
+        size_t e = b;
+        while (e < order.size() && row[order[e]] == row[order[b]]) ++e;
+        for (size_t s = b; s < e; s += tpt) {
+            const size_t f = std::min(e, s + tpt);
+            PrefillTile t{};
+            t.row = row[order[s]];
+            t.first = order[s];
+            t.last = order[f - 1];
+            t.count = (int32_t)(f - s);
+            int32_t ke = 0;
+            for (size_t j = s; j < f; ++j) {
+                const int32_t i = order[j];
+                ke = std::max(ke, std::min(kv_len[i], pos[i] + 1));
+            }
+            t.kv_end = ke;
+            plan->tiles.push_back(t);
+            sum_kv += ke;
+            max_kv = std::max<int64_t>(max_kv, ke);
+        }
+        b = e;
+    }
+    const int64_t KT = kPrefillKvTile;
+    int64_t split_tokens;
+    if (kv_splits == 1) {
+        split_tokens = round_up(std::max<int64_t>(max_kv, 1), KT);
+    } else if (kv_splits > 1) {
+        split_tokens = round_up(std::max<int64_t>((max_kv + kv_splits - 1) / kv_splits, 1), KT);
+    } else {
+        const int64_t need = (512 + d->n_kv_heads - 1) / d->n_kv_heads;   // ~2 workgroups per CU
+        if ((int64_t)plan->tiles.size() >= need)
+            split_tokens = round_up(std::max<int64_t>(max_kv, 1), KT);
+        else
+            split_tokens = std::max<int64_t>(256, round_up((sum_kv + need - 1) / need, KT));
+    }
+    split_tokens = std::min<int64_t>(split_tokens, round_up(std::max<int64_t>(max_kv, 1), KT));
+    plan->split_tokens = (int32_t)split_tokens;
+    plan->max_splits = 1;
+    for (auto& t : plan->tiles) {
+        t.n_splits = (int32_t)((t.kv_end + split_tokens - 1) / split_tokens);
+        plan->max_splits = std::max(plan->max_splits, t.n_splits);
+    }
+    if (plan->max_splits > 1) {
+        const size_t rows = (size_t)n_tokens * n_q_heads * plan->max_splits;
+        plan->m_off = 0;
+        plan->l_off = align256(rows * 4);
+        plan->acc_off = plan->l_off + align256(rows * 4);
+        plan->bytes = plan->acc_off + align256(rows * (size_t)d->head_dim * 4);
+    }
+    return PA_OK;
+}
+
+}  // namespace
+}  // namespace pa
+
+using namespace pa;
+
+extern "C" {
+
+const char* pa_last_error(void) { return g_error.c_str(); }
+
+int32_t pa_version(void) { return 100; }
+
+pa_status pa_reshape_and_cache(const pa_cache_desc* desc, void* k_cache, void* v_cache,
+                               const void* k_new, const void* v_new, int32_t src_is_f32,
+                               const int32_t* slot_mapping, int32_t n_tokens, pa_stream stream) {
+    pa_status st = check_desc("pa_reshape_and_cache", desc);
+    if (st != PA_OK) return st;
+    if (n_tokens < 0) return fail(PA_ERR_INVALID, "pa_reshape_and_cache: n_tokens < 0");
+    if (n_tokens == 0) return PA_OK;
+    if (!k_cache || !v_cache || !k_new || !v_new || !slot_mapping)
+        return fail(PA_ERR_INVALID, "pa_reshape_and_cache: null pointer");
+    if (src_is_f32 != 0 && src_is_f32 != 1)
+        return fail(PA_ERR_INVALID, "pa_reshape_and_cache: src_is_f32 must be 0 or 1");
+    hipError_t e = launch_reshape_and_cache(k_cache, v_cache, k_new, v_new, src_is_f32 == 1,
+                                            slot_mapping, n_tokens, desc->n_kv_heads,
+                                            desc->page_size, desc->head_dim, (hipStream_t)stream);
+    return e == hipSuccess ? PA_OK : hip_fail("pa_reshape_and_cache", e);
+}
+
+pa_status pa_copy_blocks(const pa_cache_desc* desc, void* const* k_caches_host,
+                         void* const* v_caches_host, int32_t n_layers, const int32_t* pairs_host,
+                         int32_t n_pairs, pa_stream stream) {
+    pa_status st = check_desc("pa_copy_blocks", desc);
+    if (st != PA_OK) return st;
+    if (n_layers < 0 || n_pairs < 0) return fail(PA_ERR_INVALID, "pa_copy_blocks: negative count");
+    if (n_layers == 0 || n_pairs == 0) return PA_OK;
+    if (!k_caches_host || !v_caches_host || !pairs_host)
+        return fail(PA_ERR_INVALID, "pa_copy_blocks: null pointer");
+    for (int32_t l = 0; l < n_layers; ++l)
+        if (!k_caches_host[l] || !v_caches_host[l])
+            return fail(PA_ERR_INVALID, "pa_copy_blocks: null cache pointer");
+    std::vector<char> is_dst(desc->num_pages, 0), is_src(desc->num_pages, 0);
+    for (int32_t i = 0; i < n_pairs; ++i) {
+        const int32_t s = pairs_host[2 * i], dpg = pairs_host[2 * i + 1];
+        if (s < 0 || s >= desc->num_pages || dpg < 0 || dpg >= desc->num_pages)
+            return fail(PA_ERR_INVALID, "pa_copy_blocks: page id out of range");
+        if (is_dst[dpg]) return fail(PA_ERR_INVALID, "pa_copy_blocks: a destination repeats");
+        is_dst[dpg] = 1;
+        is_src[s] = 1;
+    }
+    for (int32_t p = 0; p < desc->num_pages; ++p)
+        if (is_dst[p] && is_src[p])
+            return fail(PA_ERR_INVALID, "pa_copy_blocks: a destination is also a source");
+    const int64_t page_bytes =
+        (int64_t)desc->n_kv_heads * desc->page_size * desc->head_dim * 2;
+    hipError_t e = launch_copy_blocks(k_caches_host, v_caches_host, n_layers, pairs_host, n_pairs,
+                                      page_bytes, (hipStream_t)stream);
+    return e == hipSuccess ? PA_OK : hip_fail("pa_copy_blocks", e);
+}
+
+size_t pa_decode_workspace_bytes(const pa_cache_desc* desc, int32_t n_seqs, int32_t n_q_heads,
+                                 int32_t max_pages, const int32_t* kv_lens_host,
+                                 int32_t partition_tokens) {
+    if (check_desc("pa_decode_workspace_bytes", desc) != PA_OK) return 0;
+    if (check_heads("pa_decode_workspace_bytes", desc, n_q_heads) != PA_OK) return 0;
+    DecodePlan plan;
+    if (plan_decode(desc, n_seqs, n_q_heads, max_pages, kv_lens_host, partition_tokens, &plan) != PA_OK)
+        return 0;
+    return plan.bytes;
+}
+
+pa_status pa_decode(const pa_cache_desc* desc, const void* k_cache, const void* v_cache,
+                    const float* q, float* out, const int32_t* block_tables,
+                    const int32_t* kv_lens, const int32_t* kv_lens_host, int32_t n_seqs,
+                    int32_t max_pages, int32_t n_q_heads, float scale, int32_t partition_tokens,
+                    void* workspace, size_t workspace_bytes, pa_stream stream) {
+    pa_status st = check_desc("pa_decode", desc);
+    if (st != PA_OK) return st;
+    if ((st = check_heads("pa_decode", desc, n_q_heads)) != PA_OK) return st;
+    if (n_seqs == 0) return PA_OK;
+    if (!k_cache || !v_cache || !q || !out || !block_tables || !kv_lens)
+        return fail(PA_ERR_INVALID, "pa_decode: null pointer");
+    if (!std::isfinite(scale)) return fail(PA_ERR_INVALID, "pa_decode: scale must be finite");
+    DecodePlan plan;
+    if ((st = plan_decode(desc, n_seqs, n_q_heads, max_pages, kv_lens_host, partition_tokens, &plan)) != PA_OK)
+        return st;
+    if (plan.bytes > 0 && (!workspace || workspace_bytes < plan.bytes))
+        return fail(PA_ERR_WORKSPACE, "pa_decode: workspace missing or too small (need " +
+                                          std::to_string(plan.bytes) + " bytes)");
+    if (validate_env() && kv_lens_host == nullptr)
+        return fail(PA_ERR_INVALID, "pa_decode: PA_VALIDATE=1 needs kv_lens_host");
+    DecodeArgs a{};
+    a.k_cache = (const uint16_t*)k_cache;
+    a.v_cache = (const uint16_t*)v_cache;
+    a.q = q;
+    a.out = out;
+    a.block_tables = block_tables;
+    a.kv_lens = kv_lens;
+    if (plan.n_part > 1) {
+        char* ws = (char*)workspace;
+        a.part_m = (float*)(ws + plan.m_off);
+        a.part_l = (float*)(ws + plan.l_off);
+        a.part_acc = (float*)(ws + plan.acc_off);
+    }
+    a.n_seqs = n_seqs;
+    a.max_pages = max_pages;
+    a.n_q_heads = n_q_heads;
+    a.n_kv_heads = desc->n_kv_heads;
+    a.page_size = desc->page_size;
+    a.head_dim = desc->head_dim;
+    a.partition_tokens = plan.partition_tokens;
+    a.n_part = plan.n_part;
+    a.scale_log2 = (float)((double)scale * kLog2e);
+    hipError_t e = launch_decode(a, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail("pa_decode", e);
+    if (plan.n_part > 1) {
+        e = launch_decode_reduce(a, (hipStream_t)stream);
+        if (e != hipSuccess) return hip_fail("pa_decode (reduce)", e);
+    }
+    return PA_OK;
+}
+
+size_t pa_prefill_workspace_bytes(const pa_cache_desc* desc, int32_t n_tokens, int32_t n_q_heads,
+                                  const int32_t* token_row_host, const int32_t* token_kv_len_host,
+                                  const int32_t* token_pos_host, int32_t kv_splits) {
+    if (check_desc("pa_prefill_workspace_bytes", desc) != PA_OK) return 0;
+    if (check_heads("pa_prefill_workspace_bytes", desc, n_q_heads) != PA_OK) return 0;
+    PrefillPlan plan;
+    if (plan_prefill(desc, n_tokens, n_q_heads, -1, -1, token_row_host, token_kv_len_host,
+                     token_pos_host, kv_splits, &plan) != PA_OK)
+        return 0;
+    return plan.bytes;
+}
+
+pa_status pa_prefill(const pa_cache_desc* desc, const void* k_cache, const void* v_cache,
+                     const float* q, float* out, const int32_t* block_tables,
+                     const int32_t* token_row, const int32_t* token_kv_len,
+                     const int32_t* token_pos, const int32_t* token_row_host,
+                     const int32_t* token_kv_len_host, const int32_t* token_pos_host,
+                     int32_t n_tokens, int32_t n_rows, int32_t max_pages, int32_t n_q_heads,
+                     float scale, int32_t kv_splits, void* workspace, size_t workspace_bytes,
+                     pa_stream stream) {
+    pa_status st = check_desc("pa_prefill", desc);
+    if (st != PA_OK) return st;
+    if ((st = check_heads("pa_prefill", desc, n_q_heads)) != PA_OK) return st;
+    if (n_tokens == 0) return PA_OK;
+    if (!k_cache || !v_cache || !q || !out || !block_tables || !token_row || !token_kv_len ||
+        !token_pos)
+        return fail(PA_ERR_INVALID, "pa_prefill: null pointer");
+    if (n_rows < 1 || max_pages < 1)
+        return fail(PA_ERR_INVALID, "pa_prefill: n_rows and max_pages must be >= 1");
+    if (!std::isfinite(scale)) return fail(PA_ERR_INVALID, "pa_prefill: scale must be finite");
+    PrefillPlan plan;
+    if ((st = plan_prefill(desc, n_tokens, n_q_heads, n_rows, max_pages, token_row_host,
+                           token_kv_len_host, token_pos_host, kv_splits, &plan)) != PA_OK)
+        return st;
+    if (plan.bytes > 0 && (!workspace || workspace_bytes < plan.bytes))
+        return fail(PA_ERR_WORKSPACE, "pa_prefill: workspace missing or too small (need " +
+                                          std::to_string(plan.bytes) + " bytes)");
+    PrefillArgs a{};
+    a.k_cache = (const uint16_t*)k_cache;
+    a.v_cache = (const uint16_t*)v_cache;
+    a.q = q;
+    a.out = out;
+    a.block_tables = block_tables;
+    a.token_row = token_row;
+    a.token_kv_len = token_kv_len;
+    a.token_pos = token_pos;
+    if (plan.max_splits > 1) {
+        char* ws = (char*)workspace;
+        a.part_m = (float*)(ws + plan.m_off);
+        a.part_l = (float*)(ws + plan.l_off);
+        a.part_acc = (float*)(ws + plan.acc_off);
+    }
+    a.n_tokens = n_tokens;
+    a.max_pages = max_pages;
+    a.n_q_heads = n_q_heads;
+    a.n_kv_heads = desc->n_kv_heads;
+    a.page_size = desc->page_size;
+    a.head_dim = desc->head_dim;
+    a.split_tokens = plan.split_tokens;
+    a.max_splits = plan.max_splits;
+    a.scale_log2 = (float)((double)scale * kLog2e);
+    const int n_tiles = (int)plan.tiles.size();
+    for (int b = 0; b < n_tiles; b += kMaxTilesPerLaunch) {
+        const int nb = std::min(kMaxTilesPerLaunch, n_tiles - b);
+        hipError_t e = launch_prefill(a, plan.tiles.data() + b, nb, plan.max_splits,
+                                      (hipStream_t)stream);
+        if (e != hipSuccess) return hip_fail("pa_prefill", e);
+    }
+    hipError_t e = hipSuccess;
+    if (plan.max_splits > 1)
+        e = launch_prefill_reduce(a, (hipStream_t)stream);
+    else if (plan.has_padding)
+        e = launch_zero_rows(out, token_row, n_tokens, n_q_heads * desc->head_dim,
+                             (hipStream_t)stream);
+    return e == hipSuccess ? PA_OK : hip_fail("pa_prefill (reduce)", e);
+}
+
+}  // extern "C"

@@ -1,0 +1,155 @@
+// Reshape-and-cache and block copy ("CacheFlow：基于 llama.cpp 的多请求 LLM 推理优化引擎",
+// section 3: fused kernels that write new tokens' K/V into their blocks and
+// copy blocks for copy-on-write sharing, section 2).
+//
+// Both kernels move bits; the only arithmetic is the float32 -> binary16
+// conversion (v_cvt_f16_f32, round to nearest even) for float32 sources.
+#include "pa_internal.h"
+
+namespace pa {
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// One thread writes 8 consecutive head_dim elements of one (token, KV head).
+// K rows are contiguous in the cache (one 16-byte store); V is stored with the
+// slot innermost, so its 8 elements go to 8 rows of the page-head block.
+template <bool kSrcF32>
+__global__ __launch_bounds__(256) void reshape_and_cache_kernel(
+    uint16_t* __restrict__ k_cache, uint16_t* __restrict__ v_cache, const void* __restrict__ k_new,
+    const void* __restrict__ v_new, const int32_t* __restrict__ slots, int32_t n_tokens,
+    int32_t n_kv_heads, int32_t page_size, int32_t head_dim) {
+    const int chunks = head_dim >> 3;
+    const int64_t per_token = (int64_t)n_kv_heads * chunks;
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= (int64_t)n_tokens * per_token) return;
+    const int32_t tok = (int32_t)(i / per_token);
+    const int32_t rem = (int32_t)(i - (int64_t)tok * per_token);
+    const int32_t h = rem / chunks;
+    const int32_t d0 = (rem - h * chunks) << 3;
+    const int32_t slot = slots[tok];
+    if (slot < 0) return;
+    const int32_t page = slot / page_size;
+    const int32_t off = slot - page * page_size;
+    const int64_t src = ((int64_t)tok * n_kv_heads + h) * head_dim + d0;
+
+    uint16_t kv[8], vv[8];
+    if constexpr (kSrcF32) {
+        const float* ks = reinterpret_cast<const float*>(k_new) + src;
+        const float* vs = reinterpret_cast<const float*>(v_new) + src;
+        const float4 k0 = *reinterpret_cast<const float4*>(ks);
+        const float4 k1 = *reinterpret_cast<const float4*>(ks + 4);
+        const float4 v0 = *reinterpret_cast<const float4*>(vs);
+        const float4 v1 = *reinterpret_cast<const float4*>(vs + 4);
+        const float kf[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
+        const float vf[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            kv[e] = __builtin_bit_cast(uint16_t, (_Float16)kf[e]);
+            vv[e] = __builtin_bit_cast(uint16_t, (_Float16)vf[e]);
+        }
+    } else {
+        const u32x4 kk = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(k_new) + src);
+        const u32x4 vw = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(v_new) + src);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            kv[2 * w] = (uint16_t)(kk[w] & 0xffffu);
+            kv[2 * w + 1] = (uint16_t)(kk[w] >> 16);
+            vv[2 * w] = (uint16_t)(vw[w] & 0xffffu);
+            vv[2 * w + 1] = (uint16_t)(vw[w] >> 16);
+        }
+    }
+    u32x4 kout;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) kout[w] = (uint32_t)kv[2 * w] | ((uint32_t)kv[2 * w + 1] << 16);
+    uint16_t* kdst = k_cache + (((int64_t)page * n_kv_heads + h) * page_size + off) * head_dim + d0;
+    *reinterpret_cast<u32x4*>(kdst) = kout;
+    uint16_t* vdst = v_cache + (((int64_t)page * n_kv_heads + h) * head_dim + d0) * page_size + off;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) vdst[(int64_t)e * page_size] = vv[e];
+}
+
+struct CopyBlocksArgs {
+    uint16_t* k[kMaxCopyLayers];
+    uint16_t* v[kMaxCopyLayers];
+    int32_t pairs[2 * kMaxCopyPairs];
+};
+
+constexpr int kCopyBytesPerBlock = 16384;
+
+// grid: (ceil(page_bytes / 16 KiB), n_pairs, 2 * n_layers); 16-byte vector copies.
+__global__ __launch_bounds__(256) void copy_blocks_kernel(CopyBlocksArgs args, int64_t page_bytes) {
+    const int pair = blockIdx.y;
+    const int layer = blockIdx.z >> 1;
+    uint16_t* base = (blockIdx.z & 1) ? args.v[layer] : args.k[layer];
+    const char* src = reinterpret_cast<const char*>(base) + (int64_t)args.pairs[2 * pair] * page_bytes;
+    char* dst = reinterpret_cast<char*>(base) + (int64_t)args.pairs[2 * pair + 1] * page_bytes;
+    const int64_t begin = (int64_t)blockIdx.x * kCopyBytesPerBlock;
+    const int64_t end = begin + kCopyBytesPerBlock < page_bytes ? begin + kCopyBytesPerBlock : page_bytes;
+    for (int64_t off = begin + (int64_t)threadIdx.x * 16; off < end; off += 256 * 16)
+        *reinterpret_cast<u32x4*>(dst + off) = *reinterpret_cast<const u32x4*>(src + off);
+}
+
+__global__ __launch_bounds__(256) void zero_rows_kernel(float* __restrict__ out,
+                                                        const int32_t* __restrict__ token_row,
+                                                        int32_t n_tokens, int32_t row_elems) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t tok = i / row_elems;
+    if (tok >= n_tokens) return;
+    if (token_row[tok] < 0) out[i] = 0.0f;
+}
+
+}  // namespace
+
+hipError_t launch_reshape_and_cache(void* k_cache, void* v_cache, const void* k_new,
+                                    const void* v_new, bool src_f32, const int32_t* slots,
+                                    int32_t n_tokens, int32_t n_kv_heads, int32_t page_size,
+                                    int32_t head_dim, hipStream_t stream) {
+    const int64_t threads = (int64_t)n_tokens * n_kv_heads * (head_dim / 8);
+    if (threads == 0) return hipSuccess;
+    const dim3 grid((unsigned)((threads + 255) / 256));
+    if (src_f32)
+        hipLaunchKernelGGL(reshape_and_cache_kernel<true>, grid, dim3(256), 0, stream,
+                           (uint16_t*)k_cache, (uint16_t*)v_cache, k_new, v_new, slots, n_tokens,
+                           n_kv_heads, page_size, head_dim);
+    else
+        hipLaunchKernelGGL(reshape_and_cache_kernel<false>, grid, dim3(256), 0, stream,
+                           (uint16_t*)k_cache, (uint16_t*)v_cache, k_new, v_new, slots, n_tokens,
+                           n_kv_heads, page_size, head_dim);
+    return hipGetLastError();
+}
+
+hipError_t launch_copy_blocks(void* const* k_caches, void* const* v_caches, int32_t n_layers,
+                              const int32_t* pairs, int32_t n_pairs, int64_t page_bytes,
+                              hipStream_t stream) {
+    for (int32_t l0 = 0; l0 < n_layers; l0 += kMaxCopyLayers) {
+        const int32_t nl = n_layers - l0 < kMaxCopyLayers ? n_layers - l0 : kMaxCopyLayers;
+        for (int32_t p0 = 0; p0 < n_pairs; p0 += kMaxCopyPairs) {
+            const int32_t np = n_pairs - p0 < kMaxCopyPairs ? n_pairs - p0 : kMaxCopyPairs;
+            CopyBlocksArgs args{};
+            for (int32_t l = 0; l < nl; ++l) {
+                args.k[l] = (uint16_t*)k_caches[l0 + l];
+                args.v[l] = (uint16_t*)v_caches[l0 + l];
+            }
+            for (int32_t i = 0; i < 2 * np; ++i) args.pairs[i] = pairs[2 * p0 + i];
+            const dim3 grid((unsigned)((page_bytes + kCopyBytesPerBlock - 1) / kCopyBytesPerBlock),
+                            (unsigned)np, (unsigned)(2 * nl));
+            hipLaunchKernelGGL(copy_blocks_kernel, grid, dim3(256), 0, stream, args, page_bytes);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_zero_rows(float* out, const int32_t* token_row, int32_t n_tokens,
+                            int32_t row_elems, hipStream_t stream) {
+    const int64_t n = (int64_t)n_tokens * row_elems;
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(zero_rows_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
+                       out, token_row, n_tokens, row_elems);
+    return hipGetLastError();
+}
+
+}  // namespace pa

@@ -1,0 +1,106 @@
+// Internal declarations shared by the C-ABI layer (api.cpp) and the kernel
+// translation units.  Not part of the public interface.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+// ---- reshape_and_cache / copy_blocks -------------------------------------
+
+hipError_t launch_reshape_and_cache(void* k_cache, void* v_cache, const void* k_new,
+                                    const void* v_new, bool src_f32, const int32_t* slots,
+                                    int32_t n_tokens, int32_t n_kv_heads, int32_t page_size,
+                                    int32_t head_dim, hipStream_t stream);
+
+// Copies up to kMaxCopyPairs pairs for up to kMaxCopyLayers layers per launch.
+constexpr int kMaxCopyPairs = 128;
+constexpr int kMaxCopyLayers = 32;
+hipError_t launch_copy_blocks(void* const* k_caches, void* const* v_caches, int32_t n_layers,
+                              const int32_t* pairs, int32_t n_pairs, int64_t page_bytes,
+                              hipStream_t stream);
+
+// ---- decode ---------------------------------------------------------------
+
+// Tokens per partition are a multiple of this (waves per workgroup x chunk x 2).
+constexpr int kDecodePartitionQuantum = 256;
+
+struct DecodeArgs {
+    const uint16_t* k_cache;
+    const uint16_t* v_cache;
+    const float* q;
+    float* out;
+    const int32_t* block_tables;
+    const int32_t* kv_lens;
+    float* part_m;      // [n_seqs][Hq][n_part] (log2 domain), or null for one pass
+    float* part_l;      // [n_seqs][Hq][n_part]
+    float* part_acc;    // [n_seqs][Hq][n_part][D]
+    int32_t n_seqs;
+    int32_t max_pages;
+    int32_t n_q_heads;
+    int32_t n_kv_heads;
+    int32_t page_size;
+    int32_t head_dim;
+    int32_t partition_tokens;
+    int32_t n_part;     // partitions per sequence in the grid
+    float scale_log2;   // scale * log2(e)
+};
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+
+// ---- prefill ---------------------------------------------------------------
+
+// One tile = the tokens of one sequence (block-table row) that a workgroup
+// handles for one KV head.  Tokens are found on the device by scanning
+// token_row[first .. last] for `row`; exactly `count` of them match.
+struct PrefillTile {
+    int32_t row;
+    int32_t first;      // ubatch index of the tile's first token
+    int32_t last;       // ubatch index of the tile's last token
+    int32_t count;      // tokens in the tile (<= tokens per tile)
+    int32_t kv_end;     // largest visible length of any token in the tile
+    int32_t n_splits;   // KV splits used by this tile (<= grid splits)
+};
+
+constexpr int kMaxTilesPerLaunch = 128;
+
+struct PrefillArgs {
+    const uint16_t* k_cache;
+    const uint16_t* v_cache;
+    const float* q;
+    float* out;
+    const int32_t* block_tables;
+    const int32_t* token_row;
+    const int32_t* token_kv_len;
+    const int32_t* token_pos;
+    float* part_m;      // [n_tokens][Hq][max_splits] or null when no tile splits
+    float* part_l;
+    float* part_acc;    // [n_tokens][Hq][max_splits][D]
+    int32_t n_tokens;
+    int32_t max_pages;
+    int32_t n_q_heads;
+    int32_t n_kv_heads;
+    int32_t page_size;
+    int32_t head_dim;
+    int32_t split_tokens;   // KV keys per split (multiple of the KV tile)
+    int32_t max_splits;     // split slots per (token, head) in the partials
+    float scale_log2;
+};
+
+int prefill_tokens_per_tile(int group);   // query tokens per tile for GQA group size
+constexpr int kPrefillKvTile = 64;
+
+hipError_t launch_prefill(const PrefillArgs& a, const PrefillTile* tiles, int n_tiles,
+                          int grid_splits, hipStream_t stream);
+
+// Combine split partials (log2-domain m, l, acc) into out for `n_rows` rows of
+// `head_dim`; rows whose part count is 1 were written directly and are skipped
+// when `skip_single` is set.  Row r has its parts at r*max_parts.
+hipError_t launch_prefill_reduce(const PrefillArgs& a, hipStream_t stream);
+hipError_t launch_decode_reduce(const DecodeArgs& a, hipStream_t stream);
+
+hipError_t launch_zero_rows(float* out, const int32_t* token_row, int32_t n_tokens,
+                            int32_t row_elems, hipStream_t stream);
+
+}  // namespace pa

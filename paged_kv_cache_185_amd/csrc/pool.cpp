@@ -1,0 +1,219 @@
+// Host page pool and block tables.
+//
+// Structure from "CacheFlow：基于 llama.cpp 的多请求 LLM 推理优化引擎", section 2
+// (fixed-size blocks mapped by a block table, copy-on-write sharing), and from
+// "面向多并发长上下文的 llama.cpp 分页式 KV Cache 与计算加速优化", section 作品简介
+// (a page mapping and a true length per sequence).  Sharing semantics from
+// "面向边缘智能体推理的 llama.cpp KV Cache 共享与复用优化", section 主要功能与技术路线
+// (read-only shared prefix, private suffix per request, budget over the union
+// of physical cells -- here: a page is counted once, whatever its refcount).
+//
+// Policy (fixes the choice the pages leave open, so block tables are unique):
+// a stack of free pages seeded so that free_order[0] is handed out first; freed
+// pages are pushed in logical order; ids are the smallest unused; every call
+// checks all its preconditions before changing anything.
+#include <algorithm>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "pa.h"
+
+namespace pa {
+void set_error(const std::string& msg);
+}
+
+struct pa_pool {
+    int32_t num_pages = 0;
+    int32_t page_size = 0;
+    std::vector<int32_t> free_stack;   // back() is the top
+    std::vector<int32_t> ref;
+    struct Seq {
+        bool live = false;
+        int64_t len = 0;
+        std::vector<int32_t> pages;
+    };
+    std::vector<Seq> seqs;
+
+    int32_t pop() {
+        int32_t p = free_stack.back();
+        free_stack.pop_back();
+        return p;
+    }
+    bool live(int32_t s) const {
+        return s >= 0 && s < (int32_t)seqs.size() && seqs[s].live;
+    }
+    int32_t new_id() {
+        for (size_t i = 0; i < seqs.size(); ++i)
+            if (!seqs[i].live) return (int32_t)i;
+        seqs.emplace_back();
+        return (int32_t)seqs.size() - 1;
+    }
+};
+
+static pa_status fail(pa_status st, const char* msg) {
+    pa::set_error(msg);
+    return st;
+}
+
+extern "C" {
+
+pa_status pa_pool_create(int32_t num_pages, int32_t page_size, const int32_t* free_order,
+                         pa_pool** out) {
+    if (!out) return fail(PA_ERR_INVALID, "pa_pool_create: out is null");
+    *out = nullptr;
+    if (num_pages < 1 || page_size < 1)
+        return fail(PA_ERR_INVALID, "pa_pool_create: num_pages and page_size must be >= 1");
+    if ((int64_t)num_pages * page_size > INT32_MAX)
+        return fail(PA_ERR_INVALID, "pa_pool_create: num_pages * page_size overflows int32 slots");
+    std::vector<int32_t> order(num_pages);
+    if (free_order) {
+        std::vector<char> seen(num_pages, 0);
+        for (int32_t i = 0; i < num_pages; ++i) {
+            int32_t p = free_order[i];
+            if (p < 0 || p >= num_pages || seen[p])
+                return fail(PA_ERR_INVALID, "pa_pool_create: free_order is not a permutation");
+            seen[p] = 1;
+            order[i] = p;
+        }
+    } else {
+        for (int32_t i = 0; i < num_pages; ++i) order[i] = i;
+    }
+    pa_pool* pool = new (std::nothrow) pa_pool();
+    if (!pool) return fail(PA_ERR_INVALID, "pa_pool_create: out of host memory");
+    pool->num_pages = num_pages;
+    pool->page_size = page_size;
+    pool->free_stack.assign(order.rbegin(), order.rend());
+    pool->ref.assign(num_pages, 0);
+    *out = pool;
+    return PA_OK;
+}
+
+void pa_pool_destroy(pa_pool* pool) { delete pool; }
+
+pa_status pa_seq_new(pa_pool* pool, int32_t* seq_out) {
+    if (!pool || !seq_out) return fail(PA_ERR_INVALID, "pa_seq_new: null argument");
+    int32_t id = pool->new_id();
+    pool->seqs[id].live = true;
+    pool->seqs[id].len = 0;
+    pool->seqs[id].pages.clear();
+    *seq_out = id;
+    return PA_OK;
+}
+
+pa_status pa_seq_append(pa_pool* pool, int32_t seq, int32_t n_new, int32_t* slot_mapping_out,
+                        int32_t cow_pair_out[2], int32_t* n_cow_out) {
+    if (!pool) return fail(PA_ERR_INVALID, "pa_seq_append: pool is null");
+    if (!pool->live(seq)) return fail(PA_ERR_STATE, "pa_seq_append: sequence is not live");
+    if (n_new < 0) return fail(PA_ERR_INVALID, "pa_seq_append: n_new < 0");
+    if (n_new > 0 && !slot_mapping_out)
+        return fail(PA_ERR_INVALID, "pa_seq_append: slot_mapping_out is null");
+    auto& s = pool->seqs[seq];
+    const int64_t P = pool->page_size;
+    const int64_t L = s.len;
+    if (n_cow_out) *n_cow_out = 0;
+    if (n_new == 0) return PA_OK;
+    const bool cow = (L % P) != 0 && pool->ref[s.pages.back()] > 1;
+    const int64_t need = (L + n_new + P - 1) / P - (L + P - 1) / P + (cow ? 1 : 0);
+    if (need > (int64_t)pool->free_stack.size())
+        return fail(PA_ERR_NO_PAGES, "pa_seq_append: page pool exhausted");
+    if (cow && (!cow_pair_out || !n_cow_out))
+        return fail(PA_ERR_INVALID, "pa_seq_append: copy-on-write needed but cow outputs are null");
+    if (cow) {
+        int32_t src = s.pages.back();
+        int32_t dst = pool->pop();
+        pool->ref[src] -= 1;
+        pool->ref[dst] = 1;
+        s.pages.back() = dst;
+        cow_pair_out[0] = src;
+        cow_pair_out[1] = dst;
+        *n_cow_out = 1;
+    }
+    for (int32_t j = 0; j < n_new; ++j) {
+        int64_t t = L + j;
+        if (t % P == 0) {
+            int32_t p = pool->pop();
+            pool->ref[p] = 1;
+            s.pages.push_back(p);
+        }
+        slot_mapping_out[j] = (int32_t)(s.pages[t / P] * P + t % P);
+    }
+    s.len = L + n_new;
+    return PA_OK;
+}
+
+pa_status pa_seq_fork(pa_pool* pool, int32_t src_seq, int32_t* dst_seq_out) {
+    if (!pool || !dst_seq_out) return fail(PA_ERR_INVALID, "pa_seq_fork: null argument");
+    if (!pool->live(src_seq)) return fail(PA_ERR_STATE, "pa_seq_fork: source is not live");
+    int32_t id = pool->new_id();               // may grow seqs: take copies after
+    auto& d = pool->seqs[id];
+    const auto& s = pool->seqs[src_seq];
+    d.live = true;
+    d.len = s.len;
+    d.pages = s.pages;
+    for (int32_t p : d.pages) pool->ref[p] += 1;
+    *dst_seq_out = id;
+    return PA_OK;
+}
+
+pa_status pa_seq_cow(pa_pool* pool, int32_t seq, int32_t logical_page, int32_t pair_out[2]) {
+    if (!pool || !pair_out) return fail(PA_ERR_INVALID, "pa_seq_cow: null argument");
+    if (!pool->live(seq)) return fail(PA_ERR_STATE, "pa_seq_cow: sequence is not live");
+    auto& s = pool->seqs[seq];
+    if (logical_page < 0 || logical_page >= (int32_t)s.pages.size())
+        return fail(PA_ERR_INVALID, "pa_seq_cow: logical page out of range");
+    int32_t src = s.pages[logical_page];
+    if (pool->ref[src] < 2) return fail(PA_ERR_STATE, "pa_seq_cow: page is not shared");
+    if (pool->free_stack.empty()) return fail(PA_ERR_NO_PAGES, "pa_seq_cow: page pool exhausted");
+    int32_t dst = pool->pop();
+    pool->ref[src] -= 1;
+    pool->ref[dst] = 1;
+    s.pages[logical_page] = dst;
+    pair_out[0] = src;
+    pair_out[1] = dst;
+    return PA_OK;
+}
+
+pa_status pa_seq_free(pa_pool* pool, int32_t seq) {
+    if (!pool) return fail(PA_ERR_INVALID, "pa_seq_free: pool is null");
+    if (!pool->live(seq)) return fail(PA_ERR_STATE, "pa_seq_free: sequence is not live");
+    auto& s = pool->seqs[seq];
+    for (int32_t p : s.pages) {
+        if (--pool->ref[p] == 0) pool->free_stack.push_back(p);
+    }
+    s.pages.clear();
+    s.len = 0;
+    s.live = false;
+    return PA_OK;
+}
+
+pa_status pa_block_tables(const pa_pool* pool, const int32_t* seqs, int32_t n, int32_t max_pages,
+                          int32_t* bt_out, int32_t* kv_len_out) {
+    if (!pool || (n > 0 && (!seqs || !bt_out || !kv_len_out)) || n < 0 || max_pages < 0)
+        return fail(PA_ERR_INVALID, "pa_block_tables: bad argument");
+    for (int32_t i = 0; i < n; ++i) {
+        if (!pool->live(seqs[i])) return fail(PA_ERR_STATE, "pa_block_tables: sequence is not live");
+        if ((int32_t)pool->seqs[seqs[i]].pages.size() > max_pages)
+            return fail(PA_ERR_INVALID, "pa_block_tables: max_pages too small");
+        if (pool->seqs[seqs[i]].len > INT32_MAX)
+            return fail(PA_ERR_INVALID, "pa_block_tables: length overflows int32");
+    }
+    for (int32_t i = 0; i < n; ++i) {
+        const auto& s = pool->seqs[seqs[i]];
+        int32_t* row = bt_out + (int64_t)i * max_pages;
+        for (int32_t j = 0; j < max_pages; ++j)
+            row[j] = j < (int32_t)s.pages.size() ? s.pages[j] : -1;
+        kv_len_out[i] = (int32_t)s.len;
+    }
+    return PA_OK;
+}
+
+pa_status pa_pool_stats(const pa_pool* pool, int32_t* n_free_out, int32_t* refcount_out) {
+    if (!pool || !n_free_out) return fail(PA_ERR_INVALID, "pa_pool_stats: null argument");
+    *n_free_out = (int32_t)pool->free_stack.size();
+    if (refcount_out) std::copy(pool->ref.begin(), pool->ref.end(), refcount_out);
+    return PA_OK;
+}
+
+}  // extern "C"

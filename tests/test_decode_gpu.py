@@ -1,0 +1,177 @@
+"""pa_decode on the GPU against the float64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_185_amd as pa
+import workloads as W
+from gpu_util import assert_attention_close, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def run_decode(c, partition_tokens=0, host_lens=True, k=None, v=None, bt=None):
+    out = pa.pa_decode(to_dev(c.q), to_dev(c.k_pool) if k is None else k,
+                       to_dev(c.v_pool) if v is None else v,
+                       to_dev(c.block_tables if bt is None else bt), to_dev(c.kv_lens),
+                       float(c.scale), kv_lens_host=c.kv_lens if host_lens else None,
+                       partition_tokens=partition_tokens)
+    return to_host(out)
+
+
+def ref_decode(c):
+    return oracle.paged_decode(c.q, c.k_pool, c.v_pool, c.block_tables, c.kv_lens, c.scale)
+
+
+@pytest.mark.parametrize("mode", [0, -1, 256])
+def test_tiny_decode(mode):
+    c = W.tiny_decode()
+    assert_attention_close(run_decode(c, mode), ref_decode(c), f"tiny decode mode {mode}")
+
+
+CASES = [
+    # Hq, Hkv, D, P, lengths
+    (4, 2, 64, 16, [1, 15, 16, 17, 37, 200]),
+    (8, 8, 128, 16, [33, 64, 300]),
+    (32, 8, 128, 128, [1, 127, 128, 129, 1000, 3001]),
+    (16, 1, 128, 32, [700, 31, 32, 96]),
+    (16, 2, 64, 64, [5, 511, 513, 2100]),
+    (8, 4, 128, 256, [257, 1, 600]),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"Hq{c[0]}Hkv{c[1]}D{c[2]}P{c[3]}")
+@pytest.mark.parametrize("mode", [0, -1, 256])
+def test_decode_shapes(case, mode):
+    Hq, Hkv, D, P, lens = case
+    rng = np.random.default_rng(Hq * 1000 + D + P)
+    N = int(1.5 * sum((L + P - 1) // P for L in lens)) + 3
+    c = W.make_decode_case(rng, "shape", Hq, Hkv, D, P, lens, N)
+    assert_attention_close(run_decode(c, mode), ref_decode(c), f"{case} mode {mode}")
+
+
+def test_one_pass_equals_split_and_is_deterministic():
+    rng = np.random.default_rng(9)
+    c = W.make_decode_case(rng, "split", 32, 8, 128, 16, [4000, 257, 2048], 700)
+    a = run_decode(c, -1)
+    b = run_decode(c, 256)
+    d = run_decode(c, 1024)
+    # P enters the P.V product as binary16, rounded against the running maximum
+    # of whichever pass produced it; one pass and split therefore differ by a few
+    # binary16 roundings of P (observed <= 3e-5), far inside the oracle tolerance
+    np.testing.assert_allclose(a, b, rtol=1e-3, atol=2e-4)
+    np.testing.assert_allclose(a, d, rtol=1e-3, atol=2e-4)
+    assert np.array_equal(run_decode(c, 256), b)        # bitwise repeatable
+
+
+def test_page_permutation_bitwise():
+    c = W.tiny_decode()
+    base = run_decode(c, 256)
+    pi = np.random.default_rng(5).permutation(c.num_pages)
+    k2 = np.empty_like(c.k_pool)
+    v2 = np.empty_like(c.v_pool)
+    k2[pi] = c.k_pool
+    v2[pi] = c.v_pool
+    bt2 = np.where(c.block_tables >= 0, pi[np.maximum(c.block_tables, 0)], -1).astype(np.int32)
+    got = run_decode(c, 256, k=to_dev(k2), v=to_dev(v2), bt=bt2)
+    assert np.array_equal(base, got)
+
+
+def test_nan_poison_is_never_read():
+    c = W.tiny_decode()
+    base = run_decode(c, 0)
+    rng = np.random.default_rng(6)
+    k = c.k_pool.copy()
+    v = c.v_pool.copy()
+    k[np.isnan(k)] = (rng.standard_normal(int(np.isnan(k).sum())) * 100).astype(np.float16)
+    v[np.isnan(v)] = (rng.standard_normal(int(np.isnan(v).sum())) * 100).astype(np.float16)
+    got = run_decode(c, 0, k=to_dev(k), v=to_dev(v))
+    assert np.array_equal(base, got)
+    # garbage page ids past a sequence's last page are never dereferenced
+    bt = c.block_tables.copy()
+    bt[0, 3:] = 10 ** 9
+    assert np.array_equal(base, run_decode(c, 0, bt=bt))
+
+
+def test_decode_without_host_lengths():
+    c = W.tiny_decode()
+    assert_attention_close(run_decode(c, 0, host_lens=False), ref_decode(c), "no host lens")
+
+
+def test_workspace_too_small_is_rejected():
+    c = W.make_decode_case(np.random.default_rng(4), "ws", 4, 2, 64, 16, [1000, 37], 80)
+    with pytest.raises(pa.WorkspaceError):
+        pa.pa_decode(to_dev(c.q), to_dev(c.k_pool), to_dev(c.v_pool), to_dev(c.block_tables),
+                     to_dev(c.kv_lens), float(c.scale), kv_lens_host=c.kv_lens,
+                     partition_tokens=256,
+                     workspace=torch.empty(16, dtype=torch.uint8, device="cuda"))
+
+
+def test_qwen3_decode_full_size():
+    """8 sequences x 16384 tokens, GQA 32/8, D 128, P 128, in the benchmark's
+    launch configuration (automatic split) and forced one pass."""
+    c = W.qwen3_decode()
+    ref = ref_decode(c)
+    assert_attention_close(run_decode(c, 0), ref, "qwen3 decode auto")
+    assert_attention_close(run_decode(c, -1), ref, "qwen3 decode one pass")
+
+
+@pytest.mark.parametrize("P", [16, 128])
+def test_varlen_decode(P):
+    """64 sequences with log-uniform lengths in [256, 32768]; the oracle checks a
+    sample of 12 sequences including the shortest and the longest."""
+    c = W.varlen_decode(P)
+    got = run_decode(c, 0)
+    order = np.argsort(c.kv_lens)
+    pick = np.unique(np.concatenate([order[:3], order[-3:], np.linspace(0, 63, 6).astype(int)]))
+    ref = oracle.paged_decode(c.q[pick], c.k_pool, c.v_pool, c.block_tables[pick], c.kv_lens[pick],
+                              c.scale)
+    assert_attention_close(got[pick], ref, f"varlen P={P}")
+
+
+def test_sharing_and_copy_on_write():
+    """16 sequences share an 8192-token prefix (refcounted pages) and own a
+    1024-token suffix; decode, copy-on-write of the last shared page for 4
+    sequences, decode again: outputs bitwise unchanged."""
+    s = W.sharing_case()
+    Hkv, P, D = s.n_kv_heads, s.page_size, s.head_dim
+    pool = pa.Pool(s.num_pages, P, s.free_order)
+    model = oracle.AllocatorModel(s.num_pages, P, s.free_order)
+    k_pool, v_pool = W.nan_pools(s.num_pages, Hkv, P, D)
+    kd, vd = to_dev(k_pool), to_dev(v_pool)
+    s0 = pool.seq_new()
+    assert model.seq_new() == s0
+    slots, cow = pool.seq_append(s0, s.prefix_k.shape[0])
+    mslots, _ = model.seq_append(s0, s.prefix_k.shape[0])
+    assert cow is None and np.array_equal(slots, mslots)
+    pa.pa_reshape_and_cache(kd, vd, to_dev(s.prefix_k), to_dev(s.prefix_v), to_dev(slots))
+    k_pool, v_pool = oracle.reshape_and_cache(k_pool, v_pool, s.prefix_k, s.prefix_v, mslots)
+    seqs = [s0]
+    for _ in range(s.q.shape[0] - 1):
+        f = pool.seq_fork(s0)
+        assert model.seq_fork(s0) == f
+        seqs.append(f)
+    for i, sq in enumerate(seqs):
+        slots, cow = pool.seq_append(sq, s.suffix_k.shape[1])
+        mslots, mcow = model.seq_append(sq, s.suffix_k.shape[1])
+        assert cow is None and mcow is None and np.array_equal(slots, mslots)
+        pa.pa_reshape_and_cache(kd, vd, to_dev(s.suffix_k[i]), to_dev(s.suffix_v[i]), to_dev(slots))
+        k_pool, v_pool = oracle.reshape_and_cache(k_pool, v_pool, s.suffix_k[i], s.suffix_v[i], mslots)
+    max_pages = 72
+    bt, kv = pool.block_tables(seqs, max_pages)
+    mbt, mkv = model.block_tables(seqs, max_pages)
+    assert np.array_equal(bt, mbt) and np.array_equal(kv, mkv)
+    assert s.num_pages - pool.stats()[0] == 64 + 16 * 8
+    out1 = to_host(pa.pa_decode(to_dev(s.q), kd, vd, to_dev(bt), to_dev(kv), float(s.scale),
+                                kv_lens_host=kv))
+    ref = oracle.paged_decode(s.q, k_pool, v_pool, mbt, mkv, s.scale)
+    assert_attention_close(out1, ref, "shared prefix decode")
+    pairs = [pool.seq_cow(sq, 63) for sq in seqs[:4]]
+    assert pairs == [model.seq_cow(sq, 63) for sq in seqs[:4]]
+    pa.pa_copy_blocks([kd], [vd], pairs)
+    bt2, kv2 = pool.block_tables(seqs, max_pages)
+    assert not np.array_equal(bt2, bt)
+    out2 = to_host(pa.pa_decode(to_dev(s.q), kd, vd, to_dev(bt2), to_dev(kv2), float(s.scale),
+                                kv_lens_host=kv2))
+    assert np.array_equal(out1, out2)

@@ -15,6 +15,7 @@ import torch
 
 import oracle
 import workloads as W
+from pool_script import run_pool_script
 
 GOLD = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
@@ -360,52 +361,11 @@ def test_copy_blocks():
 
 # ---------------------------------------------------------------- allocator
 
-def run_pool_script(make_pool, script):
-    """Drive a pool object through the golden script; shared by the oracle model
-    test and the C library test.  ``make_pool(N, P, free_order)`` returns an
-    object with the AllocatorModel method names."""
-    pool = make_pool(script["num_pages"], script["page_size"], script["free_order"])
-    err_types = {"state": oracle.StateError, "no_pages": oracle.NoPagesError,
-                 "invalid": oracle.InvalidError}
-    for st in script["steps"]:
-        op = st["op"]
-        if "expect_error" in st:
-            before = (pool.stats()[0], pool.stats()[1].tolist())
-            with pytest.raises(err_types[st["expect_error"]]):
-                if op == "cow":
-                    pool.seq_cow(st["seq"], st["logical_page"])
-                elif op == "append":
-                    pool.seq_append(st["seq"], st["n"])
-                elif op == "free":
-                    pool.seq_free(st["seq"])
-            assert (pool.stats()[0], pool.stats()[1].tolist()) == before, st
-            continue
-        if op == "seq_new":
-            assert pool.seq_new() == st["expect_seq"]
-        elif op == "append":
-            slots, cow = pool.seq_append(st["seq"], st["n"])
-            assert list(slots) == st["expect_slots"], st
-            assert (None if cow is None else list(cow)) == st["expect_cow"], st
-        elif op == "fork":
-            assert pool.seq_fork(st["seq"]) == st["expect_seq"]
-        elif op == "cow":
-            assert list(pool.seq_cow(st["seq"], st["logical_page"])) == st["expect_pair"]
-        elif op == "free":
-            pool.seq_free(st["seq"])
-        elif op == "tables":
-            bt, kv = pool.block_tables(st["seqs"], st["max_pages"])
-            assert bt.tolist() == st["expect_bt"] and kv.tolist() == st["expect_len"]
-        elif op == "stats":
-            nf, ref = pool.stats()
-            assert nf == st["expect_free"] and list(ref) == st["expect_ref"]
-        else:
-            raise AssertionError(op)
-    return pool
-
-
 def test_allocator_golden_script():
     script = json.load(open(os.path.join(GOLD, "pool_script.json")))
-    run_pool_script(oracle.AllocatorModel, script)
+    run_pool_script(oracle.AllocatorModel, script,
+                    {"state": oracle.StateError, "no_pages": oracle.NoPagesError,
+                     "invalid": oracle.InvalidError})
 
 
 def _check_invariants(pool: oracle.AllocatorModel):

@@ -1,0 +1,159 @@
+"""pa_prefill (UA mixed-ubatch paged prefill) on the GPU against the oracle."""
+import numpy as np
+import pytest
+
+import oracle
+import paged_kv_cache_185_amd as pa
+import workloads as W
+from gpu_util import assert_attention_close, bits16, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def run_prefill(c, k_dev, v_dev, kv_splits=0, token_row=None):
+    row = c.token_row if token_row is None else token_row
+    out = pa.pa_prefill(to_dev(c.q), k_dev, v_dev, to_dev(c.block_tables), to_dev(row),
+                        to_dev(c.token_kv_len), to_dev(c.token_pos), float(c.scale),
+                        token_row_host=row, token_kv_len_host=c.token_kv_len,
+                        token_pos_host=c.token_pos, kv_splits=kv_splits)
+    return to_host(out)
+
+
+def write_new_tokens(c):
+    kd, vd = to_dev(c.k_pool), to_dev(c.v_pool)
+    pa.pa_reshape_and_cache(kd, vd, to_dev(c.k_new), to_dev(c.v_new), to_dev(c.slot_mapping))
+    k2, v2 = oracle.reshape_and_cache(c.k_pool, c.v_pool, c.k_new, c.v_new, c.slot_mapping)
+    assert np.array_equal(bits16(to_host(kd)), bits16(k2))
+    return kd, vd, k2, v2
+
+
+CASES = [
+    # Hq, Hkv, D, P, prefixes, new tokens, order
+    (4, 2, 64, 16, [37, 20, 0], [9, 12, 40], "round_robin"),
+    (32, 8, 128, 128, [300, 1000], [70, 33], "round_robin"),
+    (32, 8, 128, 64, [0, 130], [200, 64], "grouped"),
+    (8, 8, 128, 16, [50, 7, 333], [17, 130, 3], "round_robin"),
+    (16, 1, 64, 32, [100], [20], "grouped"),
+    (16, 2, 128, 128, [700, 5], [33, 61], "round_robin"),
+    (32, 4, 64, 16, [64, 65], [31, 2], "grouped"),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"Hq{c[0]}Hkv{c[1]}D{c[2]}P{c[3]}{c[6][0]}")
+@pytest.mark.parametrize("kv_splits", [0, 1, 3])
+def test_prefill_shapes(case, kv_splits):
+    Hq, Hkv, D, P, pre, new, order = case
+    rng = np.random.default_rng(Hq + D + P + sum(pre))
+    N = int(1.3 * sum((a + b + P - 1) // P for a, b in zip(pre, new))) + 4
+    c = W.make_prefill_case(rng, "shape", Hq, Hkv, D, P, N, pre, new, order)
+    kd, vd, k2, v2 = write_new_tokens(c)
+    got = run_prefill(c, kd, vd, kv_splits)
+    ref = oracle.paged_attention(c.q, k2, v2, c.block_tables, c.token_row, c.token_kv_len,
+                                 c.token_pos, c.scale)
+    assert_attention_close(got, ref, f"{case} splits {kv_splits}")
+
+
+def test_padding_tokens_get_zero_rows():
+    rng = np.random.default_rng(21)
+    c = W.make_prefill_case(rng, "pad", 8, 2, 64, 16, 40, [30, 50], [10, 14], "round_robin")
+    kd, vd, k2, v2 = write_new_tokens(c)
+    row = c.token_row.copy()
+    row[[0, 5, 23]] = -1
+    for splits in (1, 3):
+        got = run_prefill(c, kd, vd, splits, token_row=row)
+        ref = oracle.paged_attention(c.q, k2, v2, c.block_tables, row, c.token_kv_len,
+                                     c.token_pos, c.scale)
+        assert np.all(got[[0, 5, 23]] == 0)
+        assert_attention_close(got, ref, f"padding splits {splits}")
+
+
+def test_prefill_of_last_tokens_equals_decode():
+    """One token per sequence at position L-1 is a decode step."""
+    c = W.tiny_decode()
+    kd, vd = to_dev(c.k_pool), to_dev(c.v_pool)
+    dec = to_host(pa.pa_decode(to_dev(c.q), kd, vd, to_dev(c.block_tables), to_dev(c.kv_lens),
+                               float(c.scale), kv_lens_host=c.kv_lens))
+    rows = np.array([1, 0], dtype=np.int32)
+    pre = to_host(pa.pa_prefill(to_dev(c.q[::-1].copy()), kd, vd, to_dev(c.block_tables),
+                                to_dev(rows), to_dev(c.kv_lens[rows]), to_dev(c.kv_lens[rows] - 1),
+                                float(c.scale), token_row_host=rows,
+                                token_kv_len_host=c.kv_lens[rows],
+                                token_pos_host=c.kv_lens[rows] - 1))
+    # decode carries Q to ~22 bits, prefill rounds Q to binary16: compare at the
+    # attention tolerance, both against the oracle and against each other
+    ref = oracle.paged_decode(c.q, c.k_pool, c.v_pool, c.block_tables, c.kv_lens, c.scale)
+    assert_attention_close(pre[::-1], ref, "prefill as decode")
+    assert_attention_close(pre[::-1], dec.astype(np.float64), "prefill vs decode")
+
+
+def test_prefill_deterministic_and_permutation_invariant():
+    rng = np.random.default_rng(22)
+    c = W.make_prefill_case(rng, "perm", 32, 8, 128, 16, 120, [200, 90], [40, 24], "round_robin")
+    kd, vd, k2, v2 = write_new_tokens(c)
+    a = run_prefill(c, kd, vd, 3)
+    assert np.array_equal(a, run_prefill(c, kd, vd, 3))
+    pi = rng.permutation(c.num_pages)
+    kp = np.empty_like(k2)
+    vp = np.empty_like(v2)
+    kp[pi] = k2
+    vp[pi] = v2
+    bt = np.where(c.block_tables >= 0, pi[np.maximum(c.block_tables, 0)], -1).astype(np.int32)
+    out = pa.pa_prefill(to_dev(c.q), to_dev(kp), to_dev(vp), to_dev(bt), to_dev(c.token_row),
+                        to_dev(c.token_kv_len), to_dev(c.token_pos), float(c.scale),
+                        token_row_host=c.token_row, token_kv_len_host=c.token_kv_len,
+                        token_pos_host=c.token_pos, kv_splits=3)
+    assert np.array_equal(a, to_host(out))
+
+
+def test_ua_prefill_full_size():
+    """512 tokens interleaved from 8 sequences after 2K-16K prefixes, in the
+    automatic launch configuration; oracle on every 8th token (64 tokens, all
+    8 sequences)."""
+    c = W.ua_prefill()
+    kd, vd, k2, v2 = write_new_tokens(c)
+    got = run_prefill(c, kd, vd, 0)
+    pick = np.arange(0, 512, 7)
+    ref = oracle.paged_attention(c.q[pick], k2, v2, c.block_tables, c.token_row[pick],
+                                 c.token_kv_len[pick], c.token_pos[pick], c.scale)
+    assert_attention_close(got[pick], ref, "ua prefill")
+
+
+def test_chunked_prefill_sampled_ubatches():
+    """Fresh sequences prefilled in 512-token ubatches (the throughput workload),
+    shortened to 2 sequences x 4096 tokens; every ubatch runs, the oracle checks
+    the first, a middle and the last ubatch on sampled tokens."""
+    cp = W.chunked_prefill(n_seqs=2, seq_len=4096, chunk=512, num_pages=128)
+    P, Hkv, D = cp.page_size, cp.n_kv_heads, cp.head_dim
+    pool = pa.Pool(cp.num_pages, P, cp.free_order)
+    model = oracle.AllocatorModel(cp.num_pages, P, cp.free_order)
+    seqs = [pool.seq_new() for _ in range(cp.n_seqs)]
+    assert seqs == [model.seq_new() for _ in range(cp.n_seqs)]
+    k_pool, v_pool = W.nan_pools(cp.num_pages, Hkv, P, D)
+    kd, vd = to_dev(k_pool), to_dev(v_pool)
+    max_pages = cp.seq_len // P
+    checks = {0, 5, 15}
+    for j, (s, p0) in enumerate(cp.ubatches()):
+        n = cp.chunk
+        slots, cow = pool.seq_append(seqs[s], n)
+        mslots, _ = model.seq_append(seqs[s], n)
+        assert cow is None and np.array_equal(slots, mslots)
+        pa.pa_reshape_and_cache(kd, vd, to_dev(cp.k[s, p0:p0 + n]), to_dev(cp.v[s, p0:p0 + n]),
+                                to_dev(slots))
+        k_pool, v_pool = oracle.reshape_and_cache(k_pool, v_pool, cp.k[s, p0:p0 + n],
+                                                  cp.v[s, p0:p0 + n], mslots)
+        bt, kv = pool.block_tables(seqs, max_pages)
+        mbt, _ = model.block_tables(seqs, max_pages)
+        assert np.array_equal(bt, mbt)
+        row = np.full(n, s, dtype=np.int32)
+        kvl = np.full(n, p0 + n, dtype=np.int32)
+        pos = np.arange(p0, p0 + n, dtype=np.int32)
+        out = pa.pa_prefill(to_dev(cp.q[s, p0:p0 + n]), kd, vd, to_dev(bt), to_dev(row),
+                            to_dev(kvl), to_dev(pos), float(cp.scale), token_row_host=row,
+                            token_kv_len_host=kvl, token_pos_host=pos)
+        if j in checks:
+            got = to_host(out)
+            pick = np.array([0, 1, 63, 64, 200, 311, 510, 511])
+            ref = oracle.paged_attention(cp.q[s, p0:p0 + n][pick], k_pool, v_pool, mbt, row[pick],
+                                         kvl[pick], pos[pick], cp.scale)
+            assert_attention_close(got[pick], ref, f"ubatch {j}")
+    assert np.array_equal(bits16(to_host(kd)), bits16(k_pool))
