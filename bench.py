@@ -1,0 +1,315 @@
+#!/usr/bin/env python3
+"""Benchmark: paged decode valid-KV GB/s and paged prefill TFLOP/s on one MI355X.
+
+Decode workload (the headline value): 8 sequences x 16384 tokens, 32 query /
+8 KV heads, head_dim 128, binary16 pages of 128 tokens scattered in a
+2048-page pool with NaN free pages; one fp32 query per sequence.  A step is
+one pa_decode call (split-KV partition kernel + log-sum-exp reduce).  Steps
+rotate over `--layers` copies of the cache (distinct HBM addresses, like the
+layers of a model), so no step can be served from the 256 MB last-level cache
+by the previous one.  value = valid K+V bytes x steps / wall time between two
+device synchronizations.
+
+Prefill workload (reported beside it): 8 fresh sequences x 16384 tokens
+prefilled in 512-token ubatches, chunk-major; each ubatch is one
+pa_reshape_and_cache + one pa_prefill.  Host-side page allocation and block
+tables are prepared before timing; the 256 ubatches are captured once in a HIP
+graph and replayed.
+
+cpu_baseline: the float64 CPU oracle on the machine's host cores, timed on the full
+decode batch (one step) and on one prefill ubatch.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, published
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas"]
+        return max(n) if n else None
+    except Exception:
+        return None
+
+
+def bench_decode(args, pa, torch, W):
+    c = W.qwen3_decode()
+    dev = torch.device("cuda:0")
+    k0 = torch.from_numpy(c.k_pool).to(dev)
+    v0 = torch.from_numpy(c.v_pool).to(dev)
+    ks = [k0] + [k0.clone() for _ in range(args.layers - 1)]
+    vs = [v0] + [v0.clone() for _ in range(args.layers - 1)]
+    q = torch.from_numpy(c.q).to(dev)
+    bt = torch.from_numpy(c.block_tables).to(dev)
+    kl = torch.from_numpy(c.kv_lens).to(dev)
+    out = torch.empty_like(q)
+    desc = pa.cache_desc(k0, v0)
+    ws_bytes = pa.pa_decode_workspace_bytes(desc, c.n_seqs, c.n_q_heads, c.block_tables.shape[1],
+                                            c.kv_lens, args.partition_tokens)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        pa.pa_decode(q, ks[i % args.layers], vs[i % args.layers], bt, kl, float(c.scale),
+                     kv_lens_host=c.kv_lens, partition_tokens=args.partition_tokens, out=out,
+                     workspace=ws, stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    call_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    valid = W.decode_valid_bytes(c.kv_lens, c.n_kv_heads, c.head_dim)
+    res = {
+        "valid_bytes": valid,
+        "wall_s": wall,
+        "ms_per_step": wall * 1e3 / args.steps,
+        "call_ms_mean": float(call_ms.mean()),
+        "call_ms_median": float(np.median(call_ms)),
+        "call_ms_p10": float(np.percentile(call_ms, 10)),
+        "call_ms_p90": float(np.percentile(call_ms, 90)),
+        "workspace_bytes": ws_bytes,
+    }
+    return c, res
+
+
+def bench_prefill(args, pa, torch, W):
+    cp = W.chunked_prefill(n_seqs=8, seq_len=args.prefill_len, chunk=512, num_pages=2048)
+    dev = torch.device("cuda:0")
+    P, Hkv, D = cp.page_size, cp.n_kv_heads, cp.head_dim
+    kc, vc = W.nan_pools(cp.num_pages, Hkv, P, D)
+    kd = torch.from_numpy(kc).to(dev)
+    vd = torch.from_numpy(vc).to(dev)
+    del kc, vc
+    qd = torch.from_numpy(cp.q).to(dev)
+    knd = torch.from_numpy(cp.k).to(dev)
+    vnd = torch.from_numpy(cp.v).to(dev)
+    # host side: page allocation, block tables and per-token metadata for every ubatch
+    pool = pa.Pool(cp.num_pages, P, cp.free_order)
+    seqs = [pool.seq_new() for _ in range(cp.n_seqs)]
+    max_pages = cp.seq_len // P
+    plans = []
+    ws_need = 0
+    pairs = 0
+    for s, p0 in cp.ubatches():
+        n = cp.chunk
+        slots, cow = pool.seq_append(seqs[s], n)
+        assert cow is None
+        bt, _ = pool.block_tables(seqs, max_pages)
+        row = np.full(n, s, dtype=np.int32)
+        kvl = np.full(n, p0 + n, dtype=np.int32)
+        pos = np.arange(p0, p0 + n, dtype=np.int32)
+        ws_need = max(ws_need, pa.pa_prefill_workspace_bytes(pa.cache_desc(kd, vd), cp.n_q_heads,
+                                                              row, kvl, pos, 0))
+        pairs += W.prefill_pairs(kvl, pos)
+        plans.append(dict(s=s, p0=p0, n=n, slots=torch.from_numpy(slots).to(dev),
+                          bt=torch.from_numpy(bt).to(dev), row=torch.from_numpy(row).to(dev),
+                          kvl=torch.from_numpy(kvl).to(dev), pos=torch.from_numpy(pos).to(dev),
+                          row_h=row, kvl_h=kvl, pos_h=pos))
+    ws = torch.empty(max(ws_need, 1), dtype=torch.uint8, device=dev)
+    out = torch.empty(cp.chunk, cp.n_q_heads, D, dtype=torch.float32, device=dev)
+    flops = W.attention_flops(pairs, cp.n_q_heads, D)
+
+    def one_pass(stream):
+        for pl in plans:
+            s, p0, n = pl["s"], pl["p0"], pl["n"]
+            pa.pa_reshape_and_cache(kd, vd, knd[s, p0:p0 + n], vnd[s, p0:p0 + n], pl["slots"],
+                                    stream=stream)
+            pa.pa_prefill(qd[s, p0:p0 + n], kd, vd, pl["bt"], pl["row"], pl["kvl"], pl["pos"],
+                          float(cp.scale), token_row_host=pl["row_h"], token_kv_len_host=pl["kvl_h"],
+                          token_pos_host=pl["pos_h"], out=out, workspace=ws, stream=stream)
+
+    # eager pass once (warms the code paths and fills the cache)
+    one_pass(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            one_pass(torch.cuda.current_stream())
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    reps = args.prefill_reps
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(reps):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pass_ms = e0.elapsed_time(e1) / reps
+    return cp, plans, {
+        "ubatches": len(plans), "flops": flops, "pairs": pairs, "pass_ms": pass_ms,
+        "wall_ms_per_pass": wall * 1e3 / reps, "reps": reps,
+        "tflops": flops / (pass_ms * 1e-3) / 1e12,
+    }
+
+
+def cpu_baseline_decode(c, oracle):
+    t0 = time.perf_counter()
+    oracle.paged_decode(c.q, c.k_pool, c.v_pool, c.block_tables, c.kv_lens, c.scale)
+    return time.perf_counter() - t0
+
+
+def cpu_baseline_prefill(cp, oracle, W, ubatch_index=None):
+    """The oracle on one prefill ubatch (sequence 0, chunk 8 by default), with the
+    pool filled on the host by the oracle's own reshape_and_cache."""
+    chunk = cp.chunk
+    j = min(8, cp.seq_len // chunk - 1) if ubatch_index is None else ubatch_index
+    p0 = j * chunk
+    n_ctx = p0 + chunk
+    n_pages = n_ctx // cp.page_size
+    k, v = W.nan_pools(n_pages, cp.n_kv_heads, cp.page_size, cp.head_dim)
+    slots = np.arange(n_ctx, dtype=np.int32)
+    k, v = oracle.reshape_and_cache(k, v, cp.k[0, :n_ctx], cp.v[0, :n_ctx], slots)
+    bt = np.arange(n_pages, dtype=np.int32)[None, :]
+    row = np.zeros(chunk, np.int32)
+    kvl = np.full(chunk, n_ctx, np.int32)
+    pos = np.arange(p0, p0 + chunk, dtype=np.int32)
+    t0 = time.perf_counter()
+    oracle.paged_attention(cp.q[0, p0:p0 + chunk], k, v, bt, row, kvl, pos, cp.scale)
+    dt = time.perf_counter() - t0
+    flops = W.attention_flops(W.prefill_pairs(kvl, pos), cp.n_q_heads, cp.head_dim)
+    return dt, flops, f"sequence 0, ubatch {j} ({chunk} tokens at positions {p0}..{p0 + chunk - 1})"
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--layers", type=int, default=4, help="cache copies rotated over decode steps")
+    ap.add_argument("--partition-tokens", type=int, default=0)
+    ap.add_argument("--prefill-len", type=int, default=16384)
+    ap.add_argument("--prefill-reps", type=int, default=3)
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on exactly one GPU: this build measures one GPU's share of the "
+              "path; how it would shard across GPUs is described, not built.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import paged_kv_cache_185_amd as pa
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    log(f"library {pa.library_path()}")
+    log("decode: generating 8 x 16384 workload")
+    c, dec = bench_decode(args, pa, torch, W)
+    gbs = dec["valid_bytes"] * args.steps / dec["wall_s"] / 1e9
+    achieved = dec["valid_bytes"] / (dec["call_ms_mean"] * 1e-3) / 1e9
+    log(f"decode: {dec['call_ms_mean'] * 1e3:.1f} us/call (events), {gbs:.0f} GB/s wall")
+
+    pre = None
+    cp = None
+    if not args.no_prefill:
+        log("prefill: generating 8 x 16384 chunked workload")
+        cp, _, pre = bench_prefill(args, pa, torch, W)
+        log(f"prefill: {pre['pass_ms']:.2f} ms/pass, {pre['tflops']:.1f} TFLOP/s")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        log("cpu baseline: oracle decode on the full batch")
+        dt = cpu_baseline_decode(c, oracle)
+        cpu = {"value": dec["valid_bytes"] / dt / 1e9, "unit": "GB/s", "kind": "oracle",
+               "cores": blas_threads() or os.cpu_count(),
+               "host_cpus": os.cpu_count(), "affinity": len(os.sched_getaffinity(0)),
+               "sample": "one decode step over all 8 sequences x 16384 tokens (the full batch)",
+               "seconds": dt}
+        if cp is not None:
+            dtp, fl, what = cpu_baseline_prefill(cp, oracle, W)
+            cpu["prefill_tflops"] = fl / dtp / 1e12
+            cpu["prefill_sample"] = what
+            cpu["prefill_seconds"] = dtp
+        log(f"cpu baseline: {cpu['value']:.2f} GB/s")
+
+    result = {
+        "metric": "paged decode valid-KV GB/s (%HBM peak) + prefill TFLOP/s, 8 seqs x 16K, GQA32/8",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(dec["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": "paged decode: 8 sequences x 16384 tokens, 32 query / 8 KV heads, head_dim 128, "
+                        "f16 pages of 128 tokens in a 2048-page pool",
+            "step": "one pa_decode call (partition + reduce) over the batch",
+            "layers_rotated": args.layers,
+            "partition_tokens": args.partition_tokens,
+            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        },
+        "roofline": {
+            "kernel": "pa_decode (decode_partition_kernel + decode_reduce_kernel)",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "bytes_per_launch": dec["valid_bytes"],
+            "call_us_mean": round(dec["call_ms_mean"] * 1e3, 2),
+            "call_us_median": round(dec["call_ms_median"] * 1e3, 2),
+            "call_us_p10": round(dec["call_ms_p10"] * 1e3, 2),
+            "call_us_p90": round(dec["call_ms_p90"] * 1e3, 2),
+        },
+        "cpu_baseline": cpu,
+    }
+    if pre is not None:
+        result["prefill"] = {
+            "workload": f"8 fresh sequences x {args.prefill_len} tokens in 512-token ubatches "
+                        "(reshape_and_cache + pa_prefill each), HIP-graph replay",
+            "tflops": round(pre["tflops"], 2),
+            "frac_of_mfma_f16_peak": round(pre["tflops"] / MFMA_F16_PEAK_TFLOPS, 4),
+            "ms_per_pass": round(pre["pass_ms"], 4),
+            "flops_per_pass": pre["flops"],
+            "ubatches": pre["ubatches"],
+            "reps": pre["reps"],
+        }
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
