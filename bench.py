@@ -4,11 +4,14 @@
 Decode workload (the headline value): 8 sequences x 16384 tokens, 32 query /
 8 KV heads, head_dim 128, binary16 pages of 128 tokens scattered in a
 2048-page pool with NaN free pages; one fp32 query per sequence.  A step is
-one pa_decode call (split-KV partition kernel + log-sum-exp reduce).  Steps
-rotate over `--layers` copies of the cache (distinct HBM addresses, like the
-layers of a model), so no step can be served from the 256 MB last-level cache
-by the previous one.  value = valid K+V bytes x steps / wall time between two
-device synchronizations.
+one pa_decode call (one launch: split-KV partitions with the log-sum-exp reduce
+done by the last workgroup of each sequence and KV head).
+Steps rotate over `--layers` copies of the cache (distinct HBM addresses, like
+the layers of a model), so no step can be served from the 256 MB last-level
+cache by the previous one.  The K timed steps are one HIP graph replay (as a
+serving engine replays a captured decode step).  value = valid K+V bytes x
+steps / wall time between two device synchronizations; roofline.achieved =
+valid bytes / (HIP-event time of the replay on the launch stream / steps).
 
 Prefill workload (reported beside it): 8 fresh sequences x 16384 tokens
 prefilled in 512-token ubatches, chunk-major; each ubatch is one
@@ -51,7 +54,10 @@ def blas_threads():
 
 
 def bench_decode(args, pa, torch, W):
-    c = W.qwen3_decode()
+    if args.decode_workload == "qwen3":
+        c = W.qwen3_decode()
+    else:   # "varlen16" / "varlen128": 64 sequences, log-uniform lengths
+        c = W.varlen_decode(int(args.decode_workload[len("varlen"):]))
     dev = torch.device("cuda:0")
     k0 = torch.from_numpy(c.k_pool).to(dev)
     v0 = torch.from_numpy(c.v_pool).to(dev)
@@ -64,27 +70,49 @@ def bench_decode(args, pa, torch, W):
     desc = pa.cache_desc(k0, v0)
     ws_bytes = pa.pa_decode_workspace_bytes(desc, c.n_seqs, c.n_q_heads, c.block_tables.shape[1],
                                             c.kv_lens, args.partition_tokens)
-    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream()
+    ws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
 
-    def step(i):
-        pa.pa_decode(q, ks[i % args.layers], vs[i % args.layers], bt, kl, float(c.scale),
-                     kv_lens_host=c.kv_lens, partition_tokens=args.partition_tokens, out=out,
-                     workspace=ws, stream=stream)
+    def call(layer, stream):
+        pa.pa_decode(q, ks[layer], vs[layer], bt, kl, float(c.scale), kv_lens_host=c.kv_lens,
+                     partition_tokens=args.partition_tokens, out=out, workspace=ws, stream=stream)
 
-    for i in range(args.warmup):
-        step(i)
+    # The K timed steps are captured as one HIP graph (step i reads cache copy
+    # i % layers), as a serving engine replays a whole decode step; the
+    # warmup steps are a second graph replayed first.
+    call(0, torch.cuda.current_stream())
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
+
+    def capture(n):
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                for i in range(n):
+                    call(i % args.layers, torch.cuda.current_stream())
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        return g
+
+    stream = torch.cuda.current_stream()
+    if args.eager:
+        run = lambda: [call(i % args.layers, stream) for i in range(args.steps)]   # noqa: E731
+        for i in range(args.warmup):
+            call(i % args.layers, stream)
+    else:
+        timed = capture(args.steps)
+        if args.warmup:
+            capture(args.warmup).replay()
+        run = timed.replay
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        ev[i][0].record(stream)
-        step(i)
-        ev[i][1].record(stream)
+    e0.record(stream)
+    run()
+    e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    call_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    call_ms = np.array([e0.elapsed_time(e1) / args.steps])
     valid = W.decode_valid_bytes(c.kv_lens, c.n_kv_heads, c.head_dim)
     res = {
         "valid_bytes": valid,
@@ -207,10 +235,13 @@ def cpu_baseline_prefill(cp, oracle, W, ubatch_index=None):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=48)
+    ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--layers", type=int, default=4, help="cache copies rotated over decode steps")
     ap.add_argument("--partition-tokens", type=int, default=0)
+    ap.add_argument("--eager", action="store_true", help="time decode steps as eager calls, not graph replays")
+    ap.add_argument("--decode-workload", default="qwen3", choices=["qwen3", "varlen16", "varlen128"],
+                    help="qwen3 = the 8 x 16384 headline batch; varlen* = 64 log-uniform sequences")
     ap.add_argument("--prefill-len", type=int, default=16384)
     ap.add_argument("--prefill-reps", type=int, default=3)
     ap.add_argument("--no-prefill", action="store_true")
@@ -276,13 +307,13 @@ def main():
         "config": {
             "workload": "paged decode: 8 sequences x 16384 tokens, 32 query / 8 KV heads, head_dim 128, "
                         "f16 pages of 128 tokens in a 2048-page pool",
-            "step": "one pa_decode call (partition + reduce) over the batch",
+            "step": "one pa_decode call over the batch; the timed steps are one HIP graph replay",
             "layers_rotated": args.layers,
             "partition_tokens": args.partition_tokens,
             "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         },
         "roofline": {
-            "kernel": "pa_decode (decode_partition_kernel + decode_reduce_kernel)",
+            "kernel": "decode_partition_kernel (the single launch of pa_decode)",
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
@@ -291,9 +322,6 @@ def main():
             "traffic": None,
             "bytes_per_launch": dec["valid_bytes"],
             "call_us_mean": round(dec["call_ms_mean"] * 1e3, 2),
-            "call_us_median": round(dec["call_ms_median"] * 1e3, 2),
-            "call_us_p10": round(dec["call_ms_p10"] * 1e3, 2),
-            "call_us_p90": round(dec["call_ms_p90"] * 1e3, 2),
         },
         "cpu_baseline": cpu,
     }

@@ -156,14 +156,25 @@ pa_status pa_copy_blocks(const pa_cache_desc* desc, void* const* k_caches_host,
                          int32_t n_pairs, pa_stream stream);
 
 /* Workspace bytes pa_decode needs for these arguments (0 if it needs none).
- * Same meaning of arguments as pa_decode. */
+ * Same meaning of arguments as pa_decode.  A decode workspace starts with
+ * per-(sequence, KV head) completion counters (a region of
+ * max(64 KiB, 4 * n_seqs * n_kv_heads) bytes) followed by split partials.
+ * The counter region must be zero-filled before the workspace's first use;
+ * every pa_decode call puts each counter it used back to zero before its
+ * kernel ends, so the workspace can be reused by later calls on the same
+ * stream, including calls of other shapes as long as
+ * n_seqs * n_kv_heads <= 16384 (beyond that, re-zero it when the shape
+ * changes).  Calls that overlap in time need different workspaces, and
+ * nothing else may write to the workspace. */
 size_t pa_decode_workspace_bytes(const pa_cache_desc* desc, int32_t n_seqs, int32_t n_q_heads,
                                  int32_t max_pages, const int32_t* kv_lens_host,
                                  int32_t partition_tokens);
 
 /* Paged decode attention ([UA] 作品简介; [CF] section 3): one query token per
  * sequence at position kv_len-1, reading only the sequence's first kv_len
- * cells through its block-table row.
+ * cells through its block-table row.  One kernel launch: when sequences are
+ * split into partitions, the last workgroup of each (sequence, KV head)
+ * combines them (log-sum-exp reduce).
  *   q            device fp32 [n_seqs][n_q_heads][head_dim]
  *   out          device fp32 [n_seqs][n_q_heads][head_dim]
  *   block_tables device int32 [n_seqs][max_pages]; only the first

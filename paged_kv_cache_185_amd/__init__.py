@@ -241,7 +241,10 @@ def pa_decode_workspace_bytes(desc: CacheDesc, n_seqs: int, n_q_heads: int, max_
 
 def pa_decode(q, k_cache, v_cache, block_tables, kv_lens, scale: float, kv_lens_host=None,
               partition_tokens: int = 0, out=None, workspace=None, stream=None):
-    """Paged decode attention; q fp32 [S][Hq][D] -> out fp32 [S][Hq][D]."""
+    """Paged decode attention; q fp32 [S][Hq][D] -> out fp32 [S][Hq][D].
+
+    A caller-supplied ``workspace`` must be zero-filled before its first use;
+    pa_decode leaves its counter region zero-filled again."""
     import torch
     desc = cache_desc(k_cache, v_cache)
     S, Hq, D = (int(x) for x in q.shape)
@@ -253,7 +256,8 @@ def pa_decode(q, k_cache, v_cache, block_tables, kv_lens, scale: float, kv_lens_
         out = torch.empty_like(q)
     need = pa_decode_workspace_bytes(desc, S, Hq, max_pages, kl, partition_tokens)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        # zero-filled: the split's completion counters start at zero
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
     ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(_L().pa_decode(

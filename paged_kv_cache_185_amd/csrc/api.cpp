@@ -70,7 +70,7 @@ pa_status check_heads(const char* fn, const pa_cache_desc* d, int32_t n_q_heads)
 struct DecodePlan {
     int32_t partition_tokens = 0;
     int32_t n_part = 1;
-    size_t m_off = 0, l_off = 0, acc_off = 0, bytes = 0;
+    size_t cnt_off = 0, m_off = 0, l_off = 0, acc_off = 0, bytes = 0;
 };
 
 pa_status plan_decode(const pa_cache_desc* d, int32_t n_seqs, int32_t n_q_heads, int32_t max_pages,
@@ -99,19 +99,29 @@ pa_status plan_decode(const pa_cache_desc* d, int32_t n_seqs, int32_t n_q_heads,
             return fail(PA_ERR_INVALID, "pa_decode: partition_tokens must be a multiple of 256");
         T = partition_tokens;
     } else if (partition_tokens == 0) {
-        // aim for about four workgroups per compute unit (256 CUs)
+        // about one workgroup (4 waves streaming one partition) per compute
+        // unit: measured faster on the 256-CU part than more, shorter
+        // partitions, and it keeps the split partials small
         const int64_t work = total * d->n_kv_heads;
-        T = std::max<int64_t>(Q, round_up((work + 1023) / 1024, Q));
+        T = std::max<int64_t>(Q, round_up((work + 255) / 256, Q));
         if (T >= longest) T = round_up(longest, Q);
     } else {
         return fail(PA_ERR_INVALID, "pa_decode: partition_tokens must be -1, 0 or a positive multiple of 256");
     }
+    // the kernel stages one partition's page ids in LDS: cap the partition so
+    // the table fits (a "one pass" request beyond that becomes a split)
+    const int64_t t_cap = (int64_t)(kDecodeMaxPageEntries - 1) * d->page_size / Q * Q;
+    T = std::min(T, t_cap);
     plan->partition_tokens = (int32_t)std::min<int64_t>(T, INT32_MAX / 2);
     plan->n_part = (int32_t)((longest + T - 1) / T);
     if (plan->n_part > 1) {
         const size_t rows = (size_t)n_seqs * n_q_heads * plan->n_part;
-        plan->m_off = 0;
-        plan->l_off = align256(rows * 4);
+        // completion counters first, in a region of at least 64 KiB, so the
+        // partials of a call with n_seqs * n_kv_heads <= 16384 never land on
+        // another call's counters when one workspace serves several shapes
+        plan->cnt_off = 0;
+        plan->m_off = align256(std::max<size_t>(kDecodeCounterBytes, (size_t)n_seqs * d->n_kv_heads * 4));
+        plan->l_off = plan->m_off + align256(rows * 4);
         plan->acc_off = plan->l_off + align256(rows * 4);
         plan->bytes = plan->acc_off + align256(rows * (size_t)d->head_dim * 4);
     }
@@ -183,13 +193,18 @@ pa_status plan_prefill(const pa_cache_desc* d, int32_t n_tokens, int32_t n_q_hea
     } else if (kv_splits > 1) {
         split_tokens = round_up(std::max<int64_t>((max_kv + kv_splits - 1) / kv_splits, 1), KT);
     } else {
-        const int64_t need = (512 + d->n_kv_heads - 1) / d->n_kv_heads;   // ~2 workgroups per CU
+        // one 8-wave workgroup per compute unit (256 CUs): enough (tile, split)
+        // pairs per KV head to cover them, splits no shorter than 256 keys
+        const int64_t need = (256 + d->n_kv_heads - 1) / d->n_kv_heads;
         if ((int64_t)plan->tiles.size() >= need)
             split_tokens = round_up(std::max<int64_t>(max_kv, 1), KT);
         else
             split_tokens = std::max<int64_t>(256, round_up((sum_kv + need - 1) / need, KT));
     }
     split_tokens = std::min<int64_t>(split_tokens, round_up(std::max<int64_t>(max_kv, 1), KT));
+    // the kernel stages one split's page ids in LDS: very long ranges are split
+    const int64_t lds_cap = (int64_t)(kPrefillMaxPageEntries - 1) * d->page_size / KT * KT;
+    split_tokens = std::min(split_tokens, lds_cap);
     plan->split_tokens = (int32_t)split_tokens;
     plan->max_splits = 1;
     for (auto& t : plan->tiles) {
@@ -305,6 +320,7 @@ pa_status pa_decode(const pa_cache_desc* desc, const void* k_cache, const void* 
     a.kv_lens = kv_lens;
     if (plan.n_part > 1) {
         char* ws = (char*)workspace;
+        a.counters = (int32_t*)(ws + plan.cnt_off);
         a.part_m = (float*)(ws + plan.m_off);
         a.part_l = (float*)(ws + plan.l_off);
         a.part_acc = (float*)(ws + plan.acc_off);
@@ -320,10 +336,6 @@ pa_status pa_decode(const pa_cache_desc* desc, const void* k_cache, const void* 
     a.scale_log2 = (float)((double)scale * kLog2e);
     hipError_t e = launch_decode(a, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail("pa_decode", e);
-    if (plan.n_part > 1) {
-        e = launch_decode_reduce(a, (hipStream_t)stream);
-        if (e != hipSuccess) return hip_fail("pa_decode (reduce)", e);
-    }
     return PA_OK;
 }
 

@@ -7,7 +7,9 @@
 // section 3 -- a one-pass kernel for short contexts and a partition-plus-reduce
 // kernel for long ones.  Both are the same kernel here: a workgroup owns one
 // (sequence, KV head, partition); with one partition it writes the output,
-// otherwise (m, l, acc) partials that decode_reduce_kernel combines.
+// otherwise it writes (m, l, acc) partials and the last workgroup of that
+// (sequence, KV head) to finish combines them (log-sum-exp reduce), so a
+// decode is always a single launch.
 //
 // Design (MI355X):
 // * All G = Hq/Hkv query heads of a KV head are served by one pass over each
@@ -50,6 +52,15 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
                                                    __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
+// Device-scope (all XCDs) store and load, used only for the split partials.
+__device__ __forceinline__ void store_device(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ float load_device(const float* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __device__ __forceinline__ u32x4 ld16(const uint16_t* p) {
     return *reinterpret_cast<const u32x4*>(p);
 }
@@ -61,7 +72,7 @@ struct ChunkRegs {
 };
 
 template <int D>
-__global__ __launch_bounds__(256) void decode_partition_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256, 2) void decode_partition_kernel(DecodeArgs a) {
     constexpr int KS = D / 32;
     constexpr int NB = D / 16;
     const int part = blockIdx.x;
@@ -104,7 +115,17 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeArgs a) {
         }
     }
 
-    const int32_t* bt = a.block_tables + (int64_t)seq * a.max_pages;
+    // ---- page ids of this partition, staged once in LDS (entry i = logical page
+    // t0/P + i); every later lookup is an LDS read instead of a dependent load.
+    extern __shared__ int32_t sm_pages[];
+    {
+        const int32_t* bt = a.block_tables + (int64_t)seq * a.max_pages;
+        const int first = t0 / P;
+        const int n_pages = (t1 - 1) / P - first + 1;
+        for (int i = threadIdx.x; i < n_pages; i += blockDim.x) sm_pages[i] = bt[first + i];
+    }
+    __syncthreads();
+    const int page_base = t0 / P;
     const uint16_t* kc = a.k_cache;
     const uint16_t* vc = a.v_cache;
     // token row of this lane inside a chunk for K block 0 (block 1 is +4)
@@ -114,14 +135,14 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeArgs a) {
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
             const int t = min(c0 + tk + 4 * b, L - 1);
-            const int page = bt[t / P];
+            const int page = sm_pages[t / P - page_base];
             const uint16_t* row = kc + (((int64_t)page * Hkv + kvh) * P + (t % P)) * D + 8 * g;
 #pragma unroll
             for (int s = 0; s < KS; ++s) r.k[b][s] = ld16(row + 32 * s);
         }
         int tv = c0 + 8 * g;
         if (tv > L - 1) tv = (L - 1) & ~7;
-        const int vpage = bt[tv / P];
+        const int vpage = sm_pages[tv / P - page_base];
         const uint16_t* vrow = vc + (((int64_t)vpage * Hkv + kvh) * D + m16) * P + (tv % P);
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) r.v[nb] = ld16(vrow + (int64_t)16 * nb * P);
@@ -247,56 +268,92 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeArgs a) {
             a.out[((int64_t)seq * a.n_q_heads + qh) * D + d] = num / den;
         } else {
             const int64_t pi = ((int64_t)seq * a.n_q_heads + qh) * a.n_part + part;
-            a.part_acc[pi * D + d] = num;
+            store_device(a.part_acc + pi * D + d, num);
             if (d == 0) {
-                a.part_m[pi] = M;
-                a.part_l[pi] = den;
+                store_device(a.part_m + pi, M);
+                store_device(a.part_l + pi, den);
             }
         }
     }
-}
+    if (single) return;
 
-// One workgroup of D threads per (sequence, query head): log-sum-exp combine
-// of the sequence's partitions.  Sequences with a single partition were
-// written by the partition kernel and are skipped.
-template <int D>
-__global__ __launch_bounds__(D) void decode_reduce_kernel(DecodeArgs a) {
-    const int seq = blockIdx.x;
-    const int qh = blockIdx.y;
-    const int d = threadIdx.x;
-    const int L = a.kv_lens[seq];
+    // ---- fused log-sum-exp reduce.  The partials above are device-scope
+    // stores (written through to the device coherence point, past the
+    // per-XCD L2s); each wave waits until its stores are acknowledged, the
+    // barrier makes that true for the whole workgroup, and only then is the
+    // (device-scope) completion counter of this (sequence, KV head) bumped.
+    // The workgroup that brings the counter to the partition count reads all
+    // partials with device-scope loads, writes the output and puts the counter
+    // back to zero for the next call.  No L2 write-back or invalidate is needed.
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    __shared__ int s_last;
     const int np = (L + a.partition_tokens - 1) / a.partition_tokens;
-    if (np <= 1) return;
-    const int64_t base = ((int64_t)seq * a.n_q_heads + qh) * a.n_part;
-    float M = -INFINITY;
-    for (int p = 0; p < np; ++p) M = fmaxf(M, a.part_m[base + p]);
-    float num = 0.0f, den = 0.0f;
-    for (int p = 0; p < np; ++p) {
-        const float f = __builtin_amdgcn_exp2f(a.part_m[base + p] - M);
-        num += f * a.part_acc[(base + p) * D + d];
-        den += f * a.part_l[base + p];
+    int32_t* counter = a.counters + seq * Hkv + kvh;
+    if (threadIdx.x == 0) s_last = (atomicAdd(counter, 1) == np - 1);
+    __syncthreads();
+    if (!s_last) return;
+    constexpr int kFast = 16;   // partitions combined with one round of loads
+    for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x) {
+        const int h = idx / D;
+        const int d = idx - h * D;
+        const int qh = kvh * G + h;
+        const int64_t base = ((int64_t)seq * a.n_q_heads + qh) * a.n_part;
+        float num = 0.0f, den = 0.0f;
+        if (np <= kFast) {
+            float pm[kFast], pl[kFast], px[kFast];
+#pragma unroll
+            for (int p = 0; p < kFast; ++p) {
+                if (p < np) {
+                    pm[p] = load_device(a.part_m + base + p);
+                    pl[p] = load_device(a.part_l + base + p);
+                    px[p] = load_device(a.part_acc + (base + p) * D + d);
+                }
+            }
+            float M = pm[0];
+#pragma unroll
+            for (int p = 1; p < kFast; ++p)
+                if (p < np) M = fmaxf(M, pm[p]);
+#pragma unroll
+            for (int p = 0; p < kFast; ++p) {
+                if (p < np) {
+                    const float f = __builtin_amdgcn_exp2f(pm[p] - M);
+                    num += f * px[p];
+                    den += f * pl[p];
+                }
+            }
+        } else {
+            float M = -INFINITY;
+            for (int p = 0; p < np; ++p) M = fmaxf(M, load_device(a.part_m + base + p));
+            for (int p = 0; p < np; ++p) {
+                const float f = __builtin_amdgcn_exp2f(load_device(a.part_m + base + p) - M);
+                num += f * load_device(a.part_acc + (base + p) * D + d);
+                den += f * load_device(a.part_l + base + p);
+            }
+        }
+        a.out[((int64_t)seq * a.n_q_heads + qh) * D + d] = num / den;
     }
-    a.out[((int64_t)seq * a.n_q_heads + qh) * D + d] = num / den;
+    if (threadIdx.x == 0)
+        __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace
 
+int decode_page_table_entries(int partition_tokens, int page_size) {
+    // a partition starting at a multiple of partition_tokens touches at most
+    // ceil(partition_tokens / P) + 1 pages
+    return (partition_tokens + page_size - 1) / page_size + 1;
+}
+
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
     const dim3 grid((unsigned)a.n_part, (unsigned)a.n_kv_heads, (unsigned)a.n_seqs);
+    const size_t lds = sizeof(int32_t) * (size_t)decode_page_table_entries(a.partition_tokens, a.page_size);
     if (a.head_dim == 128)
-        hipLaunchKernelGGL(decode_partition_kernel<128>, grid, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL(decode_partition_kernel<128>, grid, dim3(256), lds, stream, a);
     else
-        hipLaunchKernelGGL(decode_partition_kernel<64>, grid, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL(decode_partition_kernel<64>, grid, dim3(256), lds, stream, a);
     return hipGetLastError();
 }
 
-hipError_t launch_decode_reduce(const DecodeArgs& a, hipStream_t stream) {
-    const dim3 grid((unsigned)a.n_seqs, (unsigned)a.n_q_heads);
-    if (a.head_dim == 128)
-        hipLaunchKernelGGL(decode_reduce_kernel<128>, grid, dim3(128), 0, stream, a);
-    else
-        hipLaunchKernelGGL(decode_reduce_kernel<64>, grid, dim3(64), 0, stream, a);
-    return hipGetLastError();
-}
 
 }  // namespace pa

@@ -36,6 +36,7 @@ struct DecodeArgs {
     float* part_m;      // [n_seqs][Hq][n_part] (log2 domain), or null for one pass
     float* part_l;      // [n_seqs][Hq][n_part]
     float* part_acc;    // [n_seqs][Hq][n_part][D]
+    int32_t* counters;  // [n_seqs][Hkv] finished partitions; zero between calls
     int32_t n_seqs;
     int32_t max_pages;
     int32_t n_q_heads;
@@ -48,6 +49,14 @@ struct DecodeArgs {
 };
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+// LDS entries the decode kernel needs for one partition's page ids.
+int decode_page_table_entries(int partition_tokens, int page_size);
+// Largest page-id table the decode kernel stages in LDS (32 KiB).
+constexpr int kDecodeMaxPageEntries = 8192;
+// Minimum size of the completion-counter region at the start of a decode
+// workspace (16384 counters).
+constexpr size_t kDecodeCounterBytes = 65536;
+
 
 // ---- prefill ---------------------------------------------------------------
 
@@ -85,20 +94,22 @@ struct PrefillArgs {
     int32_t head_dim;
     int32_t split_tokens;   // KV keys per split (multiple of the KV tile)
     int32_t max_splits;     // split slots per (token, head) in the partials
+    int32_t n_tiles;        // tiles in the current launch (set by launch_prefill)
     float scale_log2;
 };
 
 int prefill_tokens_per_tile(int group);   // query tokens per tile for GQA group size
 constexpr int kPrefillKvTile = 64;
+// LDS entries the prefill kernel needs for one split's page ids, and the cap.
+int prefill_page_table_entries(int split_tokens, int page_size);
+constexpr int kPrefillMaxPageEntries = 8192;
 
 hipError_t launch_prefill(const PrefillArgs& a, const PrefillTile* tiles, int n_tiles,
                           int grid_splits, hipStream_t stream);
 
-// Combine split partials (log2-domain m, l, acc) into out for `n_rows` rows of
-// `head_dim`; rows whose part count is 1 were written directly and are skipped
-// when `skip_single` is set.  Row r has its parts at r*max_parts.
+// Combine the split partials of every token (log-sum-exp); padding tokens get
+// zero rows.
 hipError_t launch_prefill_reduce(const PrefillArgs& a, hipStream_t stream);
-hipError_t launch_decode_reduce(const DecodeArgs& a, hipStream_t stream);
 
 hipError_t launch_zero_rows(float* out, const int32_t* token_row, int32_t n_tokens,
                             int32_t row_elems, hipStream_t stream);

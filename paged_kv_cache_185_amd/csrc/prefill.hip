@@ -6,13 +6,18 @@
 // valid cells of that sequence: cells t < min(kv_len, pos + 1).
 //
 // Design (MI355X):
-// * The host groups each sequence's tokens into tiles (128 query rows = 128/G
-//   tokens x G heads of one KV head).  A workgroup (4 waves) owns one
+// * The host groups each sequence's tokens into tiles of 256 query rows
+//   (256/G tokens x G heads of one KV head).  A workgroup (8 waves) owns one
 //   (tile, KV split, KV head); wave w owns 32 query columns.  The tile's
 //   tokens are found on the device by a ballot scan of token_row over the
 //   tile's ubatch index range, so no plan has to be copied to the device.
+//   Workgroups are numbered KV-head-fastest: on an 8-XCD part with 8 KV heads
+//   every workgroup of one head lands on the same XCD, and the tiles and
+//   splits of that head share its K/V through that XCD's L2.
 // * K and V tiles of 64 keys are staged through LDS (double buffered, XOR
-//   swizzled in 16-byte units) and shared by the 4 waves.
+//   swizzled in 16-byte units) and shared by the 8 waves.  Global loads run
+//   two tiles ahead of the MFMA work (two register sets), so about two
+//   tiles' worth of compute covers each load's latency.
 // * Both products run on v_mfma_f32_32x32x16_f16 with fp32 accumulation.
 //   Scores are computed transposed, S^T = K Q^T (rows = keys, columns =
 //   queries): each lane's C registers belong to one query column, so the
@@ -21,11 +26,16 @@
 //   permuted (bits 2 and 3 of the row index swapped) so that the 8 keys a lane
 //   holds for each P.V k-step are contiguous, which lets the V operand be one
 //   16-byte LDS read from the slot-innermost V tile.
-// * Q is rounded to binary16 (nearest even) once, P is rounded to binary16 for
-//   the P.V product and the row sum uses the rounded values.
-// * Masking is by select (scores -> -inf); V cells at or past the tile's
-//   visible end are zeroed in registers before they reach LDS, so NaN padding
-//   can never meet a zero weight.
+// * Q is multiplied by scale*log2(e) and rounded to binary16 once, so scores
+//   come out of the MFMA already in the log2 domain; P is rounded to binary16
+//   for the P.V product; row sums and accumulators are fp32.
+// * The running maximum is raised only when a new score exceeds it by more
+//   than 8 (log2 units): until then P <= 2^8 stays exact enough in binary16
+//   and the output rescale (a multiply per accumulator) is skipped.
+// * Masking is by select (scores -> -inf), and only on tiles that cross some
+//   token's visible end.  V cells at or past the tile's visible end are zeroed
+//   in registers before they reach LDS, so NaN padding never meets a zero
+//   weight.
 // * Long KV ranges are split across workgroups; each split writes (m, l, acc)
 //   partials that prefill_reduce_kernel combines by log-sum-exp.
 #include <math.h>
@@ -40,8 +50,11 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;
-constexpr int kKvTile = kPrefillKvTile;   // 64 keys per iteration
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRows = 32 * kWaves;          // query rows (token x head) per tile
+constexpr int kKvTile = kPrefillKvTile;     // 64 keys per iteration
+constexpr float kRescaleSlack = 8.0f;       // log2 units the max may lag by
 
 struct TileList {
     PrefillTile t[kMaxTilesPerLaunch];
@@ -61,7 +74,8 @@ template <int D>
 struct Smem {
     u32x4 k[2][kKvTile * D / 8];   // [buf][key][D/8 chunks], chunk swizzled by key % 8
     u32x4 v[2][D * kKvTile / 8];   // [buf][d][8 chunks of 8 keys], chunk swizzled by d % 8
-    int32_t tok[128];
+    int32_t tok[kRows];
+    int32_t min_vis;
 };
 
 template <int D>
@@ -73,29 +87,33 @@ struct Staging {
 };
 
 template <int D, int G>
-__global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a, TileList tl) {
+__global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, TileList tl) {
     constexpr int TPW = 32 / G;       // tokens per wave
     constexpr int KS = D / 16;        // k-steps of the score product
     constexpr int DB = D / 32;        // 32-row output blocks
     constexpr int CPR = D / 8;        // 16-byte chunks per K row
 
-    const PrefillTile tile = tl.t[blockIdx.x];
-    const int split = blockIdx.y;
-    const int kvh = blockIdx.z;
+    const int Hkv = a.n_kv_heads;
+    const int kvh = blockIdx.x % Hkv;
+    const int rest = blockIdx.x / Hkv;
+    const int tile_idx = rest % a.n_tiles;
+    const int split = rest / a.n_tiles;
+    const PrefillTile tile = tl.t[tile_idx];
     if (split >= tile.n_splits) return;
     const int kv_begin = split * a.split_tokens;
     const int kv_end = min(tile.kv_end, kv_begin + a.split_tokens);
 
     __shared__ Smem<D> sm;
+    extern __shared__ int32_t sm_pages[];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int col = lane & 31;
     const int hh = lane >> 5;
-    const int Hkv = a.n_kv_heads;
     const int P = a.page_size;
 
-    // ---- tokens of this tile: ballot scan of token_row[first..last]
+    // ---- tokens of this tile (ballot scan of token_row[first..last]) and the
+    // page ids of this split's key range
     if (wave == 0) {
         int found = 0;
         for (int base = tile.first; base <= tile.last && found < tile.count; base += 64) {
@@ -107,6 +125,13 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a, Til
             found += __popcll(mask);
         }
     }
+    if (tid == 0) sm.min_vis = kv_end;
+    const int page_base = kv_begin / P;
+    {
+        const int32_t* bt = a.block_tables + (int64_t)tile.row * a.max_pages;
+        const int n_pages = (kv_end - 1) / P - page_base + 1;
+        for (int i = tid; i < n_pages; i += kThreads) sm_pages[i] = bt[page_base + i];
+    }
     __syncthreads();
 
     // ---- this lane's query column
@@ -116,10 +141,12 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a, Til
     int n_vis = 0;
     if (tok >= 0) n_vis = min(a.token_kv_len[tok], a.token_pos[tok] + 1);
     const int qh = kvh * G + hq;
+    if (tok >= 0) atomicMin(&sm.min_vis, n_vis);
 
     u32x4 qb[KS];
     {
         const float* qrow = a.q + ((int64_t)(tok >= 0 ? tok : 0) * a.n_q_heads + qh) * D;
+        const float qs = tok >= 0 ? a.scale_log2 : 0.0f;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const int d0 = 16 * ks + 8 * hh;
@@ -128,12 +155,11 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a, Til
             const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
             f16x8 h;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) h[e] = (_Float16)(tok >= 0 ? xs[e] : 0.0f);
+            for (int e = 0; e < 8; ++e) h[e] = (_Float16)(xs[e] * qs);
             qb[ks] = __builtin_bit_cast(u32x4, h);
         }
     }
 
-    const int32_t* bt = a.block_tables + (int64_t)tile.row * a.max_pages;
     const uint16_t* kc = a.k_cache;
     const uint16_t* vc = a.v_cache;
 
@@ -145,7 +171,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a, Til
             const int key = id / CPR;
             const int c = id - key * CPR;
             const int t = min(t0 + key, kv_end - 1);
-            const int page = bt[t / P];
+            const int page = sm_pages[t / P - page_base];
             st.k[i] = *reinterpret_cast<const u32x4*>(
                 kc + (((int64_t)page * Hkv + kvh) * P + (t % P)) * D + 8 * c);
         }
@@ -156,7 +182,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a, Til
             const int c = id & 7;
             const int tb = t0 + 8 * c;
             const int tv = tb < kv_end ? tb : ((kv_end - 1) & ~7);
-            const int page = bt[tv / P];
+            const int page = sm_pages[tv / P - page_base];
             u32x4 x = *reinterpret_cast<const u32x4*>(
                 vc + (((int64_t)page * Hkv + kvh) * D + d) * P + (tv % P));
             const int nvalid = max(0, min(8, kv_end - tb));
@@ -196,22 +222,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a, Til
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[db][r] = 0.0f;
 
-    const int n_tiles = (kv_end - kv_begin + kKvTile - 1) / kKvTile;
-    {
-        Staging<D> st;
-        load_tile(kv_begin, st);
-        store_tile(0, st);
-    }
-    __syncthreads();
-
-    for (int it = 0; it < n_tiles; ++it) {
-        const int buf = it & 1;
-        const int t0 = kv_begin + it * kKvTile;
-        Staging<D> st;
-        const bool more = it + 1 < n_tiles;
-        if (more) load_tile(t0 + kKvTile, st);
-
-        // S^T = K Q^T for two 32-key blocks
+    // one 64-key tile from LDS buffer `buf`, keys t0..t0+63
+    auto compute_tile = [&](int buf, int t0, bool full) {
         f32x16 s[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
@@ -225,22 +237,32 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a, Til
                 s[kb] = mfma32(kop, qb[ks], s[kb]);
             }
         }
-        // scale, mask, online softmax (log2 domain)
-        float mx = -INFINITY;
+        if (!full) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = t0 + 32 * kb + 16 * (r >> 3) + 8 * hh + (r & 7);
+                    s[kb][r] = key < n_vis ? s[kb][r] : -INFINITY;
+                }
+        }
+        float mx = s[0][0];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int key = t0 + 32 * kb + 16 * (r >> 3) + 8 * hh + (r & 7);
-                const float x = s[kb][r] * a.scale_log2;
-                s[kb][r] = key < n_vis ? x : -INFINITY;
-                mx = fmaxf(mx, s[kb][r]);
-            }
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
         mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run, mx);
-        const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-        m_run = m_new;
+        // raise the running max only when the new one is well above it
+        const bool raise = mx > m_run + kRescaleSlack;
+        if (__ballot(raise)) {
+            const float m_new = raise ? mx : m_run;
+            const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+            l_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+            m_run = m_new;
+        }
+        const float m_use = m_run == -INFINITY ? 0.0f : m_run;
         u32x4 pb[4];
         float psum = 0.0f;
 #pragma unroll
@@ -248,16 +270,13 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a, Til
             f16x8 p;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const _Float16 pe =
-                    (_Float16)__builtin_amdgcn_exp2f(s[ks >> 1][8 * (ks & 1) + e] - m_use);
-                p[e] = pe;
-                psum += (float)pe;
+                const float pe = __builtin_amdgcn_exp2f(s[ks >> 1][8 * (ks & 1) + e] - m_use);
+                psum += pe;
+                p[e] = (_Float16)pe;
             }
             pb[ks] = __builtin_bit_cast(u32x4, p);
         }
-        l_run = l_run * alpha + psum;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+        l_run += psum;
         // O^T += V^T P^T
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
@@ -269,8 +288,34 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a, Til
                 acc[db] = mfma32(vop, pb[ks], acc[db]);
             }
         }
-        if (more) store_tile(buf ^ 1, st);
-        __syncthreads();
+    };
+
+    __syncthreads();   // sm.min_vis complete
+    const int min_vis = min(sm.min_vis, kv_end);
+    const int n_tiles = (kv_end - kv_begin + kKvTile - 1) / kKvTile;
+
+    // ---- pipeline: registers hold tiles it+1 and it+2 while tile it is
+    // computed from LDS; one barrier per tile
+    Staging<D> sa, sb;
+    load_tile(kv_begin, sa);
+    if (n_tiles > 1) load_tile(kv_begin + kKvTile, sb);
+    store_tile(0, sa);
+    __syncthreads();
+    for (int it = 0; it < n_tiles; it += 2) {
+        {   // even tile: computed from buffer 0; sb holds tile it+1
+            const int t0 = kv_begin + it * kKvTile;
+            if (it + 2 < n_tiles) load_tile(t0 + 2 * kKvTile, sa);
+            compute_tile(0, t0, t0 + kKvTile <= min_vis);
+            if (it + 1 < n_tiles) store_tile(1, sb);
+            __syncthreads();
+        }
+        if (it + 1 < n_tiles) {   // odd tile: computed from buffer 1; sa holds tile it+2
+            const int t0 = kv_begin + (it + 1) * kKvTile;
+            if (it + 3 < n_tiles) load_tile(t0 + 2 * kKvTile, sb);
+            compute_tile(1, t0, t0 + kKvTile <= min_vis);
+            if (it + 2 < n_tiles) store_tile(0, sa);
+            __syncthreads();
+        }
     }
 
     l_run += __shfl_xor(l_run, 32);
@@ -314,9 +359,11 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a, Til
 }
 
 // One workgroup of D threads per (token, query head).  Combines the splits
-// that hold keys visible to the token; padding tokens get a zero row.
+// that hold keys visible to the token, loading up to kFast of them in one
+// round; padding tokens get a zero row.
 template <int D>
 __global__ __launch_bounds__(D) void prefill_reduce_kernel(PrefillArgs a) {
+    constexpr int kFast = 16;
     const int tok = blockIdx.x;
     const int qh = blockIdx.y;
     const int d = threadIdx.x;
@@ -328,29 +375,53 @@ __global__ __launch_bounds__(D) void prefill_reduce_kernel(PrefillArgs a) {
     const int n_vis = min(a.token_kv_len[tok], a.token_pos[tok] + 1);
     const int ns = (n_vis + a.split_tokens - 1) / a.split_tokens;
     const int64_t base = ((int64_t)tok * a.n_q_heads + qh) * a.max_splits;
-    float M = -INFINITY;
-    for (int s = 0; s < ns; ++s) M = fmaxf(M, a.part_m[base + s]);
     float num = 0.0f, den = 0.0f;
-    for (int s = 0; s < ns; ++s) {
-        const float ms = a.part_m[base + s];
-        const float f = ms == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ms - M);
-        num += f * a.part_acc[(base + s) * D + d];
-        den += f * a.part_l[base + s];
+    if (ns <= kFast) {
+        float pm[kFast], pl[kFast], px[kFast];
+#pragma unroll
+        for (int s = 0; s < kFast; ++s) {
+            if (s < ns) {
+                pm[s] = a.part_m[base + s];
+                pl[s] = a.part_l[base + s];
+                px[s] = a.part_acc[(base + s) * D + d];
+            }
+        }
+        float M = pm[0];
+#pragma unroll
+        for (int s = 1; s < kFast; ++s)
+            if (s < ns) M = fmaxf(M, pm[s]);
+#pragma unroll
+        for (int s = 0; s < kFast; ++s) {
+            if (s < ns) {
+                const float f = pm[s] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(pm[s] - M);
+                num += f * px[s];
+                den += f * pl[s];
+            }
+        }
+    } else {
+        float M = -INFINITY;
+        for (int s = 0; s < ns; ++s) M = fmaxf(M, a.part_m[base + s]);
+        for (int s = 0; s < ns; ++s) {
+            const float ms = a.part_m[base + s];
+            const float f = ms == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ms - M);
+            num += f * a.part_acc[(base + s) * D + d];
+            den += f * a.part_l[base + s];
+        }
     }
     orow[d] = num / den;
 }
 
 template <int D>
-hipError_t launch_prefill_d(const PrefillArgs& a, const TileList& tl, int n_tiles, int splits,
+hipError_t launch_prefill_d(const PrefillArgs& a, const TileList& tl, int n_items, size_t lds,
                             hipStream_t stream) {
     const int G = a.n_q_heads / a.n_kv_heads;
-    const dim3 grid((unsigned)n_tiles, (unsigned)splits, (unsigned)a.n_kv_heads);
+    const dim3 grid((unsigned)n_items);
     switch (G) {
-        case 1: hipLaunchKernelGGL((prefill_kernel<D, 1>), grid, dim3(kThreads), 0, stream, a, tl); break;
-        case 2: hipLaunchKernelGGL((prefill_kernel<D, 2>), grid, dim3(kThreads), 0, stream, a, tl); break;
-        case 4: hipLaunchKernelGGL((prefill_kernel<D, 4>), grid, dim3(kThreads), 0, stream, a, tl); break;
-        case 8: hipLaunchKernelGGL((prefill_kernel<D, 8>), grid, dim3(kThreads), 0, stream, a, tl); break;
-        case 16: hipLaunchKernelGGL((prefill_kernel<D, 16>), grid, dim3(kThreads), 0, stream, a, tl); break;
+        case 1: hipLaunchKernelGGL((prefill_kernel<D, 1>), grid, dim3(kThreads), lds, stream, a, tl); break;
+        case 2: hipLaunchKernelGGL((prefill_kernel<D, 2>), grid, dim3(kThreads), lds, stream, a, tl); break;
+        case 4: hipLaunchKernelGGL((prefill_kernel<D, 4>), grid, dim3(kThreads), lds, stream, a, tl); break;
+        case 8: hipLaunchKernelGGL((prefill_kernel<D, 8>), grid, dim3(kThreads), lds, stream, a, tl); break;
+        case 16: hipLaunchKernelGGL((prefill_kernel<D, 16>), grid, dim3(kThreads), lds, stream, a, tl); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -358,7 +429,11 @@ hipError_t launch_prefill_d(const PrefillArgs& a, const TileList& tl, int n_tile
 
 }  // namespace
 
-int prefill_tokens_per_tile(int group) { return 128 / group; }
+int prefill_tokens_per_tile(int group) { return kRows / group; }
+
+int prefill_page_table_entries(int split_tokens, int page_size) {
+    return (split_tokens + page_size - 1) / page_size + 1;
+}
 
 hipError_t launch_prefill(const PrefillArgs& a, const PrefillTile* tiles, int n_tiles,
                           int grid_splits, hipStream_t stream) {
@@ -366,8 +441,12 @@ hipError_t launch_prefill(const PrefillArgs& a, const PrefillTile* tiles, int n_
     if (n_tiles > kMaxTilesPerLaunch) return hipErrorInvalidValue;
     TileList tl;
     for (int i = 0; i < n_tiles; ++i) tl.t[i] = tiles[i];
-    if (a.head_dim == 128) return launch_prefill_d<128>(a, tl, n_tiles, grid_splits, stream);
-    return launch_prefill_d<64>(a, tl, n_tiles, grid_splits, stream);
+    PrefillArgs b = a;
+    b.n_tiles = n_tiles;
+    const int n_items = n_tiles * grid_splits * a.n_kv_heads;
+    const size_t lds = sizeof(int32_t) * (size_t)prefill_page_table_entries(a.split_tokens, a.page_size);
+    if (a.head_dim == 128) return launch_prefill_d<128>(b, tl, n_items, lds, stream);
+    return launch_prefill_d<64>(b, tl, n_items, lds, stream);
 }
 
 hipError_t launch_prefill_reduce(const PrefillArgs& a, hipStream_t stream) {

@@ -175,3 +175,64 @@ def test_sharing_and_copy_on_write():
     out2 = to_host(pa.pa_decode(to_dev(s.q), kd, vd, to_dev(bt2), to_dev(kv2), float(s.scale),
                                 kv_lens_host=kv2))
     assert np.array_equal(out1, out2)
+
+
+def test_workspace_reused_across_calls_and_shapes():
+    """The split's completion counters return to zero after every call, so one
+    zero-filled workspace serves calls of different shapes and split sizes, and
+    a repeated call reproduces its first result bitwise."""
+    cases = [W.make_decode_case(np.random.default_rng(40 + i), "ws", Hq, Hkv, 128, P, lens, N)
+             for i, (Hq, Hkv, P, lens, N) in enumerate([(32, 8, 16, [3000, 700, 5000], 600),
+                                                      (8, 2, 128, [2000, 300], 30),
+                                                      (16, 16, 32, [1100] * 5, 200)])]
+    ws = torch.zeros(1 << 22, dtype=torch.uint8, device="cuda")
+    first = None
+    for rep in range(2):
+        for c, part in zip(cases, (256, 512, 0)):
+            out = to_host(pa.pa_decode(to_dev(c.q), to_dev(c.k_pool), to_dev(c.v_pool),
+                                       to_dev(c.block_tables), to_dev(c.kv_lens), float(c.scale),
+                                       kv_lens_host=c.kv_lens, partition_tokens=part, workspace=ws))
+            if rep == 0:
+                assert_attention_close(out, ref_decode(c), f"reuse {part}")
+                if first is None:
+                    first = out
+            elif c is cases[0]:
+                assert np.array_equal(out, first)
+    torch.cuda.synchronize()
+    # the counter region (the first 64 KiB of a decode workspace) is all zero again
+    assert int(ws[:65536].count_nonzero()) == 0
+
+
+def test_graph_replay_matches_eager():
+    """pa_decode captured in a HIP graph; every replay, with eager work and
+    synchronizations in between, equals the eager result bitwise."""
+    c = W.make_decode_case(np.random.default_rng(44), "graph", 32, 8, 128, 128, [9000, 4000, 1], 200)
+    q, k, v = to_dev(c.q), to_dev(c.k_pool), to_dev(c.v_pool)
+    bt, kl = to_dev(c.block_tables), to_dev(c.kv_lens)
+    eager = to_host(pa.pa_decode(q, k, v, bt, kl, float(c.scale), kv_lens_host=c.kv_lens,
+                                 partition_tokens=1024))
+    assert_attention_close(eager, ref_decode(c), "graph eager")
+    need = pa.pa_decode_workspace_bytes(pa.cache_desc(k, v), 3, 32, c.block_tables.shape[1],
+                                        c.kv_lens, 1024)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(q)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            pa.pa_decode(q, k, v, bt, kl, float(c.scale), kv_lens_host=c.kv_lens,
+                         partition_tokens=1024, out=out, workspace=ws,
+                         stream=torch.cuda.current_stream())
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for r in range(4):
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(to_host(out), eager), f"replay {r}"
+        # unrelated eager work between replays
+        other = pa.pa_decode(q, k, v, bt, kl, float(c.scale), kv_lens_host=c.kv_lens,
+                             partition_tokens=256)
+        torch.cuda.synchronize()
+        assert_attention_close(to_host(other), eager.astype(np.float64), "eager between replays")
