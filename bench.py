@@ -160,7 +160,7 @@ def bench_prefill(args, pa, torch, W):
                           bt=torch.from_numpy(bt).to(dev), row=torch.from_numpy(row).to(dev),
                           kvl=torch.from_numpy(kvl).to(dev), pos=torch.from_numpy(pos).to(dev),
                           row_h=row, kvl_h=kvl, pos_h=pos))
-    ws = torch.empty(max(ws_need, 1), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(max(ws_need, 1), dtype=torch.uint8, device=dev)
     out = torch.empty(cp.chunk, cp.n_q_heads, D, dtype=torch.float32, device=dev)
     flops = W.attention_flops(pairs, cp.n_q_heads, D)
 

@@ -32,7 +32,7 @@
  *     NULL is the default stream) and only launch kernels: they do not
  *     allocate, copy host memory to the device, or synchronize.
  *   - Host pointers are read during the call only.
- *   - Supported shapes: head_dim in {64, 128}; page_size a multiple of 16 in
+ *   - Supported shapes: head_dim in {64, 128}; page_size a power of two in
  *     [16, 1024]; n_q_heads a multiple of n_kv_heads with group size
  *     G = n_q_heads / n_kv_heads in {1, 2, 4, 8, 16}.  Other shapes return
  *     PA_ERR_UNSUPPORTED before anything is launched.
@@ -193,13 +193,22 @@ pa_status pa_decode(const pa_cache_desc* desc, const void* k_cache, const void* 
                     int32_t max_pages, int32_t n_q_heads, float scale, int32_t partition_tokens,
                     void* workspace, size_t workspace_bytes, pa_stream stream);
 
-/* Workspace bytes pa_prefill needs for these arguments. */
+/* Workspace bytes pa_prefill needs for these arguments (0 if no tile's KV
+ * range is split).  Same meaning of arguments as pa_prefill.  A prefill
+ * workspace starts with per-(tile, KV head) completion counters (a region of
+ * max(64 KiB, 4 * tiles * n_kv_heads) bytes, tiles <= n_tokens) followed by
+ * split partials; the counter region follows the same rules as pa_decode's:
+ * zero-filled before first use, left zeroed by every call, reusable across
+ * calls (and with pa_decode) on one stream while the region stays within
+ * 64 KiB, one workspace per concurrently running call. */
 size_t pa_prefill_workspace_bytes(const pa_cache_desc* desc, int32_t n_tokens, int32_t n_q_heads,
                                   const int32_t* token_row_host, const int32_t* token_kv_len_host,
                                   const int32_t* token_pos_host, int32_t kv_splits);
 
 /* UA paged prefill ([UA] 作品简介): attention for one ubatch whose tokens may
- * come from several sequences in any order.  Token i carries its sequence's
+ * come from several sequences in any order.  One kernel launch per 128 tiles
+ * (plus one that zeroes padding rows if there are any): when a tile's KV
+ * range is split, the last split to finish combines the partials.  Token i carries its sequence's
  * block-table row token_row[i] (-1 = padding token: its output row is set to
  * 0), the sequence's true KV length token_kv_len[i] (K/V of this ubatch
  * already written) and its position token_pos[i]; it attends to cells

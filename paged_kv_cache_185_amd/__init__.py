@@ -284,7 +284,9 @@ def pa_prefill(q, k_cache, v_cache, block_tables, token_row, token_kv_len, token
     """UA paged prefill; q fp32 [T][Hq][D] -> out fp32 [T][Hq][D].
 
     The host copies of the token arrays are taken from the device tensors if
-    not given (a synchronizing copy; pass them to avoid it)."""
+    not given (a synchronizing copy; pass them to avoid it).  A caller-supplied
+    ``workspace`` must be zero-filled before its first use (each call leaves
+    its counter region zeroed again)."""
     import torch
     desc = cache_desc(k_cache, v_cache)
     T, Hq, D = (int(x) for x in q.shape)
@@ -297,7 +299,7 @@ def pa_prefill(q, k_cache, v_cache, block_tables, token_row, token_kv_len, token
         out = torch.empty_like(q)
     need = pa_prefill_workspace_bytes(desc, Hq, rh, kh, ph, kv_splits)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
     ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     n_rows, max_pages = (int(x) for x in block_tables.shape)

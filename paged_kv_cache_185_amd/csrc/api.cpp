@@ -40,6 +40,12 @@ bool validate_env() {
 
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
+int32_t log2_exact(int32_t x) {
+    int32_t s = 0;
+    while ((1 << s) < x) ++s;
+    return s;
+}
+
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 pa_status check_desc(const char* fn, const pa_cache_desc* d) {
@@ -48,9 +54,9 @@ pa_status check_desc(const char* fn, const pa_cache_desc* d) {
         return fail(PA_ERR_INVALID, std::string(fn) + ": cache dimensions must be >= 1");
     if (d->head_dim != 64 && d->head_dim != 128)
         return fail(PA_ERR_UNSUPPORTED, std::string(fn) + ": head_dim must be 64 or 128");
-    if (d->page_size % 16 != 0 || d->page_size > 1024)
+    if (d->page_size < 16 || d->page_size > 1024 || (d->page_size & (d->page_size - 1)) != 0)
         return fail(PA_ERR_UNSUPPORTED,
-                    std::string(fn) + ": page_size must be a multiple of 16 in [16, 1024]");
+                    std::string(fn) + ": page_size must be a power of two in [16, 1024]");
     if ((int64_t)d->num_pages * d->page_size > INT32_MAX)
         return fail(PA_ERR_INVALID, std::string(fn) + ": num_pages * page_size overflows int32 slots");
     return PA_OK;
@@ -135,7 +141,7 @@ struct PrefillPlan {
     int32_t split_tokens = 0;
     int32_t max_splits = 1;
     bool has_padding = false;
-    size_t m_off = 0, l_off = 0, acc_off = 0, bytes = 0;
+    size_t ml_off = 0, acc_off = 0, bytes = 0;
 };
 
 pa_status plan_prefill(const pa_cache_desc* d, int32_t n_tokens, int32_t n_q_heads, int32_t n_rows,
@@ -212,11 +218,15 @@ pa_status plan_prefill(const pa_cache_desc* d, int32_t n_tokens, int32_t n_q_hea
         plan->max_splits = std::max(plan->max_splits, t.n_splits);
     }
     if (plan->max_splits > 1) {
-        const size_t rows = (size_t)n_tokens * n_q_heads * plan->max_splits;
-        plan->m_off = 0;
-        plan->l_off = align256(rows * 4);
-        plan->acc_off = plan->l_off + align256(rows * 4);
-        plan->bytes = plan->acc_off + align256(rows * (size_t)d->head_dim * 4);
+        // counters first (zero-filled region shared with pa_decode's
+        // convention), then per (tile, KV head, split) slot the (m, l) pairs
+        // and the accumulators of every lane of the workgroup
+        const size_t groups = plan->tiles.size() * (size_t)d->n_kv_heads;
+        const size_t slots = groups * plan->max_splits;
+        const size_t threads = (size_t)prefill_threads();
+        plan->ml_off = align256(std::max<size_t>(kDecodeCounterBytes, groups * 4));
+        plan->acc_off = plan->ml_off + align256(slots * threads * 2 * 4);
+        plan->bytes = plan->acc_off + align256(slots * threads * (size_t)d->head_dim / 2 * 4);
     }
     return PA_OK;
 }
@@ -330,6 +340,7 @@ pa_status pa_decode(const pa_cache_desc* desc, const void* k_cache, const void* 
     a.n_q_heads = n_q_heads;
     a.n_kv_heads = desc->n_kv_heads;
     a.page_size = desc->page_size;
+    a.page_shift = log2_exact(desc->page_size);
     a.head_dim = desc->head_dim;
     a.partition_tokens = plan.partition_tokens;
     a.n_part = plan.n_part;
@@ -387,8 +398,8 @@ pa_status pa_prefill(const pa_cache_desc* desc, const void* k_cache, const void*
     a.token_pos = token_pos;
     if (plan.max_splits > 1) {
         char* ws = (char*)workspace;
-        a.part_m = (float*)(ws + plan.m_off);
-        a.part_l = (float*)(ws + plan.l_off);
+        a.counters = (int32_t*)ws;
+        a.part_ml = (float*)(ws + plan.ml_off);
         a.part_acc = (float*)(ws + plan.acc_off);
     }
     a.n_tokens = n_tokens;
@@ -396,6 +407,7 @@ pa_status pa_prefill(const pa_cache_desc* desc, const void* k_cache, const void*
     a.n_q_heads = n_q_heads;
     a.n_kv_heads = desc->n_kv_heads;
     a.page_size = desc->page_size;
+    a.page_shift = log2_exact(desc->page_size);
     a.head_dim = desc->head_dim;
     a.split_tokens = plan.split_tokens;
     a.max_splits = plan.max_splits;
@@ -403,17 +415,17 @@ pa_status pa_prefill(const pa_cache_desc* desc, const void* k_cache, const void*
     const int n_tiles = (int)plan.tiles.size();
     for (int b = 0; b < n_tiles; b += kMaxTilesPerLaunch) {
         const int nb = std::min(kMaxTilesPerLaunch, n_tiles - b);
+        a.group_base = b * desc->n_kv_heads;
         hipError_t e = launch_prefill(a, plan.tiles.data() + b, nb, plan.max_splits,
                                       (hipStream_t)stream);
         if (e != hipSuccess) return hip_fail("pa_prefill", e);
     }
-    hipError_t e = hipSuccess;
-    if (plan.max_splits > 1)
-        e = launch_prefill_reduce(a, (hipStream_t)stream);
-    else if (plan.has_padding)
-        e = launch_zero_rows(out, token_row, n_tokens, n_q_heads * desc->head_dim,
-                             (hipStream_t)stream);
-    return e == hipSuccess ? PA_OK : hip_fail("pa_prefill (reduce)", e);
+    if (plan.has_padding) {
+        hipError_t e = launch_zero_rows(out, token_row, n_tokens, n_q_heads * desc->head_dim,
+                                        (hipStream_t)stream);
+        if (e != hipSuccess) return hip_fail("pa_prefill (padding rows)", e);
+    }
+    return PA_OK;
 }
 
 }  // extern "C"

@@ -12,62 +12,97 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// One thread writes 8 consecutive head_dim elements of one (token, KV head).
-// K rows are contiguous in the cache (one 16-byte store); V is stored with the
-// slot innermost, so its 8 elements go to 8 rows of the page-head block.
-template <bool kSrcF32>
+// One workgroup per (64 tokens, KV head).  K rows are contiguous in the cache:
+// each 16-byte chunk of a token's row is one store.  V is stored with the slot
+// innermost, so V goes through LDS as [d][token] and each run of 8 tokens whose
+// slots are consecutive and 8-aligned (the usual case: a sequence's new tokens
+// fill its pages in order) becomes one 16-byte store per d row; any other slot
+// pattern falls back to 2-byte stores.
+constexpr int kRcTokens = 64;
+
+template <bool kSrcF32, int D>
 __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
     uint16_t* __restrict__ k_cache, uint16_t* __restrict__ v_cache, const void* __restrict__ k_new,
     const void* __restrict__ v_new, const int32_t* __restrict__ slots, int32_t n_tokens,
-    int32_t n_kv_heads, int32_t page_size, int32_t head_dim) {
-    const int chunks = head_dim >> 3;
-    const int64_t per_token = (int64_t)n_kv_heads * chunks;
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= (int64_t)n_tokens * per_token) return;
-    const int32_t tok = (int32_t)(i / per_token);
-    const int32_t rem = (int32_t)(i - (int64_t)tok * per_token);
-    const int32_t h = rem / chunks;
-    const int32_t d0 = (rem - h * chunks) << 3;
-    const int32_t slot = slots[tok];
-    if (slot < 0) return;
-    const int32_t page = slot / page_size;
-    const int32_t off = slot - page * page_size;
-    const int64_t src = ((int64_t)tok * n_kv_heads + h) * head_dim + d0;
+    int32_t n_kv_heads, int32_t page_shift) {
+    constexpr int CH = D / 8;
+    constexpr int kRow = kRcTokens + 8;   // LDS row of one d: 144 bytes, 16-byte aligned
+    __shared__ uint16_t sv[D * kRow];
+    __shared__ int32_t sslot[kRcTokens];
+    const int h = blockIdx.y;
+    const int tok0 = blockIdx.x * kRcTokens;
+    const int tid = threadIdx.x;
+    const int P = 1 << page_shift;
+    if (tid < kRcTokens) sslot[tid] = tok0 + tid < n_tokens ? slots[tok0 + tid] : -1;
+    __syncthreads();
 
-    uint16_t kv[8], vv[8];
-    if constexpr (kSrcF32) {
-        const float* ks = reinterpret_cast<const float*>(k_new) + src;
-        const float* vs = reinterpret_cast<const float*>(v_new) + src;
-        const float4 k0 = *reinterpret_cast<const float4*>(ks);
-        const float4 k1 = *reinterpret_cast<const float4*>(ks + 4);
-        const float4 v0 = *reinterpret_cast<const float4*>(vs);
-        const float4 v1 = *reinterpret_cast<const float4*>(vs + 4);
-        const float kf[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
-        const float vf[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    for (int task = tid; task < kRcTokens * CH; task += 256) {
+        const int tl = task / CH;
+        const int c = task - tl * CH;
+        const int32_t slot = sslot[tl];
+        if (slot < 0) continue;
+        const int64_t src = ((int64_t)(tok0 + tl) * n_kv_heads + h) * D + 8 * c;
+        uint16_t kv[8], vv[8];
+        if constexpr (kSrcF32) {
+            const float* ks = reinterpret_cast<const float*>(k_new) + src;
+            const float* vs = reinterpret_cast<const float*>(v_new) + src;
+            const float4 k0 = *reinterpret_cast<const float4*>(ks);
+            const float4 k1 = *reinterpret_cast<const float4*>(ks + 4);
+            const float4 v0 = *reinterpret_cast<const float4*>(vs);
+            const float4 v1 = *reinterpret_cast<const float4*>(vs + 4);
+            const float kf[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
+            const float vf[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            kv[e] = __builtin_bit_cast(uint16_t, (_Float16)kf[e]);
-            vv[e] = __builtin_bit_cast(uint16_t, (_Float16)vf[e]);
+            for (int e = 0; e < 8; ++e) {
+                kv[e] = __builtin_bit_cast(uint16_t, (_Float16)kf[e]);
+                vv[e] = __builtin_bit_cast(uint16_t, (_Float16)vf[e]);
+            }
+        } else {
+            const u32x4 kk = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(k_new) + src);
+            const u32x4 vw = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(v_new) + src);
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                kv[2 * w] = (uint16_t)(kk[w] & 0xffffu);
+                kv[2 * w + 1] = (uint16_t)(kk[w] >> 16);
+                vv[2 * w] = (uint16_t)(vw[w] & 0xffffu);
+                vv[2 * w + 1] = (uint16_t)(vw[w] >> 16);
+            }
         }
-    } else {
-        const u32x4 kk = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(k_new) + src);
-        const u32x4 vw = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(v_new) + src);
+        u32x4 kout;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            kv[2 * w] = (uint16_t)(kk[w] & 0xffffu);
-            kv[2 * w + 1] = (uint16_t)(kk[w] >> 16);
-            vv[2 * w] = (uint16_t)(vw[w] & 0xffffu);
-            vv[2 * w + 1] = (uint16_t)(vw[w] >> 16);
+        for (int w = 0; w < 4; ++w) kout[w] = (uint32_t)kv[2 * w] | ((uint32_t)kv[2 * w + 1] << 16);
+        const int64_t page = slot >> page_shift;
+        const int off = slot & (P - 1);
+        *reinterpret_cast<u32x4*>(k_cache + ((page * n_kv_heads + h) * P + off) * D + 8 * c) = kout;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sv[(8 * c + e) * kRow + tl] = vv[e];
+    }
+    __syncthreads();
+
+    // V rows: task (d, g) covers tokens 8g..8g+7 of row d; lanes of a wave
+    // take consecutive g, so a run of pages in order is written contiguously
+    for (int task = tid; task < D * (kRcTokens / 8); task += 256) {
+        const int d = task >> 3;
+        const int g = task & 7;
+        const int32_t s0 = sslot[8 * g];
+        bool run = s0 >= 0 && (s0 & 7) == 0;
+#pragma unroll
+        for (int j = 1; j < 8; ++j) run = run && sslot[8 * g + j] == s0 + j;
+        if (run) {
+            const int64_t page = s0 >> page_shift;
+            const int off = s0 & (P - 1);
+            *reinterpret_cast<u32x4*>(v_cache + ((page * n_kv_heads + h) * D + d) * P + off) =
+                *reinterpret_cast<const u32x4*>(&sv[d * kRow + 8 * g]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int32_t sj = sslot[8 * g + j];
+                if (sj < 0) continue;
+                const int64_t page = sj >> page_shift;
+                v_cache[((page * n_kv_heads + h) * D + d) * P + (sj & (P - 1))] = sv[d * kRow + 8 * g + j];
+            }
         }
     }
-    u32x4 kout;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) kout[w] = (uint32_t)kv[2 * w] | ((uint32_t)kv[2 * w + 1] << 16);
-    uint16_t* kdst = k_cache + (((int64_t)page * n_kv_heads + h) * page_size + off) * head_dim + d0;
-    *reinterpret_cast<u32x4*>(kdst) = kout;
-    uint16_t* vdst = v_cache + (((int64_t)page * n_kv_heads + h) * head_dim + d0) * page_size + off;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) vdst[(int64_t)e * page_size] = vv[e];
 }
 
 struct CopyBlocksArgs {
@@ -106,17 +141,27 @@ hipError_t launch_reshape_and_cache(void* k_cache, void* v_cache, const void* k_
                                     const void* v_new, bool src_f32, const int32_t* slots,
                                     int32_t n_tokens, int32_t n_kv_heads, int32_t page_size,
                                     int32_t head_dim, hipStream_t stream) {
-    const int64_t threads = (int64_t)n_tokens * n_kv_heads * (head_dim / 8);
-    if (threads == 0) return hipSuccess;
-    const dim3 grid((unsigned)((threads + 255) / 256));
-    if (src_f32)
-        hipLaunchKernelGGL(reshape_and_cache_kernel<true>, grid, dim3(256), 0, stream,
-                           (uint16_t*)k_cache, (uint16_t*)v_cache, k_new, v_new, slots, n_tokens,
-                           n_kv_heads, page_size, head_dim);
-    else
-        hipLaunchKernelGGL(reshape_and_cache_kernel<false>, grid, dim3(256), 0, stream,
-                           (uint16_t*)k_cache, (uint16_t*)v_cache, k_new, v_new, slots, n_tokens,
-                           n_kv_heads, page_size, head_dim);
+    if (n_tokens == 0) return hipSuccess;
+    int shift = 0;
+    while ((1 << shift) < page_size) ++shift;
+    const dim3 grid((unsigned)((n_tokens + kRcTokens - 1) / kRcTokens), (unsigned)n_kv_heads);
+    auto* kc = (uint16_t*)k_cache;
+    auto* vc = (uint16_t*)v_cache;
+    if (head_dim == 128) {
+        if (src_f32)
+            hipLaunchKernelGGL((reshape_and_cache_kernel<true, 128>), grid, dim3(256), 0, stream, kc, vc,
+                               k_new, v_new, slots, n_tokens, n_kv_heads, shift);
+        else
+            hipLaunchKernelGGL((reshape_and_cache_kernel<false, 128>), grid, dim3(256), 0, stream, kc, vc,
+                               k_new, v_new, slots, n_tokens, n_kv_heads, shift);
+    } else {
+        if (src_f32)
+            hipLaunchKernelGGL((reshape_and_cache_kernel<true, 64>), grid, dim3(256), 0, stream, kc, vc,
+                               k_new, v_new, slots, n_tokens, n_kv_heads, shift);
+        else
+            hipLaunchKernelGGL((reshape_and_cache_kernel<false, 64>), grid, dim3(256), 0, stream, kc, vc,
+                               k_new, v_new, slots, n_tokens, n_kv_heads, shift);
+    }
     return hipGetLastError();
 }
 

@@ -120,12 +120,14 @@ __global__ __launch_bounds__(256, 2) void decode_partition_kernel(DecodeArgs a) 
     extern __shared__ int32_t sm_pages[];
     {
         const int32_t* bt = a.block_tables + (int64_t)seq * a.max_pages;
-        const int first = t0 / P;
-        const int n_pages = (t1 - 1) / P - first + 1;
+        const int first = t0 >> a.page_shift;
+        const int n_pages = ((t1 - 1) >> a.page_shift) - first + 1;
         for (int i = threadIdx.x; i < n_pages; i += blockDim.x) sm_pages[i] = bt[first + i];
     }
     __syncthreads();
-    const int page_base = t0 / P;
+    const int page_base = t0 >> a.page_shift;
+    const int sh = a.page_shift;
+    const int64_t page_elems = (int64_t)Hkv * P * D;   // one page of one cache, all heads
     const uint16_t* kc = a.k_cache;
     const uint16_t* vc = a.v_cache;
     // token row of this lane inside a chunk for K block 0 (block 1 is +4)
@@ -135,15 +137,15 @@ __global__ __launch_bounds__(256, 2) void decode_partition_kernel(DecodeArgs a) 
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
             const int t = min(c0 + tk + 4 * b, L - 1);
-            const int page = sm_pages[t / P - page_base];
-            const uint16_t* row = kc + (((int64_t)page * Hkv + kvh) * P + (t % P)) * D + 8 * g;
+            const int page = sm_pages[(t >> sh) - page_base];
+            const uint16_t* row = kc + page * page_elems + ((kvh * P + (t & (P - 1))) * D + 8 * g);
 #pragma unroll
             for (int s = 0; s < KS; ++s) r.k[b][s] = ld16(row + 32 * s);
         }
         int tv = c0 + 8 * g;
         if (tv > L - 1) tv = (L - 1) & ~7;
-        const int vpage = sm_pages[tv / P - page_base];
-        const uint16_t* vrow = vc + (((int64_t)vpage * Hkv + kvh) * D + m16) * P + (tv % P);
+        const int vpage = sm_pages[(tv >> sh) - page_base];
+        const uint16_t* vrow = vc + vpage * page_elems + ((kvh * D + m16) * P + (tv & (P - 1)));
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) r.v[nb] = ld16(vrow + (int64_t)16 * nb * P);
     };

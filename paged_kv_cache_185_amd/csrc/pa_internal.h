@@ -41,7 +41,8 @@ struct DecodeArgs {
     int32_t max_pages;
     int32_t n_q_heads;
     int32_t n_kv_heads;
-    int32_t page_size;
+    int32_t page_size;  // a power of two
+    int32_t page_shift; // log2(page_size)
     int32_t head_dim;
     int32_t partition_tokens;
     int32_t n_part;     // partitions per sequence in the grid
@@ -83,22 +84,27 @@ struct PrefillArgs {
     const int32_t* token_row;
     const int32_t* token_kv_len;
     const int32_t* token_pos;
-    float* part_m;      // [n_tokens][Hq][max_splits] or null when no tile splits
-    float* part_l;
-    float* part_acc;    // [n_tokens][Hq][max_splits][D]
+    // split partials (null when no tile splits), slot = group*max_splits+split
+    // with group = tile*Hkv + kvh over all tiles of the call:
+    int32_t* counters;  // [groups], zero between calls
+    float* part_ml;     // [slot][threads][2]  (m, half-wave l)
+    float* part_acc;    // [slot][D/8][threads][4]  accumulators in lane order
     int32_t n_tokens;
     int32_t max_pages;
     int32_t n_q_heads;
     int32_t n_kv_heads;
-    int32_t page_size;
+    int32_t page_size;  // a power of two
+    int32_t page_shift; // log2(page_size)
     int32_t head_dim;
     int32_t split_tokens;   // KV keys per split (multiple of the KV tile)
     int32_t max_splits;     // split slots per (token, head) in the partials
     int32_t n_tiles;        // tiles in the current launch (set by launch_prefill)
+    int32_t group_base;     // first group of the current launch
     float scale_log2;
 };
 
 int prefill_tokens_per_tile(int group);   // query tokens per tile for GQA group size
+int prefill_threads();                    // threads per prefill workgroup
 constexpr int kPrefillKvTile = 64;
 // LDS entries the prefill kernel needs for one split's page ids, and the cap.
 int prefill_page_table_entries(int split_tokens, int page_size);
@@ -107,10 +113,7 @@ constexpr int kPrefillMaxPageEntries = 8192;
 hipError_t launch_prefill(const PrefillArgs& a, const PrefillTile* tiles, int n_tiles,
                           int grid_splits, hipStream_t stream);
 
-// Combine the split partials of every token (log-sum-exp); padding tokens get
-// zero rows.
-hipError_t launch_prefill_reduce(const PrefillArgs& a, hipStream_t stream);
-
+// Zero the output rows of padding tokens (token_row < 0).
 hipError_t launch_zero_rows(float* out, const int32_t* token_row, int32_t n_tokens,
                             int32_t row_elems, hipStream_t stream);
 

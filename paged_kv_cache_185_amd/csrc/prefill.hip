@@ -15,9 +15,12 @@
 //   every workgroup of one head lands on the same XCD, and the tiles and
 //   splits of that head share its K/V through that XCD's L2.
 // * K and V tiles of 64 keys are staged through LDS (double buffered, XOR
-//   swizzled in 16-byte units) and shared by the 8 waves.  Global loads run
-//   two tiles ahead of the MFMA work (two register sets), so about two
-//   tiles' worth of compute covers each load's latency.
+//   swizzled in 16-byte units so the MFMA operand reads are free of bank
+//   conflicts) and shared by the 8 waves.  Global loads run two tiles ahead
+//   of the MFMA work (two register sets); MFMA operands are read from LDS a
+//   k-step or two ahead of their use.  When the page size is a multiple of 64
+//   a tile never crosses a page, and its addresses are one scalar page base
+//   plus fixed per-thread offsets.
 // * Both products run on v_mfma_f32_32x32x16_f16 with fp32 accumulation.
 //   Scores are computed transposed, S^T = K Q^T (rows = keys, columns =
 //   queries): each lane's C registers belong to one query column, so the
@@ -33,11 +36,13 @@
 //   than 8 (log2 units): until then P <= 2^8 stays exact enough in binary16
 //   and the output rescale (a multiply per accumulator) is skipped.
 // * Masking is by select (scores -> -inf), and only on tiles that cross some
-//   token's visible end.  V cells at or past the tile's visible end are zeroed
-//   in registers before they reach LDS, so NaN padding never meets a zero
-//   weight.
-// * Long KV ranges are split across workgroups; each split writes (m, l, acc)
-//   partials that prefill_reduce_kernel combines by log-sum-exp.
+//   token's visible end.  V cells at or past the split's visible end are
+//   zeroed in registers before they reach LDS (only the last tile has any),
+//   so NaN padding never meets a zero weight.
+// * Long KV ranges are split across workgroups.  Each split stores its
+//   (m, l, acc) partial; the last split of a (tile, KV head) to finish, found
+//   with a device-scope counter, combines them by log-sum-exp in the same
+//   launch.
 #include <math.h>
 
 #include "pa_internal.h"
@@ -47,8 +52,10 @@ namespace pa {
 namespace {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
@@ -65,6 +72,36 @@ __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
                                                    __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
+// Device-scope (all XCDs) 8-byte store, used only for split partials.
+__device__ __forceinline__ void store_device2(uint64_t* p, float x, float y) {
+    const uint64_t v = (uint64_t)__float_as_uint(x) | ((uint64_t)__float_as_uint(y) << 32);
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// LDS swizzles (16-byte units).  K rows are D*2 bytes; with 64 banks of 4 bytes
+// a 16-lane group of 16-byte reads is conflict-free when its 16 chunks cover
+// all 256 bytes of the bank range.  The score operand reads 16 different key
+// rows at one chunk index, so the chunk is XORed with the key's row index
+// within a 256-byte bank line (key & 15 for 256-byte rows; for 128-byte rows
+// two keys share a line and (key >> 1) & 7 is used).  V rows (64 keys) are
+// 128 bytes, read 16 rows at a time: (d >> 1) & 7.
+template <int D>
+__device__ __forceinline__ int kswz(int key) {
+    return D == 128 ? (key & 15) : ((key >> 1) & 7);
+}
+
+__device__ __forceinline__ int vswz(int d) { return (d >> 1) & 7; }
+
+// Workgroup barrier that orders LDS only.  __syncthreads() also fences global
+// memory, which waits for every outstanding global load (s_waitcnt vmcnt(0))
+// and so would drain the K/V prefetch at each tile; the pipeline below only
+// communicates through LDS across waves.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // score row i of a 32-key block <-> key offset (bits 2 and 3 swapped)
 __device__ __forceinline__ int kappa(int i) {
     return (i & ~0xC) | ((i & 4) << 1) | ((i & 8) >> 1);
@@ -76,6 +113,7 @@ struct Smem {
     u32x4 v[2][D * kKvTile / 8];   // [buf][d][8 chunks of 8 keys], chunk swizzled by d % 8
     int32_t tok[kRows];
     int32_t min_vis;
+    int32_t last;   // this workgroup combines the tile's splits
 };
 
 template <int D>
@@ -84,9 +122,13 @@ struct Staging {
     static constexpr int VC = D * kKvTile / 8 / kThreads;   // (V)
     u32x4 k[KC];
     u32x4 v[VC];
+    int t0;   // first key of the tile held
 };
 
-template <int D, int G>
+// ONE_PAGE: the page size is a multiple of the 64-key tile, so every tile
+// lies inside one page and its addresses are one scalar page base plus fixed
+// per-thread offsets.
+template <int D, int G, bool ONE_PAGE>
 __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, TileList tl) {
     constexpr int TPW = 32 / G;       // tokens per wave
     constexpr int KS = D / 16;        // k-steps of the score product
@@ -126,10 +168,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, Til
         }
     }
     if (tid == 0) sm.min_vis = kv_end;
-    const int page_base = kv_begin / P;
+    const int sh = a.page_shift;
+    const int page_base = kv_begin >> sh;
     {
         const int32_t* bt = a.block_tables + (int64_t)tile.row * a.max_pages;
-        const int n_pages = (kv_end - 1) / P - page_base + 1;
+        const int n_pages = ((kv_end - 1) >> sh) - page_base + 1;
         for (int i = tid; i < n_pages; i += kThreads) sm_pages[i] = bt[page_base + i];
     }
     __syncthreads();
@@ -163,54 +206,95 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, Til
     const uint16_t* kc = a.k_cache;
     const uint16_t* vc = a.v_cache;
 
-    // ---- global -> registers for one KV tile starting at key t0
-    auto load_tile = [&](int t0, Staging<D>& st) {
+    // ---- global -> registers for one KV tile starting at key t0.  Thread
+    // tid moves the K chunks (key, c) = (id / CPR, id % CPR) and the V chunks
+    // (d, c) = (id / 8, id % 8) of id = tid + kThreads*i; everything but the
+    // page lookup is fixed per thread.  Loads and stores are branch-free
+    // (tiles past the end are clamped onto the last one, the V mask is an
+    // unconditional AND at store time), so the in-order vmcnt accounting is
+    // the same on every path and a store waits only for its own tile.
+    const int64_t page_elems = (int64_t)Hkv * P * D;   // one page of one cache, all heads
+    const int k_head_off = kvh * P * D;
+    const int last_t0 = kv_begin + ((kv_end - kv_begin - 1) / kKvTile) * kKvTile;
+    // per-thread element offsets of the K chunks (key, c) and V chunks (d, c)
+    // inside one tile when it lies in one page
+    int koff[Staging<D>::KC], voff[Staging<D>::VC];
 #pragma unroll
-        for (int i = 0; i < Staging<D>::KC; ++i) {
-            const int id = tid + kThreads * i;
-            const int key = id / CPR;
-            const int c = id - key * CPR;
-            const int t = min(t0 + key, kv_end - 1);
-            const int page = sm_pages[t / P - page_base];
-            st.k[i] = *reinterpret_cast<const u32x4*>(
-                kc + (((int64_t)page * Hkv + kvh) * P + (t % P)) * D + 8 * c);
-        }
+    for (int i = 0; i < Staging<D>::KC; ++i) {
+        const int id = tid + kThreads * i;
+        koff[i] = (id / CPR) * D + 8 * (id % CPR);
+    }
 #pragma unroll
-        for (int i = 0; i < Staging<D>::VC; ++i) {
-            const int id = tid + kThreads * i;
-            const int d = id >> 3;
-            const int c = id & 7;
+    for (int i = 0; i < Staging<D>::VC; ++i) {
+        const int id = tid + kThreads * i;
+        voff[i] = (id >> 3) * P + 8 * (id & 7);
+    }
+    auto load_tile = [&](int t0_req, Staging<D>& st) {
+        const int t0 = min(t0_req, last_t0);
+        st.t0 = t0;
+        if constexpr (ONE_PAGE) {
+            // keys past kv_end in the tile are still inside its (allocated)
+            // page: K there is masked out of the scores, V is zeroed at store
+            const int page = __builtin_amdgcn_readfirstlane(sm_pages[(t0 >> sh) - page_base]);
+            const int64_t base = page * page_elems + (k_head_off + (t0 & (P - 1)) * D);
+            const uint16_t* kb = kc + base;
+            const uint16_t* vb = vc + page * page_elems + (k_head_off + (t0 & (P - 1)));
+#pragma unroll
+            for (int i = 0; i < Staging<D>::KC; ++i)
+                st.k[i] = *reinterpret_cast<const u32x4*>(kb + koff[i]);
+#pragma unroll
+            for (int i = 0; i < Staging<D>::VC; ++i)
+                st.v[i] = *reinterpret_cast<const u32x4*>(vb + voff[i]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < Staging<D>::KC; ++i) {
+                const int id = tid + kThreads * i;
+                const int key = id / CPR;
+                const int c = id % CPR;
+                const int t = min(t0 + key, kv_end - 1);
+                const int page = sm_pages[(t >> sh) - page_base];
+                st.k[i] = *reinterpret_cast<const u32x4*>(
+                    kc + page * page_elems + (k_head_off + (t & (P - 1)) * D + 8 * c));
+            }
+            const int c = tid & 7;
             const int tb = t0 + 8 * c;
             const int tv = tb < kv_end ? tb : ((kv_end - 1) & ~7);
-            const int page = sm_pages[tv / P - page_base];
-            u32x4 x = *reinterpret_cast<const u32x4*>(
-                vc + (((int64_t)page * Hkv + kvh) * D + d) * P + (tv % P));
-            const int nvalid = max(0, min(8, kv_end - tb));
-            if (nvalid < 8) {
+            const int vpage = sm_pages[(tv >> sh) - page_base];
+            const uint16_t* vbase = vc + vpage * page_elems + (k_head_off + (tv & (P - 1)));
 #pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    const uint32_t mk = (2 * w < nvalid ? 0x0000ffffu : 0u) |
-                                        (2 * w + 1 < nvalid ? 0xffff0000u : 0u);
-                    x[w] &= mk;
-                }
+            for (int i = 0; i < Staging<D>::VC; ++i) {
+                const int d = (tid + kThreads * i) >> 3;
+                st.v[i] = *reinterpret_cast<const u32x4*>(vbase + d * P);
             }
-            st.v[i] = x;
         }
     };
-    auto store_tile = [&](int buf, const Staging<D>& st) {
+    auto store_tile = [&](int buf, Staging<D>& st) {
 #pragma unroll
         for (int i = 0; i < Staging<D>::KC; ++i) {
             const int id = tid + kThreads * i;
             const int key = id / CPR;
-            const int c = id - key * CPR;
-            sm.k[buf][key * CPR + (c ^ (key & 7))] = st.k[i];
+            const int c = id % CPR;
+            sm.k[buf][key * CPR + (c ^ kswz<D>(key))] = st.k[i];
+        }
+        // zero the V halves of keys at or past the visible end (only the last
+        // tile of a split has any)
+        if (st.t0 + kKvTile > kv_end) {
+            const int nvalid = max(0, min(8, kv_end - (st.t0 + 8 * (tid & 7))));
+            uint32_t mk[4];
+#pragma unroll
+            for (int w = 0; w < 4; ++w)
+                mk[w] = (2 * w < nvalid ? 0x0000ffffu : 0u) | (2 * w + 1 < nvalid ? 0xffff0000u : 0u);
+#pragma unroll
+            for (int i = 0; i < Staging<D>::VC; ++i)
+#pragma unroll
+                for (int w = 0; w < 4; ++w) st.v[i][w] &= mk[w];
         }
 #pragma unroll
         for (int i = 0; i < Staging<D>::VC; ++i) {
             const int id = tid + kThreads * i;
             const int d = id >> 3;
             const int c = id & 7;
-            sm.v[buf][d * 8 + (c ^ (d & 7))] = st.v[i];
+            sm.v[buf][d * 8 + (c ^ vswz(d))] = st.v[i];
         }
     };
 
@@ -222,20 +306,38 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, Til
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[db][r] = 0.0f;
 
-    // one 64-key tile from LDS buffer `buf`, keys t0..t0+63
+    // one 64-key tile from LDS buffer `buf`, keys t0..t0+63; `full` (uniform)
+    // says every query column of the tile sees all 64 keys
     auto compute_tile = [&](int buf, int t0, bool full) {
         f32x16 s[2];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) s[kb][r] = 0.0f;
-            const int krow = 32 * kb + kappa(col);
+        // K operands are read from LDS two k-steps ahead of their MFMAs, and
+        // the two 32-key blocks alternate so consecutive MFMAs are independent
+        const int krow0 = kappa(col);
+        const int krow1 = 32 + kappa(col);
+        auto kread = [&](int ks, int krow) {
+            const int c = 2 * ks + hh;
+            return sm.k[buf][krow * CPR + (c ^ kswz<D>(krow))];
+        };
+        u32x4 ka[3], kb1[3];
+        ka[0] = kread(0, krow0);
+        kb1[0] = kread(0, krow1);
+        ka[1] = kread(1, krow0);
+        kb1[1] = kread(1, krow1);
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const int c = 2 * ks + hh;
-                const u32x4 kop = sm.k[buf][krow * CPR + (c ^ (krow & 7))];
-                s[kb] = mfma32(kop, qb[ks], s[kb]);
+        for (int ks = 0; ks < KS; ++ks) {
+            if (ks + 2 < KS) {
+                ka[(ks + 2) % 3] = kread(ks + 2, krow0);
+                kb1[(ks + 2) % 3] = kread(ks + 2, krow1);
             }
+            // keep the scheduler from sinking the reads back to their use
+            __builtin_amdgcn_sched_barrier(0);
+            s[0] = mfma32(ka[ks % 3], qb[ks], s[0]);
+            s[1] = mfma32(kb1[ks % 3], qb[ks], s[1]);
+            __builtin_amdgcn_sched_barrier(0);
         }
         if (!full) {
 #pragma unroll
@@ -251,7 +353,13 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, Til
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        {
+            // the other half-wave holds the same query column's other keys:
+            // one of the two swap results is mx itself, the other its partner
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                             false, false);
+            mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        }
         // raise the running max only when the new one is well above it
         const bool raise = mx > m_run + kRescaleSlack;
         if (__ballot(raise)) {
@@ -263,66 +371,79 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, Til
             m_run = m_new;
         }
         const float m_use = m_run == -INFINITY ? 0.0f : m_run;
-        u32x4 pb[4];
-        float psum = 0.0f;
+        // O^T += V^T P^T, 16 keys per k-step: P is made just before its MFMAs
+        // and the V operands of the next k-step are read from LDS meanwhile
+        auto vread = [&](int ks, int db) {
+            const int c = 2 * ks + hh;
+            const int d = 32 * db + col;
+            return sm.v[buf][d * 8 + (c ^ vswz(d))];
+        };
+        u32x4 vcur[DB], vnext[DB];
+#pragma unroll
+        for (int db = 0; db < DB; ++db) vcur[db] = vread(0, db);
+        // the row sum adds the binary16 P the MFMA consumes, two per dot2
+        const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+        float psum[2] = {0.0f, 0.0f};
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
+            if (ks + 1 < 4) {
+#pragma unroll
+                for (int db = 0; db < DB; ++db) vnext[db] = vread(ks + 1, db);
+            }
             f16x8 p;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float pe = __builtin_amdgcn_exp2f(s[ks >> 1][8 * (ks & 1) + e] - m_use);
-                psum += pe;
-                p[e] = (_Float16)pe;
-            }
-            pb[ks] = __builtin_bit_cast(u32x4, p);
-        }
-        l_run += psum;
-        // O^T += V^T P^T
+            for (int e = 0; e < 8; ++e)
+                p[e] = (_Float16)__builtin_amdgcn_exp2f(s[ks >> 1][8 * (ks & 1) + e] - m_use);
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            const int c = 2 * ks + hh;
-#pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                const int d = 32 * db + col;
-                const u32x4 vop = sm.v[buf][d * 8 + (c ^ (d & 7))];
-                acc[db] = mfma32(vop, pb[ks], acc[db]);
+            for (int e = 0; e < 8; e += 2) {
+                const f16x2 pp = {p[e], p[e + 1]};
+                psum[(e >> 1) & 1] = __builtin_amdgcn_fdot2(pp, ones, psum[(e >> 1) & 1], false);
             }
+            const u32x4 pb = __builtin_bit_cast(u32x4, p);
+#pragma unroll
+            for (int db = 0; db < DB; ++db) acc[db] = mfma32(vcur[db], pb, acc[db]);
+#pragma unroll
+            for (int db = 0; db < DB; ++db) vcur[db] = vnext[db];
         }
+        l_run += psum[0] + psum[1];
     };
 
-    __syncthreads();   // sm.min_vis complete
-    const int min_vis = min(sm.min_vis, kv_end);
-    const int n_tiles = (kv_end - kv_begin + kKvTile - 1) / kKvTile;
 
-    // ---- pipeline: registers hold tiles it+1 and it+2 while tile it is
-    // computed from LDS; one barrier per tile
+    __syncthreads();   // sm.min_vis complete
+    // read from LDS but the same in every lane: keep it scalar so the mask
+    // test below is a branch and not a per-score select
+    const int min_vis = __builtin_amdgcn_readfirstlane(min(sm.min_vis, kv_end));
+    const int n_tiles = (kv_end - kv_begin + kKvTile - 1) / kKvTile;
     Staging<D> sa, sb;
     load_tile(kv_begin, sa);
-    if (n_tiles > 1) load_tile(kv_begin + kKvTile, sb);
+    load_tile(kv_begin + kKvTile, sb);
     store_tile(0, sa);
     __syncthreads();
     for (int it = 0; it < n_tiles; it += 2) {
-        {   // even tile: computed from buffer 0; sb holds tile it+1
-            const int t0 = kv_begin + it * kKvTile;
-            if (it + 2 < n_tiles) load_tile(t0 + 2 * kKvTile, sa);
-            compute_tile(0, t0, t0 + kKvTile <= min_vis);
-            if (it + 1 < n_tiles) store_tile(1, sb);
-            __syncthreads();
-        }
-        if (it + 1 < n_tiles) {   // odd tile: computed from buffer 1; sa holds tile it+2
-            const int t0 = kv_begin + (it + 1) * kKvTile;
-            if (it + 3 < n_tiles) load_tile(t0 + 2 * kKvTile, sb);
-            compute_tile(1, t0, t0 + kKvTile <= min_vis);
-            if (it + 2 < n_tiles) store_tile(0, sa);
-            __syncthreads();
-        }
+        // even tile it from buffer 0; sb holds tile it+1, sa receives it+2
+        const int t0 = kv_begin + it * kKvTile;
+        load_tile(t0 + 2 * kKvTile, sa);
+        compute_tile(0, t0, t0 + kKvTile <= min_vis);
+        store_tile(1, sb);
+        lds_barrier();
+        if (it + 1 >= n_tiles) break;
+        // odd tile it+1 from buffer 1; sa holds tile it+2, sb receives it+3
+        const int t1 = t0 + kKvTile;
+        load_tile(t1 + 2 * kKvTile, sb);
+        compute_tile(1, t1, t1 + kKvTile <= min_vis);
+        store_tile(0, sa);
+        lds_barrier();
     }
 
-    l_run += __shfl_xor(l_run, 32);
-    if (tok < 0) return;
-
-    if (a.part_m == nullptr) {
-        const float inv = 1.0f / l_run;
+    // ---- epilogue.  l_run holds this half-wave's keys only; the column's
+    // total adds the partner half's (one of the two swap results is the
+    // lane's own value, the other its partner's).
+    auto pair_sum = [](float x) {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    };
+    auto write_out = [&](float l_tot) {
+        const float inv = 1.0f / l_tot;
         float* orow = a.out + ((int64_t)tok * a.n_q_heads + qh) * D;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
@@ -336,102 +457,126 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, Til
                 o.w = acc[db][4 * q4 + 3] * inv;
                 *reinterpret_cast<float4*>(orow + d) = o;
             }
-    } else {
-        const int64_t pi = ((int64_t)tok * a.n_q_heads + qh) * a.max_splits + split;
-        float* prow = a.part_acc + pi * D;
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const int d = 32 * db + 8 * q4 + 4 * hh;
-                float4 o;
-                o.x = acc[db][4 * q4 + 0];
-                o.y = acc[db][4 * q4 + 1];
-                o.z = acc[db][4 * q4 + 2];
-                o.w = acc[db][4 * q4 + 3];
-                *reinterpret_cast<float4*>(prow + d) = o;
-            }
-        if (hh == 0) {
-            a.part_m[pi] = m_run;
-            a.part_l[pi] = l_run;
-        }
-    }
-}
-
-// One workgroup of D threads per (token, query head).  Combines the splits
-// that hold keys visible to the token, loading up to kFast of them in one
-// round; padding tokens get a zero row.
-template <int D>
-__global__ __launch_bounds__(D) void prefill_reduce_kernel(PrefillArgs a) {
-    constexpr int kFast = 16;
-    const int tok = blockIdx.x;
-    const int qh = blockIdx.y;
-    const int d = threadIdx.x;
-    float* orow = a.out + ((int64_t)tok * a.n_q_heads + qh) * D;
-    if (a.token_row[tok] < 0) {
-        orow[d] = 0.0f;
+    };
+    if (tile.n_splits == 1) {
+        const float l_tot = pair_sum(l_run);
+        if (tok >= 0) write_out(l_tot);
         return;
     }
-    const int n_vis = min(a.token_kv_len[tok], a.token_pos[tok] + 1);
-    const int ns = (n_vis + a.split_tokens - 1) / a.split_tokens;
-    const int64_t base = ((int64_t)tok * a.n_q_heads + qh) * a.max_splits;
-    float num = 0.0f, den = 0.0f;
-    if (ns <= kFast) {
-        float pm[kFast], pl[kFast], px[kFast];
+
+    // ---- split tile: fused log-sum-exp combine.  Each split stores its
+    // partial (m, half-wave l, unnormalised acc) in the lanes' register order
+    // with device-scope stores (written through past the per-XCD L2s), waits
+    // until they are acknowledged, and bumps the (tile, KV head) counter; the
+    // split that brings it to n_splits reads the others' partials with
+    // device-scope loads, writes the output and zeroes the counter again.
+    constexpr int NV = 4 * DB;   // 16-byte accumulator pieces per lane
+    const int64_t grp = (int64_t)a.group_base + (int64_t)tile_idx * Hkv + kvh;
+    const int64_t slot0 = grp * a.max_splits;
+    const int nsp = tile.n_splits;
+    // buffer resources based at this group's partials; sc1 (cache-policy bit
+    // 16) makes the accesses coherent across the XCDs' L2s
+    constexpr int kCoherent = 16;
+    const __amdgpu_buffer_rsrc_t racc = __builtin_amdgcn_make_buffer_rsrc(
+        a.part_acc + slot0 * NV * kThreads * 4, 0, 0x7fffffff, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rml = __builtin_amdgcn_make_buffer_rsrc(
+        a.part_ml + slot0 * kThreads * 2, 0, 0x7fffffff, 0x00020000);
+    auto acc_off = [&](int sp, int j) { return ((sp * NV + j) * kThreads + tid) * 16; };
+    auto ml_off = [&](int sp) { return (sp * kThreads + tid) * 8; };
+    // own partial: 8-byte device-scope stores (sc1, like the loads below)
+    {
+        uint64_t* pacc = reinterpret_cast<uint64_t*>(a.part_acc + slot0 * NV * kThreads * 4);
 #pragma unroll
-        for (int s = 0; s < kFast; ++s) {
-            if (s < ns) {
-                pm[s] = a.part_m[base + s];
-                pl[s] = a.part_l[base + s];
-                px[s] = a.part_acc[(base + s) * D + d];
-            }
+        for (int j = 0; j < NV; ++j) {
+            const f32x16& x = acc[j >> 2];
+            const int r = 4 * (j & 3);
+            uint64_t* pp = pacc + acc_off(split, j) / 8;
+            store_device2(pp, x[r], x[r + 1]);
+            store_device2(pp + 1, x[r + 2], x[r + 3]);
         }
-        float M = pm[0];
+        store_device2(reinterpret_cast<uint64_t*>(a.part_ml + slot0 * kThreads * 2) + ml_off(split) / 8,
+                      m_run, l_run);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0) sm.last = atomicAdd(a.counters + grp, 1) == nsp - 1;
+    __syncthreads();
+    if (!sm.last) return;
+    if (tid == 0) __hip_atomic_store(a.counters + grp, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+    // maximum over the splits' m, four splits' loads in flight at a time
+    float M = -INFINITY;
+#pragma unroll 1
+    for (int sp0 = 0; sp0 < nsp; sp0 += 4) {
+        u32x2 ml[4];
 #pragma unroll
-        for (int s = 1; s < kFast; ++s)
-            if (s < ns) M = fmaxf(M, pm[s]);
+        for (int u = 0; u < 4; ++u)
+            ml[u] = __builtin_amdgcn_raw_buffer_load_b64(rml, ml_off(min(sp0 + u, nsp - 1)), 0, kCoherent);
 #pragma unroll
-        for (int s = 0; s < kFast; ++s) {
-            if (s < ns) {
-                const float f = pm[s] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(pm[s] - M);
-                num += f * px[s];
-                den += f * pl[s];
-            }
-        }
-    } else {
-        float M = -INFINITY;
-        for (int s = 0; s < ns; ++s) M = fmaxf(M, a.part_m[base + s]);
-        for (int s = 0; s < ns; ++s) {
-            const float ms = a.part_m[base + s];
-            const float f = ms == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ms - M);
-            num += f * a.part_acc[(base + s) * D + d];
-            den += f * a.part_l[base + s];
+        for (int u = 0; u < 4; ++u) M = fmaxf(M, __uint_as_float(ml[u][0]));
+    }
+    // fold the splits in ascending order, this one's own partial re-read
+    // like the others, so the result does not depend on which split finishes
+    // last; a column that no split saw (padding) keeps M = -inf: weights 0.
+    // All of one split's loads are issued before any of them is used.
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[db][r] = 0.0f;
+    float L = 0.0f;
+#pragma unroll 1
+    for (int sp = 0; sp < nsp; ++sp) {
+        u32x4 x[NV];
+        const u32x2 ml = __builtin_amdgcn_raw_buffer_load_b64(rml, ml_off(sp), 0, kCoherent);
+#pragma unroll
+        for (int j = 0; j < NV; ++j) x[j] = __builtin_amdgcn_raw_buffer_load_b128(racc, acc_off(sp, j), 0, kCoherent);
+        const float w = M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(__uint_as_float(ml[0]) - M);
+        L = __builtin_fmaf(w, __uint_as_float(ml[1]), L);
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            f32x16& t = acc[j >> 2];
+            const int r = 4 * (j & 3);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) t[r + e] = __builtin_fmaf(w, __uint_as_float(x[j][e]), t[r + e]);
         }
     }
-    orow[d] = num / den;
+    const float l_tot = pair_sum(L);
+    if (tok >= 0) write_out(l_tot);
+}
+
+template <int D, bool ONE_PAGE>
+hipError_t launch_prefill_dp(const PrefillArgs& a, const TileList& tl, int n_items, size_t lds,
+                             hipStream_t stream) {
+    const int G = a.n_q_heads / a.n_kv_heads;
+    const dim3 grid((unsigned)n_items);
+    const dim3 block(kThreads);
+    switch (G) {
+        case 1: hipLaunchKernelGGL((prefill_kernel<D, 1, ONE_PAGE>), grid, block, lds, stream, a, tl); break;
+        case 2: hipLaunchKernelGGL((prefill_kernel<D, 2, ONE_PAGE>), grid, block, lds, stream, a, tl); break;
+        case 4: hipLaunchKernelGGL((prefill_kernel<D, 4, ONE_PAGE>), grid, block, lds, stream, a, tl); break;
+        case 8: hipLaunchKernelGGL((prefill_kernel<D, 8, ONE_PAGE>), grid, block, lds, stream, a, tl); break;
+        case 16: hipLaunchKernelGGL((prefill_kernel<D, 16, ONE_PAGE>), grid, block, lds, stream, a, tl); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_prefill_d(const PrefillArgs& a, const TileList& tl, int n_items, size_t lds,
                             hipStream_t stream) {
-    const int G = a.n_q_heads / a.n_kv_heads;
-    const dim3 grid((unsigned)n_items);
-    switch (G) {
-        case 1: hipLaunchKernelGGL((prefill_kernel<D, 1>), grid, dim3(kThreads), lds, stream, a, tl); break;
-        case 2: hipLaunchKernelGGL((prefill_kernel<D, 2>), grid, dim3(kThreads), lds, stream, a, tl); break;
-        case 4: hipLaunchKernelGGL((prefill_kernel<D, 4>), grid, dim3(kThreads), lds, stream, a, tl); break;
-        case 8: hipLaunchKernelGGL((prefill_kernel<D, 8>), grid, dim3(kThreads), lds, stream, a, tl); break;
-        case 16: hipLaunchKernelGGL((prefill_kernel<D, 16>), grid, dim3(kThreads), lds, stream, a, tl); break;
-        default: return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
+    if (a.page_size % kKvTile == 0) return launch_prefill_dp<D, true>(a, tl, n_items, lds, stream);
+    return launch_prefill_dp<D, false>(a, tl, n_items, lds, stream);
 }
 
 }  // namespace
 
 int prefill_tokens_per_tile(int group) { return kRows / group; }
 
+int prefill_threads() { return kThreads; }
+
 int prefill_page_table_entries(int split_tokens, int page_size) {
+    // a split starts at a multiple of the 64-key tile: its keys span at most
+    // ceil(split_tokens / P) + 1 pages
     return (split_tokens + page_size - 1) / page_size + 1;
 }
 
@@ -449,13 +594,5 @@ hipError_t launch_prefill(const PrefillArgs& a, const PrefillTile* tiles, int n_
     return launch_prefill_d<64>(b, tl, n_items, lds, stream);
 }
 
-hipError_t launch_prefill_reduce(const PrefillArgs& a, hipStream_t stream) {
-    const dim3 grid((unsigned)a.n_tokens, (unsigned)a.n_q_heads);
-    if (a.head_dim == 128)
-        hipLaunchKernelGGL(prefill_reduce_kernel<128>, grid, dim3(128), 0, stream, a);
-    else
-        hipLaunchKernelGGL(prefill_reduce_kernel<64>, grid, dim3(64), 0, stream, a);
-    return hipGetLastError();
-}
 
 }  // namespace pa

@@ -84,6 +84,35 @@ def test_reshape_and_cache_ua_ubatch():
     assert np.array_equal(bits16(to_host(vd)), bits16(v2))
 
 
+@pytest.mark.parametrize("f32", [False, True])
+@pytest.mark.parametrize("P,D", [(16, 64), (128, 128)])
+def test_reshape_and_cache_slot_runs(f32, P, D):
+    """Sequences' new tokens in page order (8-aligned runs of consecutive
+    slots, written 16 bytes at a time) mixed with runs that start mid-group,
+    skipped tokens inside a run and a ragged tail of the last workgroup."""
+    rng = np.random.default_rng(90 + P + D + f32)
+    H, N = 3, 48
+    k, v = W.nan_pools(N, H, P, D)
+    pages = rng.permutation(N)
+    runs, used = [], 0
+    for start, length in [(0, 3 * P), (5, 2 * P - 5), (P - 3, 3), (0, 61), (8, 29)]:
+        pg = pages[used: used + (start + length + P - 1) // P]
+        used += len(pg)
+        cells = np.arange(start, start + length)
+        runs.append(pg[cells // P] * P + cells % P)
+    slots = np.concatenate(runs).astype(np.int32)
+    slots[[9, 70, 71]] = -1
+    T = len(slots)
+    dt = np.float32 if f32 else np.float16
+    kn = rng.standard_normal((T, H, D)).astype(dt)
+    vn = rng.standard_normal((T, H, D)).astype(dt)
+    kd, vd = to_dev(k), to_dev(v)
+    pa.pa_reshape_and_cache(kd, vd, to_dev(kn), to_dev(vn), to_dev(slots))
+    k2, v2 = oracle.reshape_and_cache(k, v, kn, vn, slots)
+    assert np.array_equal(bits16(to_host(kd)), bits16(k2))
+    assert np.array_equal(bits16(to_host(vd)), bits16(v2))
+
+
 @pytest.mark.parametrize("n_layers", [1, 4])
 def test_copy_blocks_bitwise(n_layers):
     rng = np.random.default_rng(n_layers)

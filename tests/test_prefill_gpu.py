@@ -157,3 +157,43 @@ def test_chunked_prefill_sampled_ubatches():
                                          kvl[pick], pos[pick], cp.scale)
             assert_attention_close(got[pick], ref, f"ubatch {j}")
     assert np.array_equal(bits16(to_host(kd)), bits16(k_pool))
+
+
+def test_workspace_reused_across_calls_and_shapes():
+    """Split tiles count their finished splits in the workspace's counter
+    region and the combining split zeroes it again, so one zero-filled
+    workspace serves calls of different shapes and split counts, and a
+    repeated call reproduces its first result bitwise (the splits are folded
+    in a fixed order whichever finishes last)."""
+    import torch
+    shapes = [(32, 8, 128, 128, [3000, 1000], [70, 33], 3),
+              (8, 2, 64, 16, [900, 50, 400], [40, 12, 7], 0),
+              (16, 4, 128, 64, [2500], [130], 5)]
+    cases = []
+    for i, (Hq, Hkv, D, P, pre, new, ks) in enumerate(shapes):
+        rng = np.random.default_rng(60 + i)
+        N = int(1.3 * sum((a + b + P - 1) // P for a, b in zip(pre, new))) + 4
+        c = W.make_prefill_case(rng, "ws", Hq, Hkv, D, P, N, pre, new, "round_robin")
+        kd, vd, k2, v2 = write_new_tokens(c)
+        ref = oracle.paged_attention(c.q, k2, v2, c.block_tables, c.token_row, c.token_kv_len,
+                                     c.token_pos, c.scale)
+        cases.append((c, kd, vd, ks, ref))
+    ws = torch.zeros(1 << 24, dtype=torch.uint8, device="cuda")
+    first = {}
+    for rep in range(3):
+        for i, (c, kd, vd, ks, ref) in enumerate(cases):
+            need = pa.pa_prefill_workspace_bytes(pa.cache_desc(kd, vd), c.q.shape[1], c.token_row,
+                                                 c.token_kv_len, c.token_pos, ks)
+            assert 0 < need <= ws.numel()
+            out = to_host(pa.pa_prefill(to_dev(c.q), kd, vd, to_dev(c.block_tables),
+                                        to_dev(c.token_row), to_dev(c.token_kv_len),
+                                        to_dev(c.token_pos), float(c.scale),
+                                        token_row_host=c.token_row, token_kv_len_host=c.token_kv_len,
+                                        token_pos_host=c.token_pos, kv_splits=ks, workspace=ws))
+            if rep == 0:
+                assert_attention_close(out, ref, f"prefill reuse {i}")
+                first[i] = out
+            else:
+                assert np.array_equal(out, first[i]), f"prefill reuse {i} rep {rep}"
+    torch.cuda.synchronize()
+    assert int(ws[:65536].count_nonzero()) == 0
