@@ -180,12 +180,16 @@ pa_status plan_prefill(const pa_cache_desc* d, int32_t n_tokens, int32_t n_q_hea
             t.first = order[s];
             t.last = order[f - 1];
             t.count = (int32_t)(f - s);
-            int32_t ke = 0;
+            int32_t ke = 0, kmin = INT32_MAX;
             for (size_t j = s; j < f; ++j) {
                 const int32_t i = order[j];
-                ke = std::max(ke, std::min(kv_len[i], pos[i] + 1));
+                const int32_t vis = std::min(kv_len[i], pos[i] + 1);
+                ke = std::max(ke, vis);
+                kmin = std::min(kmin, vis);
             }
             t.kv_end = ke;
+            t.min_vis = kmin;
+            t.dense = (t.last - t.first + 1 == t.count) ? 1 : 0;
             plan->tiles.push_back(t);
             sum_kv += ke;
             max_kv = std::max<int64_t>(max_kv, ke);

@@ -70,7 +70,9 @@ struct PrefillTile {
     int32_t last;       // ubatch index of the tile's last token
     int32_t count;      // tokens in the tile (<= tokens per tile)
     int32_t kv_end;     // largest visible length of any token in the tile
+    int32_t min_vis;    // smallest visible length of any token in the tile
     int32_t n_splits;   // KV splits used by this tile (<= grid splits)
+    int32_t dense;      // 1: the tile's tokens are first, first+1, ..., last
 };
 
 constexpr int kMaxTilesPerLaunch = 128;

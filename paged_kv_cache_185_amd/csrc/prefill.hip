@@ -62,6 +62,8 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kRows = 32 * kWaves;          // query rows (token x head) per tile
 constexpr int kKvTile = kPrefillKvTile;     // 64 keys per iteration
 constexpr float kRescaleSlack = 8.0f;       // log2 units the max may lag by
+constexpr int kKDepth = 4;                  // K operand k-steps read ahead of the score MFMAs
+constexpr int kVDepth = 1;                  // V operand k-steps read ahead of the P.V MFMAs
 
 struct TileList {
     PrefillTile t[kMaxTilesPerLaunch];
@@ -112,15 +114,18 @@ struct Smem {
     u32x4 k[2][kKvTile * D / 8];   // [buf][key][D/8 chunks], chunk swizzled by key % 8
     u32x4 v[2][D * kKvTile / 8];   // [buf][d][8 chunks of 8 keys], chunk swizzled by d % 8
     int32_t tok[kRows];
-    int32_t min_vis;
     int32_t last;   // this workgroup combines the tile's splits
 };
 
 template <int D>
-struct Staging {
-    static constexpr int KC = kKvTile * D / 8 / kThreads;   // 16-byte chunks per thread (K)
-    static constexpr int VC = D * kKvTile / 8 / kThreads;   // (V)
+struct StagingK {
+    static constexpr int KC = kKvTile * D / 8 / kThreads;   // 16-byte chunks per thread
     u32x4 k[KC];
+};
+
+template <int D>
+struct StagingV {
+    static constexpr int VC = D * kKvTile / 8 / kThreads;   // 16-byte chunks per thread
     u32x4 v[VC];
     int t0;   // first key of the tile held
 };
@@ -154,9 +159,42 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, Til
     const int hh = lane >> 5;
     const int P = a.page_size;
 
-    // ---- tokens of this tile (ballot scan of token_row[first..last]) and the
-    // page ids of this split's key range
-    if (wave == 0) {
+    // ---- this split's page ids -> LDS (loaded first: the in-order vmcnt
+    // accounting then lets the Q loads below stay in flight across the
+    // barrier), and this lane's query column: tile row (wave*32 + col) is
+    // token slot row/G, head row%G.  A dense tile's tokens are first..last,
+    // so its metadata and Q loads start at once; otherwise wave 0 finds the
+    // tile's tokens with a ballot scan of token_row[first..last].
+    const int sh = a.page_shift;
+    const int page_base = kv_begin >> sh;
+    const int32_t* bt = a.block_tables + (int64_t)tile.row * a.max_pages;
+    const int n_pages = ((kv_end - 1) >> sh) - page_base + 1;
+    const int pt0 = tid < n_pages ? bt[page_base + tid] : 0;
+    // the first tile's page (entry 0), read by every lane at one address
+    const int page0 = bt[page_base];
+    const int ti = wave * TPW + col / G;
+    const int hq = col % G;
+    const int qh = kvh * G + hq;
+    int tok = -1;
+    int tok_kv_len = 0, tok_pos = 0;
+    int n_vis = 0;   // keys this lane's query token sees
+    float4 qraw[2 * KS];
+    auto load_token = [&]() __attribute__((always_inline)) {
+        const int t = tok >= 0 ? tok : 0;
+        tok_kv_len = a.token_kv_len[t];
+        tok_pos = a.token_pos[t];
+        const float* qrow = a.q + ((int64_t)t * a.n_q_heads + qh) * D;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const int d0 = 16 * ks + 8 * hh;
+            qraw[2 * ks] = *reinterpret_cast<const float4*>(qrow + d0);
+            qraw[2 * ks + 1] = *reinterpret_cast<const float4*>(qrow + d0 + 4);
+        }
+    };
+    if (tile.dense) {
+        tok = ti < tile.count ? tile.first + ti : -1;
+        load_token();
+    } else if (wave == 0) {
         int found = 0;
         for (int base = tile.first; base <= tile.last && found < tile.count; base += 64) {
             const int i = base + lane;
@@ -167,41 +205,15 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, Til
             found += __popcll(mask);
         }
     }
-    if (tid == 0) sm.min_vis = kv_end;
-    const int sh = a.page_shift;
-    const int page_base = kv_begin >> sh;
-    {
-        const int32_t* bt = a.block_tables + (int64_t)tile.row * a.max_pages;
-        const int n_pages = ((kv_end - 1) >> sh) - page_base + 1;
-        for (int i = tid; i < n_pages; i += kThreads) sm_pages[i] = bt[page_base + i];
-    }
+    if (tid < n_pages) sm_pages[tid] = pt0;
+    for (int i = tid + kThreads; i < n_pages; i += kThreads) sm_pages[i] = bt[page_base + i];
     __syncthreads();
-
-    // ---- this lane's query column
-    const int ti = wave * TPW + col / G;
-    const int hq = col % G;
-    const int tok = ti < tile.count ? sm.tok[ti] : -1;
-    int n_vis = 0;
-    if (tok >= 0) n_vis = min(a.token_kv_len[tok], a.token_pos[tok] + 1);
-    const int qh = kvh * G + hq;
-    if (tok >= 0) atomicMin(&sm.min_vis, n_vis);
-
-    u32x4 qb[KS];
-    {
-        const float* qrow = a.q + ((int64_t)(tok >= 0 ? tok : 0) * a.n_q_heads + qh) * D;
-        const float qs = tok >= 0 ? a.scale_log2 : 0.0f;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const int d0 = 16 * ks + 8 * hh;
-            const float4 x0 = *reinterpret_cast<const float4*>(qrow + d0);
-            const float4 x1 = *reinterpret_cast<const float4*>(qrow + d0 + 4);
-            const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-            f16x8 h;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) h[e] = (_Float16)(xs[e] * qs);
-            qb[ks] = __builtin_bit_cast(u32x4, h);
-        }
+    if (!tile.dense) {
+        tok = ti < tile.count ? sm.tok[ti] : -1;
+        load_token();
     }
+
+    u32x4 qb[KS];   // Q operands, made once the first tile's loads are out
 
     const uint16_t* kc = a.k_cache;
     const uint16_t* vc = a.v_cache;
@@ -218,36 +230,38 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, Til
     const int last_t0 = kv_begin + ((kv_end - kv_begin - 1) / kKvTile) * kKvTile;
     // per-thread element offsets of the K chunks (key, c) and V chunks (d, c)
     // inside one tile when it lies in one page
-    int koff[Staging<D>::KC], voff[Staging<D>::VC];
+    int koff[StagingK<D>::KC], voff[StagingV<D>::VC];
 #pragma unroll
-    for (int i = 0; i < Staging<D>::KC; ++i) {
+    for (int i = 0; i < StagingK<D>::KC; ++i) {
         const int id = tid + kThreads * i;
         koff[i] = (id / CPR) * D + 8 * (id % CPR);
     }
 #pragma unroll
-    for (int i = 0; i < Staging<D>::VC; ++i) {
+    for (int i = 0; i < StagingV<D>::VC; ++i) {
         const int id = tid + kThreads * i;
         voff[i] = (id >> 3) * P + 8 * (id & 7);
     }
-    auto load_tile = [&](int t0_req, Staging<D>& st) {
-        const int t0 = min(t0_req, last_t0);
+    // one-page tiles: keys past kv_end are still inside the tile's
+    // (allocated) page; K there is masked out of the scores and V is zeroed
+    // at store
+    auto load_k_page = [&](int t0, int page, StagingK<D>& st) __attribute__((always_inline)) {
+        const uint16_t* kb = kc + page * page_elems + (k_head_off + (t0 & (P - 1)) * D);
+#pragma unroll
+        for (int i = 0; i < StagingK<D>::KC; ++i) st.k[i] = *reinterpret_cast<const u32x4*>(kb + koff[i]);
+    };
+    auto load_v_page = [&](int t0, int page, StagingV<D>& st) __attribute__((always_inline)) {
         st.t0 = t0;
+        const uint16_t* vb = vc + page * page_elems + (k_head_off + (t0 & (P - 1)));
+#pragma unroll
+        for (int i = 0; i < StagingV<D>::VC; ++i) st.v[i] = *reinterpret_cast<const u32x4*>(vb + voff[i]);
+    };
+    auto load_k = [&](int t0_req, StagingK<D>& st) __attribute__((always_inline)) {
+        const int t0 = min(t0_req, last_t0);
         if constexpr (ONE_PAGE) {
-            // keys past kv_end in the tile are still inside its (allocated)
-            // page: K there is masked out of the scores, V is zeroed at store
-            const int page = __builtin_amdgcn_readfirstlane(sm_pages[(t0 >> sh) - page_base]);
-            const int64_t base = page * page_elems + (k_head_off + (t0 & (P - 1)) * D);
-            const uint16_t* kb = kc + base;
-            const uint16_t* vb = vc + page * page_elems + (k_head_off + (t0 & (P - 1)));
-#pragma unroll
-            for (int i = 0; i < Staging<D>::KC; ++i)
-                st.k[i] = *reinterpret_cast<const u32x4*>(kb + koff[i]);
-#pragma unroll
-            for (int i = 0; i < Staging<D>::VC; ++i)
-                st.v[i] = *reinterpret_cast<const u32x4*>(vb + voff[i]);
+            load_k_page(t0, __builtin_amdgcn_readfirstlane(sm_pages[(t0 >> sh) - page_base]), st);
         } else {
 #pragma unroll
-            for (int i = 0; i < Staging<D>::KC; ++i) {
+            for (int i = 0; i < StagingK<D>::KC; ++i) {
                 const int id = tid + kThreads * i;
                 const int key = id / CPR;
                 const int c = id % CPR;
@@ -256,26 +270,36 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, Til
                 st.k[i] = *reinterpret_cast<const u32x4*>(
                     kc + page * page_elems + (k_head_off + (t & (P - 1)) * D + 8 * c));
             }
+        }
+    };
+    auto load_v = [&](int t0_req, StagingV<D>& st) __attribute__((always_inline)) {
+        const int t0 = min(t0_req, last_t0);
+        st.t0 = t0;
+        if constexpr (ONE_PAGE) {
+            load_v_page(t0, __builtin_amdgcn_readfirstlane(sm_pages[(t0 >> sh) - page_base]), st);
+        } else {
             const int c = tid & 7;
             const int tb = t0 + 8 * c;
             const int tv = tb < kv_end ? tb : ((kv_end - 1) & ~7);
             const int vpage = sm_pages[(tv >> sh) - page_base];
             const uint16_t* vbase = vc + vpage * page_elems + (k_head_off + (tv & (P - 1)));
 #pragma unroll
-            for (int i = 0; i < Staging<D>::VC; ++i) {
+            for (int i = 0; i < StagingV<D>::VC; ++i) {
                 const int d = (tid + kThreads * i) >> 3;
                 st.v[i] = *reinterpret_cast<const u32x4*>(vbase + d * P);
             }
         }
     };
-    auto store_tile = [&](int buf, Staging<D>& st) {
+    auto store_k = [&](int buf, StagingK<D>& st) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < Staging<D>::KC; ++i) {
+        for (int i = 0; i < StagingK<D>::KC; ++i) {
             const int id = tid + kThreads * i;
             const int key = id / CPR;
             const int c = id % CPR;
             sm.k[buf][key * CPR + (c ^ kswz<D>(key))] = st.k[i];
         }
+    };
+    auto store_v = [&](int buf, StagingV<D>& st) __attribute__((always_inline)) {
         // zero the V halves of keys at or past the visible end (only the last
         // tile of a split has any)
         if (st.t0 + kKvTile > kv_end) {
@@ -285,12 +309,12 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, Til
             for (int w = 0; w < 4; ++w)
                 mk[w] = (2 * w < nvalid ? 0x0000ffffu : 0u) | (2 * w + 1 < nvalid ? 0xffff0000u : 0u);
 #pragma unroll
-            for (int i = 0; i < Staging<D>::VC; ++i)
+            for (int i = 0; i < StagingV<D>::VC; ++i)
 #pragma unroll
                 for (int w = 0; w < 4; ++w) st.v[i][w] &= mk[w];
         }
 #pragma unroll
-        for (int i = 0; i < Staging<D>::VC; ++i) {
+        for (int i = 0; i < StagingV<D>::VC; ++i) {
             const int id = tid + kThreads * i;
             const int d = id >> 3;
             const int c = id & 7;
@@ -305,40 +329,47 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, Til
     for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[db][r] = 0.0f;
+    f32x16 s[2];   // scores of the tile between its two phases
 
-    // one 64-key tile from LDS buffer `buf`, keys t0..t0+63; `full` (uniform)
-    // says every query column of the tile sees all 64 keys
-    auto compute_tile = [&](int buf, int t0, bool full) {
-        f32x16 s[2];
+    // S^T = K Q^T for the 64 keys in K buffer `buf`.  K operands are read from
+    // LDS two k-steps ahead of their MFMAs, and the two 32-key blocks
+    // alternate so consecutive MFMAs are independent.
+    auto qk = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) s[kb][r] = 0.0f;
-        // K operands are read from LDS two k-steps ahead of their MFMAs, and
-        // the two 32-key blocks alternate so consecutive MFMAs are independent
         const int krow0 = kappa(col);
         const int krow1 = 32 + kappa(col);
-        auto kread = [&](int ks, int krow) {
+        auto kread = [&](int ks, int krow) __attribute__((always_inline)) {
             const int c = 2 * ks + hh;
             return sm.k[buf][krow * CPR + (c ^ kswz<D>(krow))];
         };
-        u32x4 ka[3], kb1[3];
-        ka[0] = kread(0, krow0);
-        kb1[0] = kread(0, krow1);
-        ka[1] = kread(1, krow0);
-        kb1[1] = kread(1, krow1);
+        // ring of kKDepth+1 k-steps of operands, kKDepth in flight
+        constexpr int R = kKDepth + 1;
+        u32x4 ka[R], kb1[R];
+#pragma unroll
+        for (int ks = 0; ks < kKDepth; ++ks) {
+            ka[ks] = kread(ks, krow0);
+            kb1[ks] = kread(ks, krow1);
+        }
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            if (ks + 2 < KS) {
-                ka[(ks + 2) % 3] = kread(ks + 2, krow0);
-                kb1[(ks + 2) % 3] = kread(ks + 2, krow1);
+            if (ks + kKDepth < KS) {
+                ka[(ks + kKDepth) % R] = kread(ks + kKDepth, krow0);
+                kb1[(ks + kKDepth) % R] = kread(ks + kKDepth, krow1);
             }
             // keep the scheduler from sinking the reads back to their use
             __builtin_amdgcn_sched_barrier(0);
-            s[0] = mfma32(ka[ks % 3], qb[ks], s[0]);
-            s[1] = mfma32(kb1[ks % 3], qb[ks], s[1]);
+            s[0] = mfma32(ka[ks % R], qb[ks], s[0]);
+            s[1] = mfma32(kb1[ks % R], qb[ks], s[1]);
             __builtin_amdgcn_sched_barrier(0);
         }
+    };
+
+    // Online softmax of the scores (keys t0..t0+63) and O^T += V^T P^T with V
+    // buffer `buf`; `full` (uniform) says every query column sees all 64 keys.
+    auto smpv = [&](int buf, int t0, bool full) __attribute__((always_inline)) {
         if (!full) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
@@ -371,24 +402,28 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, Til
             m_run = m_new;
         }
         const float m_use = m_run == -INFINITY ? 0.0f : m_run;
-        // O^T += V^T P^T, 16 keys per k-step: P is made just before its MFMAs
-        // and the V operands of the next k-step are read from LDS meanwhile
-        auto vread = [&](int ks, int db) {
+        // 16 keys per k-step: P is made just before its MFMAs and the V
+        // operands of the next k-step are read from LDS meanwhile
+        auto vread = [&](int ks, int db) __attribute__((always_inline)) {
             const int c = 2 * ks + hh;
             const int d = 32 * db + col;
             return sm.v[buf][d * 8 + (c ^ vswz(d))];
         };
-        u32x4 vcur[DB], vnext[DB];
+        // ring of kVDepth+1 k-steps of V operands, kVDepth in flight
+        constexpr int RV = kVDepth + 1;
+        u32x4 vop[RV][DB];
 #pragma unroll
-        for (int db = 0; db < DB; ++db) vcur[db] = vread(0, db);
+        for (int ks = 0; ks < kVDepth; ++ks)
+#pragma unroll
+            for (int db = 0; db < DB; ++db) vop[ks][db] = vread(ks, db);
         // the row sum adds the binary16 P the MFMA consumes, two per dot2
         const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
         float psum[2] = {0.0f, 0.0f};
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-            if (ks + 1 < 4) {
+            if (ks + kVDepth < 4) {
 #pragma unroll
-                for (int db = 0; db < DB; ++db) vnext[db] = vread(ks + 1, db);
+                for (int db = 0; db < DB; ++db) vop[(ks + kVDepth) % RV][db] = vread(ks + kVDepth, db);
             }
             f16x8 p;
 #pragma unroll
@@ -401,48 +436,105 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, Til
             }
             const u32x4 pb = __builtin_bit_cast(u32x4, p);
 #pragma unroll
-            for (int db = 0; db < DB; ++db) acc[db] = mfma32(vcur[db], pb, acc[db]);
-#pragma unroll
-            for (int db = 0; db < DB; ++db) vcur[db] = vnext[db];
+            for (int db = 0; db < DB; ++db) acc[db] = mfma32(vop[ks % RV][db], pb, acc[db]);
         }
         l_run += psum[0] + psum[1];
     };
 
-
-    __syncthreads();   // sm.min_vis complete
-    // read from LDS but the same in every lane: keep it scalar so the mask
-    // test below is a branch and not a per-score select
-    const int min_vis = __builtin_amdgcn_readfirstlane(min(sm.min_vis, kv_end));
+    // smallest visible length over the tile's tokens (from the plan): tiles
+    // ending at or before it need no mask
+    const int min_vis = min(tile.min_vis, kv_end);
     const int n_tiles = (kv_end - kv_begin + kKvTile - 1) / kKvTile;
-    Staging<D> sa, sb;
-    load_tile(kv_begin, sa);
-    load_tile(kv_begin + kKvTile, sb);
-    store_tile(0, sa);
+
+    // ---- main loop: two wave groups in ping-pong.  Waves 0-3 (group A) and
+    // 4-7 (group B) share the SIMDs pairwise; in every phase one group runs
+    // the score MFMAs of a tile while the other runs the softmax (VALU) and
+    // P.V MFMAs of the previous one, so matrix and vector work of the two
+    // waves on a SIMD overlap.  Tile j: A does QK(j) in phase 2j and
+    // softmax+PV(j) in phase 2j+1, B one phase later.  K(j) is read in
+    // phases 2j and 2j+1, V(j) in 2j+1 and 2j+2; both are double buffered,
+    // K stored in the odd phase before its first use and V in the even one.
+    // Global loads run two phases (one tile) ahead of their LDS stores and
+    // are clamped onto the last tile past the end, so every phase issues the
+    // same loads.
+    // Each group runs its own loop (same loads, stores and barriers per
+    // phase, 2*n_tiles+1 phases in all) so that register lifetimes stay
+    // simple for the compiler.
+    const int wgroup = __builtin_amdgcn_readfirstlane(wave >> 2);
+    StagingK<D> stk;
+    StagingV<D> stv;
+    if constexpr (ONE_PAGE) {
+        load_k_page(kv_begin, page0, stk);
+        load_v_page(kv_begin, page0, stv);
+    } else {
+        load_k(kv_begin, stk);
+        load_v(kv_begin, stv);
+    }
+    // Q times scale*log2(e), rounded to binary16: scores come out of the MFMA
+    // in the log2 domain
+    {
+        const float qs = tok >= 0 ? a.scale_log2 : 0.0f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const float4 x0 = qraw[2 * ks];
+            const float4 x1 = qraw[2 * ks + 1];
+            const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+            f16x8 h;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) h[e] = (_Float16)(xs[e] * qs);
+            qb[ks] = __builtin_bit_cast(u32x4, h);
+        }
+    }
+
+    n_vis = tok >= 0 ? min(tok_kv_len, tok_pos + 1) : 0;
+    store_k(0, stk);
+    load_k(kv_begin + kKvTile, stk);
     __syncthreads();
-    for (int it = 0; it < n_tiles; it += 2) {
-        // even tile it from buffer 0; sb holds tile it+1, sa receives it+2
-        const int t0 = kv_begin + it * kKvTile;
-        load_tile(t0 + 2 * kKvTile, sa);
-        compute_tile(0, t0, t0 + kKvTile <= min_vis);
-        store_tile(1, sb);
+    if (wgroup == 0) {
+        for (int j = 0; j < n_tiles; ++j) {
+            const int tj = kv_begin + j * kKvTile;
+            // phase 2j: V(j) -> LDS; QK(j)
+            store_v(j & 1, stv);
+            load_v(tj + kKvTile, stv);
+            qk(j & 1);
+            lds_barrier();
+            // phase 2j+1: K(j+1) -> LDS; softmax+PV(j)
+            store_k((j + 1) & 1, stk);
+            load_k(tj + 2 * kKvTile, stk);
+            smpv(j & 1, tj, tj + kKvTile <= min_vis);
+            lds_barrier();
+        }
+        // phase 2n: the other group's last softmax+PV
+        store_v(n_tiles & 1, stv);
         lds_barrier();
-        if (it + 1 >= n_tiles) break;
-        // odd tile it+1 from buffer 1; sa holds tile it+2, sb receives it+3
-        const int t1 = t0 + kKvTile;
-        load_tile(t1 + 2 * kKvTile, sb);
-        compute_tile(1, t1, t1 + kKvTile <= min_vis);
-        store_tile(0, sa);
+    } else {
+        // phase 0: the other group's first QK
+        store_v(0, stv);
+        load_v(kv_begin + kKvTile, stv);
         lds_barrier();
+        for (int j = 0; j < n_tiles; ++j) {
+            const int tj = kv_begin + j * kKvTile;
+            // phase 2j+1: K(j+1) -> LDS; QK(j)
+            store_k((j + 1) & 1, stk);
+            load_k(tj + 2 * kKvTile, stk);
+            qk(j & 1);
+            lds_barrier();
+            // phase 2j+2: V(j+1) -> LDS; softmax+PV(j)
+            store_v((j + 1) & 1, stv);
+            load_v(tj + 2 * kKvTile, stv);
+            smpv(j & 1, tj, tj + kKvTile <= min_vis);
+            lds_barrier();
+        }
     }
 
     // ---- epilogue.  l_run holds this half-wave's keys only; the column's
     // total adds the partner half's (one of the two swap results is the
     // lane's own value, the other its partner's).
-    auto pair_sum = [](float x) {
+    auto pair_sum = [](float x) __attribute__((always_inline)) {
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
         return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
     };
-    auto write_out = [&](float l_tot) {
+    auto write_out = [&](float l_tot) __attribute__((always_inline)) {
         const float inv = 1.0f / l_tot;
         float* orow = a.out + ((int64_t)tok * a.n_q_heads + qh) * D;
 #pragma unroll
@@ -481,8 +573,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, Til
         a.part_acc + slot0 * NV * kThreads * 4, 0, 0x7fffffff, 0x00020000);
     const __amdgpu_buffer_rsrc_t rml = __builtin_amdgcn_make_buffer_rsrc(
         a.part_ml + slot0 * kThreads * 2, 0, 0x7fffffff, 0x00020000);
-    auto acc_off = [&](int sp, int j) { return ((sp * NV + j) * kThreads + tid) * 16; };
-    auto ml_off = [&](int sp) { return (sp * kThreads + tid) * 8; };
+    auto acc_off = [&](int sp, int j) __attribute__((always_inline)) { return ((sp * NV + j) * kThreads + tid) * 16; };
+    auto ml_off = [&](int sp) __attribute__((always_inline)) { return (sp * kThreads + tid) * 8; };
     // own partial: 8-byte device-scope stores (sc1, like the loads below)
     {
         uint64_t* pacc = reinterpret_cast<uint64_t*>(a.part_acc + slot0 * NV * kThreads * 4);
