@@ -53,6 +53,37 @@ def blas_threads():
         return None
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_kernel_hbm_traffic_8x16k.txt")
+DECODE_SOURCES = [os.path.join(ROOT, "paged_kv_cache_185_amd", "csrc", "decode.hip")]
+
+
+def decode_sources_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    for f in DECODE_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def decode_traffic():
+    """Calibrated HBM bytes per decode launch (FETCH_SIZE + WRITE_SIZE) from the
+    committed counter summary, or None when the decode sources have changed
+    since the counters were taken (or there is no summary)."""
+    try:
+        kv = {}
+        with open(TRAFFIC_FILE) as fh:
+            for line in fh:
+                if ":" in line and not line.startswith("#"):
+                    k, v = line.split(":", 1)
+                    kv[k.strip()] = v.strip()
+        if kv.get("decode_sources_sha256") != decode_sources_sha256():
+            return None
+        return int(float(kv["hbm_bytes_per_launch"]))
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def bench_decode(args, pa, torch, W):
     if args.decode_workload == "qwen3":
         c = W.qwen3_decode()
@@ -246,6 +277,9 @@ def main():
     ap.add_argument("--prefill-reps", type=int, default=3)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many bytes (3 times): the "
+                         "known-size kernel that calibrates the FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -260,6 +294,14 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_bytes > 0:
+        src = torch.ones(args.copy_bytes, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copied {args.copy_bytes} bytes 3 times")
+        return
     log(f"library {pa.library_path()}")
     log("decode: generating 8 x 16384 workload")
     c, dec = bench_decode(args, pa, torch, W)
@@ -319,7 +361,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": decode_traffic(),
             "bytes_per_launch": dec["valid_bytes"],
             "call_us_mean": round(dec["call_ms_mean"] * 1e3, 2),
         },

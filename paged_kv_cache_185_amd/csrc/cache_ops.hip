@@ -12,22 +12,23 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// One workgroup per (64 tokens, KV head).  K rows are contiguous in the cache:
+// One workgroup per (16 tokens, KV head).  K rows are contiguous in the cache:
 // each 16-byte chunk of a token's row is one store.  V is stored with the slot
 // innermost, so V goes through LDS as [d][token] and each run of 8 tokens whose
 // slots are consecutive and 8-aligned (the usual case: a sequence's new tokens
 // fill its pages in order) becomes one 16-byte store per d row; any other slot
 // pattern falls back to 2-byte stores.
-constexpr int kRcTokens = 64;
+constexpr int kRcTokens = 16;
+constexpr int kRcThreads = 256;
 
 template <bool kSrcF32, int D>
-__global__ __launch_bounds__(256) void reshape_and_cache_kernel(
+__global__ __launch_bounds__(kRcThreads) void reshape_and_cache_kernel(
     uint16_t* __restrict__ k_cache, uint16_t* __restrict__ v_cache, const void* __restrict__ k_new,
     const void* __restrict__ v_new, const int32_t* __restrict__ slots, int32_t n_tokens,
     int32_t n_kv_heads, int32_t page_shift) {
     constexpr int CH = D / 8;
-    constexpr int kRow = kRcTokens + 8;   // LDS row of one d: 144 bytes, 16-byte aligned
-    __shared__ uint16_t sv[D * kRow];
+    constexpr int kRow = kRcTokens + 8;   // LDS row of one d: 48 bytes, 16-byte aligned
+    __shared__ __align__(16) uint16_t sv[D * kRow];
     __shared__ int32_t sslot[kRcTokens];
     const int h = blockIdx.y;
     const int tok0 = blockIdx.x * kRcTokens;
@@ -36,7 +37,7 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
     if (tid < kRcTokens) sslot[tid] = tok0 + tid < n_tokens ? slots[tok0 + tid] : -1;
     __syncthreads();
 
-    for (int task = tid; task < kRcTokens * CH; task += 256) {
+    for (int task = tid; task < kRcTokens * CH; task += kRcThreads) {
         const int tl = task / CH;
         const int c = task - tl * CH;
         const int32_t slot = sslot[tl];
@@ -80,10 +81,11 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
     __syncthreads();
 
     // V rows: task (d, g) covers tokens 8g..8g+7 of row d; lanes of a wave
-    // take consecutive g, so a run of pages in order is written contiguously
-    for (int task = tid; task < D * (kRcTokens / 8); task += 256) {
-        const int d = task >> 3;
-        const int g = task & 7;
+    // take consecutive g, so a run of slots in order is written contiguously
+    constexpr int NG = kRcTokens / 8;
+    for (int task = tid; task < D * NG; task += kRcThreads) {
+        const int d = task / NG;
+        const int g = task % NG;
         const int32_t s0 = sslot[8 * g];
         bool run = s0 >= 0 && (s0 & 7) == 0;
 #pragma unroll
@@ -149,17 +151,17 @@ hipError_t launch_reshape_and_cache(void* k_cache, void* v_cache, const void* k_
     auto* vc = (uint16_t*)v_cache;
     if (head_dim == 128) {
         if (src_f32)
-            hipLaunchKernelGGL((reshape_and_cache_kernel<true, 128>), grid, dim3(256), 0, stream, kc, vc,
+            hipLaunchKernelGGL((reshape_and_cache_kernel<true, 128>), grid, dim3(kRcThreads), 0, stream, kc, vc,
                                k_new, v_new, slots, n_tokens, n_kv_heads, shift);
         else
-            hipLaunchKernelGGL((reshape_and_cache_kernel<false, 128>), grid, dim3(256), 0, stream, kc, vc,
+            hipLaunchKernelGGL((reshape_and_cache_kernel<false, 128>), grid, dim3(kRcThreads), 0, stream, kc, vc,
                                k_new, v_new, slots, n_tokens, n_kv_heads, shift);
     } else {
         if (src_f32)
-            hipLaunchKernelGGL((reshape_and_cache_kernel<true, 64>), grid, dim3(256), 0, stream, kc, vc,
+            hipLaunchKernelGGL((reshape_and_cache_kernel<true, 64>), grid, dim3(kRcThreads), 0, stream, kc, vc,
                                k_new, v_new, slots, n_tokens, n_kv_heads, shift);
         else
-            hipLaunchKernelGGL((reshape_and_cache_kernel<false, 64>), grid, dim3(256), 0, stream, kc, vc,
+            hipLaunchKernelGGL((reshape_and_cache_kernel<false, 64>), grid, dim3(kRcThreads), 0, stream, kc, vc,
                                k_new, v_new, slots, n_tokens, n_kv_heads, shift);
     }
     return hipGetLastError();
