@@ -46,6 +46,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;
 constexpr int kChunk = 32;
+constexpr int kDecodeBuffers = 2;   // chunk register sets per wave
 
 __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
@@ -85,70 +86,93 @@ __global__ __launch_bounds__(256, 2) void decode_partition_kernel(DecodeArgs a) 
     const bool single = (L <= a.partition_tokens) || a.part_m == nullptr;
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: scalar loop control
     const int m16 = lane & 15;
     const int g = lane >> 4;
     const int Hkv = a.n_kv_heads;
     const int G = a.n_q_heads / Hkv;
     const int P = a.page_size;
 
-    // ---- Q as the B operand: lane holds Q[head m16][d = 32s + 8g .. +8], hi/lo.
-    u32x4 qhi[KS], qlo[KS];
+    // ---- prologue.  Loads are issued in the order the waits want them: this
+    // partition's page ids (kept in a register until the LDS store), Q, and
+    // -- when pages hold at least one 32-token chunk, so a chunk never crosses
+    // a page -- the wave's first chunk, whose page is read straight from the
+    // block table.  Only then the LDS store, the barrier and the Q conversion.
+    extern __shared__ int32_t sm_pages[];
+    const int sh = a.page_shift;
+    const int page_base = t0 >> sh;
+    const int32_t* bt = a.block_tables + (int64_t)seq * a.max_pages;
+    const int n_pages = ((t1 - 1) >> sh) - page_base + 1;
+    const int pt0 = (int)threadIdx.x < n_pages ? bt[page_base + threadIdx.x] : 0;
+
+    // Q as the B operand: lane holds Q[head m16][d = 32s + 8g .. +8], hi/lo.
+    const bool hv = m16 < G;
+    float4 qraw[2 * KS];
     {
-        const bool hv = m16 < G;
         const float* qrow = a.q + ((int64_t)seq * a.n_q_heads + kvh * G + (hv ? m16 : 0)) * D;
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
-            const float4 x0 = *reinterpret_cast<const float4*>(qrow + 32 * s + 8 * g);
-            const float4 x1 = *reinterpret_cast<const float4*>(qrow + 32 * s + 8 * g + 4);
-            const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-            f16x8 h, l;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float x = hv ? xs[e] : 0.0f;
-                const _Float16 hi = (_Float16)x;
-                h[e] = hi;
-                l[e] = (_Float16)(x - (float)hi);
-            }
-            qhi[s] = __builtin_bit_cast(u32x4, h);
-            qlo[s] = __builtin_bit_cast(u32x4, l);
+            qraw[2 * s] = *reinterpret_cast<const float4*>(qrow + 32 * s + 8 * g);
+            qraw[2 * s + 1] = *reinterpret_cast<const float4*>(qrow + 32 * s + 8 * g + 4);
         }
     }
 
-    // ---- page ids of this partition, staged once in LDS (entry i = logical page
-    // t0/P + i); every later lookup is an LDS read instead of a dependent load.
-    extern __shared__ int32_t sm_pages[];
-    {
-        const int32_t* bt = a.block_tables + (int64_t)seq * a.max_pages;
-        const int first = t0 >> a.page_shift;
-        const int n_pages = ((t1 - 1) >> a.page_shift) - first + 1;
-        for (int i = threadIdx.x; i < n_pages; i += blockDim.x) sm_pages[i] = bt[first + i];
-    }
-    __syncthreads();
-    const int page_base = t0 >> a.page_shift;
-    const int sh = a.page_shift;
     const int64_t page_elems = (int64_t)Hkv * P * D;   // one page of one cache, all heads
     const uint16_t* kc = a.k_cache;
     const uint16_t* vc = a.v_cache;
     // token row of this lane inside a chunk for K block 0 (block 1 is +4)
     const int tk = 8 * (m16 >> 2) + (m16 & 3);
 
-    auto load_chunk = [&](int c0, ChunkRegs<D>& r) {
+    // chunk c0's K rows (tokens clamped to L-1) and V^T rows; page_of maps a
+    // token to its physical page
+    auto load_chunk_with = [&](int c0, ChunkRegs<D>& r, auto page_of) __attribute__((always_inline)) {
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
             const int t = min(c0 + tk + 4 * b, L - 1);
-            const int page = sm_pages[(t >> sh) - page_base];
-            const uint16_t* row = kc + page * page_elems + ((kvh * P + (t & (P - 1))) * D + 8 * g);
+            const uint16_t* row = kc + page_of(t) * page_elems + ((kvh * P + (t & (P - 1))) * D + 8 * g);
 #pragma unroll
             for (int s = 0; s < KS; ++s) r.k[b][s] = ld16(row + 32 * s);
         }
         int tv = c0 + 8 * g;
         if (tv > L - 1) tv = (L - 1) & ~7;
-        const int vpage = sm_pages[(tv >> sh) - page_base];
-        const uint16_t* vrow = vc + vpage * page_elems + ((kvh * D + m16) * P + (tv & (P - 1)));
+        const uint16_t* vrow = vc + page_of(tv) * page_elems + ((kvh * D + m16) * P + (tv & (P - 1)));
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) r.v[nb] = ld16(vrow + (int64_t)16 * nb * P);
     };
+    auto load_chunk = [&](int c0, ChunkRegs<D>& r) __attribute__((always_inline)) {
+        load_chunk_with(c0, r, [&](int t) { return sm_pages[(t >> sh) - page_base]; });
+    };
+
+    constexpr int NBUF = kDecodeBuffers;
+    constexpr int stride = kWaves * kChunk;
+    const int cfirst = t0 + wave * kChunk;
+    ChunkRegs<D> r[NBUF];
+    const bool chunk_in_page = P >= kChunk;
+    if (chunk_in_page && cfirst < t1) {
+        const int page0 = bt[cfirst >> sh];
+        load_chunk_with(cfirst, r[0], [&](int) { return page0; });
+    }
+    if ((int)threadIdx.x < n_pages) sm_pages[threadIdx.x] = pt0;
+    for (int i = threadIdx.x + blockDim.x; i < n_pages; i += blockDim.x) sm_pages[i] = bt[page_base + i];
+    __syncthreads();
+
+    u32x4 qhi[KS], qlo[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        const float4 x0 = qraw[2 * s];
+        const float4 x1 = qraw[2 * s + 1];
+        const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+        f16x8 h, l;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float x = hv ? xs[e] : 0.0f;
+            const _Float16 hi = (_Float16)x;
+            h[e] = hi;
+            l[e] = (_Float16)(x - (float)hi);
+        }
+        qhi[s] = __builtin_bit_cast(u32x4, h);
+        qlo[s] = __builtin_bit_cast(u32x4, l);
+    }
 
     float m_run = -INFINITY;
     float l_run = 0.0f;
@@ -213,23 +237,30 @@ __global__ __launch_bounds__(256, 2) void decode_partition_kernel(DecodeArgs a) 
         }
     };
 
-    // ---- stream the wave's chunks (wave w takes chunks w, w+4, ...), two
-    // register sets so the next chunk's loads are in flight during compute.
-    const int stride = kWaves * kChunk;
-    int c = t0 + wave * kChunk;
-    if (c < t1) {
-        ChunkRegs<D> ra, rb;
-        load_chunk(c, ra);
-        while (true) {
-            const int cb = c + stride;
-            if (cb < t1) load_chunk(cb, rb);
-            compute_chunk(c, ra);
-            if (cb >= t1) break;
-            const int ca = cb + stride;
-            if (ca < t1) load_chunk(ca, ra);
-            compute_chunk(cb, rb);
-            if (ca >= t1) break;
-            c = ca;
+    // ---- stream the wave's chunks (wave w takes chunks w, w+4, ...) through
+    // kDecodeBuffers register sets, kDecodeBuffers-1 chunks of loads in flight
+    // during each compute.  Loads are issued unconditionally (a chunk past the
+    // wave's last one reloads the last one, an L2 hit whose data is unused), so
+    // every path issues the same loads and the in-order vmcnt accounting lets a
+    // chunk's compute wait for its own loads only.
+    if (cfirst < t1) {
+        const int last_c = cfirst + ((t1 - 1 - cfirst) / stride) * stride;
+        if (!chunk_in_page) load_chunk(cfirst, r[0]);
+#pragma unroll
+        for (int j = 1; j < NBUF - 1; ++j) load_chunk(min(cfirst + j * stride, last_c), r[j]);
+        for (int it = 0;; it += NBUF) {
+            bool done = false;
+#pragma unroll
+            for (int j = 0; j < NBUF; ++j) {
+                const int cj = cfirst + (it + j) * stride;
+                if (cj >= t1) {
+                    done = true;
+                    break;
+                }
+                load_chunk(min(cj + (NBUF - 1) * stride, last_c), r[(j + NBUF - 1) % NBUF]);
+                compute_chunk(cj, r[j]);
+            }
+            if (done) break;
         }
     }
 
