@@ -25,12 +25,12 @@ is pinned by tests that do not re-type its formula (brute force, library
 routines, closed forms, invariants).
 """
 from .attention import (expand_per_token, gather_logical, paged_attention, paged_decode,
-                        partitioned_decode, lse_combine)
+                        partitioned_decode, lse_combine, unified_attention)
 from .cache_ops import reshape_and_cache, copy_blocks
 from .allocator import AllocatorModel, PoolError, NoPagesError, StateError, InvalidError
 
 __all__ = [
     "expand_per_token", "gather_logical", "paged_attention", "paged_decode",
-    "partitioned_decode", "lse_combine", "reshape_and_cache", "copy_blocks",
+    "partitioned_decode", "lse_combine", "unified_attention", "reshape_and_cache", "copy_blocks",
     "AllocatorModel", "PoolError", "NoPagesError", "StateError", "InvalidError",
 ]

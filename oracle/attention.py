@@ -149,3 +149,53 @@ def lse_combine(m, l, acc):
     num = np.einsum("shp,shpd->shd", w, acc)
     den = np.einsum("shp,shp->sh", w, l)
     return num / den[..., None]
+
+
+def unified_attention(q, k_pool, v_pool, span, cell_seq, cell_pos, token_seq, token_pos,
+                      scale) -> np.ndarray:
+    """Masked attention over one unified cache span (page "面向多并发长上下文的
+    llama.cpp 分页式 KV Cache 与计算加速优化", section 作品简介: the original cache
+    the method replaces, where every query of a ubatch faces one physical span
+    of cells from all sequences, free cells and padding, and the mask excludes
+    what does not belong to it).
+
+    The span is cells 0..span-1 of the pool read as one flat array: cell c is
+    page c // P, slot c % P.  Cell c holds position ``cell_pos[c]`` of sequence
+    ``cell_seq[c]`` (-1: free or padding).  Token i (sequence ``token_seq[i]``,
+    -1 = padding, position ``token_pos[i]``) sees exactly the cells with
+    ``cell_seq == token_seq[i]`` and ``cell_pos <= token_pos[i]``; the result is
+    softmax attention over those cells, float64 ``[T][Hq][D]``.  Padding tokens
+    and tokens that see no cell get a zero row.
+
+    Pinned by: equality with :func:`paged_attention` on the span view of paged
+    cases (table gather against masked scan), a pure-Python brute force, and
+    invariance to NaN in free cells and to page order (tests/test_oracle.py)."""
+    q = np.asarray(q)
+    T, n_q, head_dim = q.shape
+    num_pages, n_kv, page_size, _ = k_pool.shape
+    G = n_q // n_kv
+    span = int(span)
+    if span > num_pages * page_size:
+        raise ValueError("span exceeds the pool")
+    scale64 = float(np.float32(scale))
+    cseq = np.asarray(cell_seq, dtype=np.int64)[:span]
+    cpos = np.asarray(cell_pos, dtype=np.int64)[:span]
+    cells = np.arange(span)
+    q64 = q.astype(np.float64)
+    out = np.zeros((T, n_q, head_dim), dtype=np.float64)
+    for i in range(T):
+        s, p = int(token_seq[i]), int(token_pos[i])
+        if s < 0:
+            continue
+        vis = cells[(cseq == s) & (cpos <= p)]
+        if vis.size == 0:
+            continue
+        K = k_pool[vis // page_size, :, vis % page_size, :].astype(np.float64)   # [n][Hkv][D]
+        V = v_pool[vis // page_size, :, :, vis % page_size].astype(np.float64)   # [n][Hkv][D]
+        for g in range(n_kv):
+            Qg = q64[i, g * G:(g + 1) * G, :]
+            z = scale64 * (Qg @ K[:, g, :].T)
+            z -= z.max(axis=1, keepdims=True)
+            w = np.exp(z)
+            out[i, g * G:(g + 1) * G, :] = (w @ V[:, g, :]) / w.sum(axis=1, keepdims=True)
+    return out

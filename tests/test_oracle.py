@@ -443,3 +443,112 @@ def test_append_cow_of_partial_shared_page():
     assert list(slots) == [cow[1] * 16 + 5, cow[1] * 16 + 6, cow[1] * 16 + 7]
     slots2, cow2 = pool.seq_append(a, 1)
     assert cow2 is None and list(slots2) == [pool.pages[a][2] * 16 + 5]
+
+
+# ---------------------------------------------------------------- unified span
+
+def _row_lens(c):
+    """Cells each table row holds in a prefill case (its tokens' largest kv_len)."""
+    lens = np.zeros(c.block_tables.shape[0], dtype=np.int64)
+    for r, kl in zip(c.token_row, c.token_kv_len):
+        if r >= 0:
+            lens[r] = max(lens[r], kl)
+    return lens
+
+
+def brute_force_unified(q, k_pool, v_pool, span, cell_seq, cell_pos, token_seq, token_pos, scale):
+    """Scalar masked scan of the flat span with math.fsum / math.exp."""
+    _, n_kv, P, D = k_pool.shape
+    T, n_q, _ = q.shape
+    G = n_q // n_kv
+    sc = float(np.float32(scale))
+    out = np.zeros((T, n_q, D))
+    for i in range(T):
+        if token_seq[i] < 0:
+            continue
+        cells = [c for c in range(span) if cell_seq[c] == token_seq[i] and cell_pos[c] <= token_pos[i]]
+        for h in range(n_q):
+            g = h // G
+            z = [sc * math.fsum(float(q[i, h, d]) * float(k_pool[c // P, g, c % P, d]) for d in range(D))
+                 for c in cells]
+            m = max(z)
+            w = [math.exp(x - m) for x in z]
+            den = math.fsum(w)
+            for d in range(D):
+                out[i, h, d] = math.fsum(wt * float(v_pool[c // P, g, d, c % P]) for wt, c in zip(w, cells)) / den
+    return out
+
+
+def test_unified_equals_paged_decode():
+    """Masked scan of the span (free NaN pages included) equals the table gather."""
+    c = W.tiny_decode()
+    span, cs, cp = W.unified_view(c.block_tables, c.kv_lens, c.num_pages, c.page_size)
+    assert span > int(c.kv_lens.sum())          # the span holds free cells as well
+    S = len(c.kv_lens)
+    got = oracle.unified_attention(c.q, c.k_pool, c.v_pool, span, cs, cp, np.arange(S), c.kv_lens - 1,
+                                   c.scale)
+    ref = oracle.paged_decode(c.q, c.k_pool, c.v_pool, c.block_tables, c.kv_lens, c.scale)
+    assert np.all(np.isfinite(got))
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("order", ["round_robin", "grouped"])
+def test_unified_equals_paged_prefill(order):
+    c, k, v = _small_prefill(order=order)
+    span, cs, cp = W.unified_view(c.block_tables, _row_lens(c), c.num_pages, c.page_size)
+    got = oracle.unified_attention(c.q, k, v, span, cs, cp, c.token_row, c.token_pos, c.scale)
+    ref = oracle.paged_attention(c.q, k, v, c.block_tables, c.token_row, c.token_kv_len,
+                                 c.token_pos, c.scale)
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-13)
+
+
+def test_unified_brute_force_with_padding_and_free_cells():
+    rng = np.random.default_rng(31)
+    N, Hkv, P, D, Hq = 6, 2, 4, 8, 4
+    k = rng.standard_normal((N, Hkv, P, D)).astype(np.float16)
+    v = rng.standard_normal((N, Hkv, D, P)).astype(np.float16)
+    span = 22
+    cs = rng.integers(-1, 3, size=span).astype(np.int32)   # three sequences and free cells
+    cp = np.zeros(span, dtype=np.int32)
+    for s in range(3):
+        idx = np.nonzero(cs == s)[0]
+        cp[idx] = rng.permutation(len(idx))                # positions scattered over the span
+    for c in np.nonzero(cs < 0)[0]:
+        k[c // P, :, c % P, :] = np.nan
+        v[c // P, :, :, c % P] = np.nan
+    T = 7
+    ts = np.array([0, 1, 2, -1, 0, 2, 1], dtype=np.int32)
+    tp = np.array([int((cs == s).sum()) - 1 if s >= 0 else 0 for s in ts], dtype=np.int32)
+    tp[4] = 1
+    q = rng.standard_normal((T, Hq, D)).astype(np.float32)
+    sc = np.float32(1 / math.sqrt(D))
+    got = oracle.unified_attention(q, k, v, span, cs, cp, ts, tp, sc)
+    ref = brute_force_unified(q, k, v, span, cs, cp, ts, tp, sc)
+    assert np.all(np.isfinite(got)) and np.all(got[3] == 0)
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-13)
+
+
+def test_unified_page_order_and_poison_invariance():
+    """Moving the pages (with their cell labels) or replacing the poison in free
+    cells by finite garbage leaves the result unchanged."""
+    c = W.tiny_decode()
+    S = len(c.kv_lens)
+    span, cs, cp = W.unified_view(c.block_tables, c.kv_lens, c.num_pages, c.page_size)
+    out = oracle.unified_attention(c.q, c.k_pool, c.v_pool, span, cs, cp, np.arange(S), c.kv_lens - 1,
+                                   c.scale)
+    pi = np.random.default_rng(8).permutation(c.num_pages)
+    k2 = np.empty_like(c.k_pool)
+    v2 = np.empty_like(c.v_pool)
+    k2[pi] = c.k_pool
+    v2[pi] = c.v_pool
+    bt2 = np.where(c.block_tables >= 0, pi[np.maximum(c.block_tables, 0)], -1)
+    span2, cs2, cp2 = W.unified_view(bt2, c.kv_lens, c.num_pages, c.page_size)
+    out2 = oracle.unified_attention(c.q, k2, v2, span2, cs2, cp2, np.arange(S), c.kv_lens - 1, c.scale)
+    np.testing.assert_allclose(out2, out, rtol=1e-13, atol=1e-14)
+    k3 = c.k_pool.copy()
+    v3 = c.v_pool.copy()
+    rng = np.random.default_rng(9)
+    k3[np.isnan(k3)] = rng.standard_normal(int(np.isnan(k3).sum())).astype(np.float16)
+    v3[np.isnan(v3)] = rng.standard_normal(int(np.isnan(v3).sum())).astype(np.float16)
+    out3 = oracle.unified_attention(c.q, k3, v3, span, cs, cp, np.arange(S), c.kv_lens - 1, c.scale)
+    np.testing.assert_array_equal(out3, out)

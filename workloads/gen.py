@@ -361,3 +361,44 @@ def prefill_pairs(token_kv_len, token_pos, token_row=None) -> int:
 def attention_flops(pairs: int, n_q_heads: int, head_dim: int) -> int:
     """QK^T and PV at 2 flop per multiply-add: 4 * D * Hq per attended pair."""
     return 4 * head_dim * n_q_heads * int(pairs)
+
+
+# ---------------------------------------------------------------- unified span
+
+def unified_view(block_tables, seq_lens, num_pages, page_size):
+    """The unified-cache view of a paged pool: the span is cells 0..span-1 of the
+    pool read as one flat array (cell c = page c // P, slot c % P), covering every
+    page any sequence uses; ``cell_seq[c]`` / ``cell_pos[c]`` say which sequence
+    position the cell holds (-1 / 0 for free cells and the unused tail of a
+    sequence's last page).  ``seq_lens[r]`` is the number of cells row r of
+    ``block_tables`` holds.  Returns (span, cell_seq int32 [span], cell_pos int32
+    [span]); the span is rounded up to a whole page."""
+    bt = np.asarray(block_tables)
+    cell_seq = np.full(num_pages * page_size, -1, dtype=np.int32)
+    cell_pos = np.zeros(num_pages * page_size, dtype=np.int32)
+    last = -1
+    for r, n in enumerate(np.asarray(seq_lens, dtype=np.int64)):
+        t = np.arange(int(n))
+        pages = bt[r, t // page_size].astype(np.int64)
+        cells = pages * page_size + t % page_size
+        cell_seq[cells] = r
+        cell_pos[cells] = t
+        if n > 0:
+            last = max(last, int(pages.max()))
+    span = (last + 1) * page_size
+    return span, cell_seq[:span].copy(), cell_pos[:span].copy()
+
+
+def unified_decode_bytes(span, n_kv_heads, head_dim, elem_bytes=2) -> int:
+    """Bytes of K and V a unified-span pass reads: every cell of the span once."""
+    return int(span) * n_kv_heads * head_dim * elem_bytes * 2
+
+
+def unified_pairs(span, n_tokens_real) -> int:
+    """(query token, cell) pairs a unified-span pass computes: every real token
+    against every cell of the span (the mask removes most of them from the
+    result, not from the work)."""
+    return int(span) * int(n_tokens_real)
+
+
+__all__ += ["unified_view", "unified_decode_bytes", "unified_pairs"]
