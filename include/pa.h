@@ -236,6 +236,40 @@ pa_status pa_prefill(const pa_cache_desc* desc, const void* k_cache, const void*
                      float scale, int32_t kv_splits, void* workspace, size_t workspace_bytes,
                      pa_stream stream);
 
+/* ---------------------------------------------------------------------------
+ * Unified-span attention: the baseline UA-PagedAttention replaces ([UA]
+ * 作品简介): with several sequences in one unified KV cache, every query of a
+ * ubatch faces one physical span of cells from all sequences, free cells and
+ * padding; the mask removes the cells that do not belong to the query from
+ * the result but not from the data access and the computation.  Provided to
+ * measure the paged path against it on the same pool.
+ *
+ * The span is cells 0..span-1 of the pool read as one flat array: cell c is
+ * page c / page_size, slot c % page_size.  Every token scans all span cells.
+ *   q, out       device fp32 [n_tokens][n_q_heads][head_dim] (q rounded to
+ *                binary16 for the products, as in pa_prefill)
+ *   cell_seq     device int32 [span]: sequence id whose position cell_pos[c]
+ *                cell c holds, -1 for a free or padding cell (its K and V may
+ *                hold anything, NaN included)
+ *   cell_pos     device int32 [span]
+ *   token_seq    device int32 [n_tokens]: the token's sequence (-1 = padding)
+ *   token_pos    device int32 [n_tokens]: the token's position
+ * Token i attends to the cells with cell_seq == token_seq[i] and cell_pos <=
+ * token_pos[i]; a padding token, or one that sees no cell, gets a zero row.
+ * Limits: sequence ids in [0, 512) and positions in [0, 2^22) (cells and
+ * tokens); outside them the mask is undefined (no out-of-bounds access).
+ * span must be in [1, num_pages * page_size] (PA_ERR_INVALID otherwise).
+ * kv_splits and the workspace follow pa_prefill's rules (same counter
+ * contract). */
+size_t pa_unified_workspace_bytes(const pa_cache_desc* desc, int32_t n_tokens, int32_t n_q_heads,
+                                  int32_t span, int32_t kv_splits);
+pa_status pa_unified_attention(const pa_cache_desc* desc, const void* k_cache, const void* v_cache,
+                               const float* q, float* out, int32_t span, const int32_t* cell_seq,
+                               const int32_t* cell_pos, const int32_t* token_seq,
+                               const int32_t* token_pos, int32_t n_tokens, int32_t n_q_heads,
+                               float scale, int32_t kv_splits, void* workspace,
+                               size_t workspace_bytes, pa_stream stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -24,7 +24,8 @@ __all__ = [
     "PaError", "InvalidError", "UnsupportedError", "NoPagesError", "StateError", "HipError",
     "WorkspaceError", "CacheDesc", "cache_desc", "pa_version", "pa_last_error", "Pool",
     "pa_reshape_and_cache", "pa_copy_blocks", "pa_decode_workspace_bytes", "pa_decode",
-    "pa_prefill_workspace_bytes", "pa_prefill", "library_path",
+    "pa_prefill_workspace_bytes", "pa_prefill", "pa_unified_workspace_bytes",
+    "pa_unified_attention", "library_path",
 ]
 
 
@@ -310,4 +311,37 @@ def pa_prefill(q, k_cache, v_cache, block_tables, token_row, token_kv_len, token
         _dev(token_row, torch.int32, "token_row", 1), _dev(token_kv_len, torch.int32, "token_kv_len", 1),
         _dev(token_pos, torch.int32, "token_pos", 1), _i32p(rh), _i32p(kh), _i32p(ph), T, n_rows,
         max_pages, Hq, float(scale), int(kv_splits), ws_ptr, ws_bytes, _stream_ptr(stream)))
+    return out
+
+
+def pa_unified_workspace_bytes(desc: CacheDesc, n_tokens: int, n_q_heads: int, span: int,
+                               kv_splits: int = 0) -> int:
+    return int(_L().pa_unified_workspace_bytes(ctypes.byref(desc), int(n_tokens), int(n_q_heads),
+                                               int(span), int(kv_splits)))
+
+
+def pa_unified_attention(q, k_cache, v_cache, span: int, cell_seq, cell_pos, token_seq, token_pos,
+                         scale: float, kv_splits: int = 0, out=None, workspace=None, stream=None):
+    """Unified-span attention (the baseline the paged path replaces): every token
+    scans cells 0..span-1 of the pool under the (cell_seq, cell_pos) mask.
+    q fp32 [T][Hq][D] -> out fp32 [T][Hq][D].  Workspace rules as pa_prefill."""
+    import torch
+    desc = cache_desc(k_cache, v_cache)
+    T, Hq, D = (int(x) for x in q.shape)
+    if D != desc.head_dim:
+        raise ValueError("q head_dim does not match the cache")
+    if out is None:
+        out = torch.empty_like(q)
+    need = pa_unified_workspace_bytes(desc, T, Hq, span, kv_splits)
+    if workspace is None and need > 0:
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(_L().pa_unified_attention(
+        ctypes.byref(desc), _dev(k_cache, torch.float16, "k_cache", 4),
+        _dev(v_cache, torch.float16, "v_cache", 4), _dev(q, torch.float32, "q", 3),
+        _dev(out, torch.float32, "out", 3), int(span), _dev(cell_seq, torch.int32, "cell_seq", 1),
+        _dev(cell_pos, torch.int32, "cell_pos", 1), _dev(token_seq, torch.int32, "token_seq", 1),
+        _dev(token_pos, torch.int32, "token_pos", 1), T, Hq, float(scale), int(kv_splits), ws_ptr,
+        ws_bytes, _stream_ptr(stream)))
     return out

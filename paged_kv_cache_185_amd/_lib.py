@@ -50,6 +50,10 @@ SIGNATURES = {
     "pa_prefill": (c_i32, [CacheDesc_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                            c_void_p, c_void_p, c_void_p, c_i32_p, c_i32_p, c_i32_p, c_i32, c_i32,
                            c_i32, c_i32, c_float, c_i32, c_void_p, c_size_t, c_void_p]),
+    "pa_unified_workspace_bytes": (c_size_t, [CacheDesc_p, c_i32, c_i32, c_i32, c_i32]),
+    "pa_unified_attention": (c_i32, [CacheDesc_p, c_void_p, c_void_p, c_void_p, c_void_p, c_i32,
+                                     c_void_p, c_void_p, c_void_p, c_void_p, c_i32, c_i32, c_float,
+                                     c_i32, c_void_p, c_size_t, c_void_p]),
 }
 
 _lib = None

@@ -144,6 +144,48 @@ struct PrefillPlan {
     size_t ml_off = 0, acc_off = 0, bytes = 0;
 };
 
+// KV split size, per-tile split counts and workspace layout, given the tiles.
+pa_status finish_prefill_plan(const pa_cache_desc* d, int32_t kv_splits, int64_t sum_kv,
+                              int64_t max_kv, PrefillPlan* plan) {
+    const int64_t KT = kPrefillKvTile;
+    int64_t split_tokens;
+    if (kv_splits == 1) {
+        split_tokens = round_up(std::max<int64_t>(max_kv, 1), KT);
+    } else if (kv_splits > 1) {
+        split_tokens = round_up(std::max<int64_t>((max_kv + kv_splits - 1) / kv_splits, 1), KT);
+    } else {
+        // one 8-wave workgroup per compute unit (256 CUs): enough (tile, split)
+        // pairs per KV head to cover them, splits no shorter than 256 keys
+        const int64_t need = (256 + d->n_kv_heads - 1) / d->n_kv_heads;
+        if ((int64_t)plan->tiles.size() >= need)
+            split_tokens = round_up(std::max<int64_t>(max_kv, 1), KT);
+        else
+            split_tokens = std::max<int64_t>(256, round_up((sum_kv + need - 1) / need, KT));
+    }
+    split_tokens = std::min<int64_t>(split_tokens, round_up(std::max<int64_t>(max_kv, 1), KT));
+    // the kernel stages one split's page ids in LDS: very long ranges are split
+    const int64_t lds_cap = (int64_t)(kPrefillMaxPageEntries - 1) * d->page_size / KT * KT;
+    split_tokens = std::min(split_tokens, lds_cap);
+    plan->split_tokens = (int32_t)split_tokens;
+    plan->max_splits = 1;
+    for (auto& t : plan->tiles) {
+        t.n_splits = (int32_t)((t.kv_end + split_tokens - 1) / split_tokens);
+        plan->max_splits = std::max(plan->max_splits, t.n_splits);
+    }
+    if (plan->max_splits > 1) {
+        // counters first (zero-filled region shared with pa_decode's
+        // convention), then per (tile, KV head, split) slot the (m, l) pairs
+        // and the accumulators of every lane of the workgroup
+        const size_t groups = plan->tiles.size() * (size_t)d->n_kv_heads;
+        const size_t slots = groups * plan->max_splits;
+        const size_t threads = (size_t)prefill_threads();
+        plan->ml_off = align256(std::max<size_t>(kDecodeCounterBytes, groups * 4));
+        plan->acc_off = plan->ml_off + align256(slots * threads * 2 * 4);
+        plan->bytes = plan->acc_off + align256(slots * threads * (size_t)d->head_dim / 2 * 4);
+    }
+    return PA_OK;
+}
+
 pa_status plan_prefill(const pa_cache_desc* d, int32_t n_tokens, int32_t n_q_heads, int32_t n_rows,
                        int32_t max_pages, const int32_t* row, const int32_t* kv_len,
                        const int32_t* pos, int32_t kv_splits, PrefillPlan* plan) {
@@ -196,41 +238,66 @@ pa_status plan_prefill(const pa_cache_desc* d, int32_t n_tokens, int32_t n_q_hea
         }
         b = e;
     }
-    const int64_t KT = kPrefillKvTile;
-    int64_t split_tokens;
-    if (kv_splits == 1) {
-        split_tokens = round_up(std::max<int64_t>(max_kv, 1), KT);
-    } else if (kv_splits > 1) {
-        split_tokens = round_up(std::max<int64_t>((max_kv + kv_splits - 1) / kv_splits, 1), KT);
-    } else {
-        // one 8-wave workgroup per compute unit (256 CUs): enough (tile, split)
-        // pairs per KV head to cover them, splits no shorter than 256 keys
-        const int64_t need = (256 + d->n_kv_heads - 1) / d->n_kv_heads;
-        if ((int64_t)plan->tiles.size() >= need)
-            split_tokens = round_up(std::max<int64_t>(max_kv, 1), KT);
-        else
-            split_tokens = std::max<int64_t>(256, round_up((sum_kv + need - 1) / need, KT));
+    return finish_prefill_plan(d, kv_splits, sum_kv, max_kv, plan);
+}
+
+// Unified span: tiles are runs of consecutive ubatch tokens, each scanning all
+// `span` cells.
+pa_status plan_unified(const pa_cache_desc* d, int32_t n_tokens, int32_t n_q_heads, int32_t span,
+                       int32_t kv_splits, PrefillPlan* plan) {
+    if (n_tokens < 0) return fail(PA_ERR_INVALID, "pa_unified_attention: n_tokens < 0");
+    if (kv_splits < 0) return fail(PA_ERR_INVALID, "pa_unified_attention: kv_splits < 0");
+    if (span < 1 || (int64_t)span > (int64_t)d->num_pages * d->page_size)
+        return fail(PA_ERR_INVALID, "pa_unified_attention: span must be in [1, num_pages*page_size]");
+    const int tpt = prefill_tokens_per_tile(n_q_heads / d->n_kv_heads);
+    int64_t sum_kv = 0;
+    for (int32_t b = 0; b < n_tokens; b += tpt) {
+        PrefillTile t{};
+        t.row = 0;
+        t.first = b;
+        t.last = std::min(n_tokens, b + tpt) - 1;
+        t.count = t.last - t.first + 1;
+        t.kv_end = span;
+        t.min_vis = 0;
+        t.dense = 1;
+        plan->tiles.push_back(t);
+        sum_kv += span;
     }
-    split_tokens = std::min<int64_t>(split_tokens, round_up(std::max<int64_t>(max_kv, 1), KT));
-    // the kernel stages one split's page ids in LDS: very long ranges are split
-    const int64_t lds_cap = (int64_t)(kPrefillMaxPageEntries - 1) * d->page_size / KT * KT;
-    split_tokens = std::min(split_tokens, lds_cap);
-    plan->split_tokens = (int32_t)split_tokens;
-    plan->max_splits = 1;
-    for (auto& t : plan->tiles) {
-        t.n_splits = (int32_t)((t.kv_end + split_tokens - 1) / split_tokens);
-        plan->max_splits = std::max(plan->max_splits, t.n_splits);
+    return finish_prefill_plan(d, kv_splits, sum_kv, span, plan);
+}
+
+// Fill the common launch arguments from a plan and launch its tiles (at most
+// kMaxTilesPerLaunch per launch) on `stream`.
+pa_status run_prefill_plan(const char* who, const pa_cache_desc* desc, const PrefillPlan& plan,
+                           PrefillArgs a, const void* k_cache, const void* v_cache, const float* q,
+                           float* out, int32_t n_tokens, int32_t n_q_heads, float scale,
+                           void* workspace, pa_stream stream) {
+    a.k_cache = (const uint16_t*)k_cache;
+    a.v_cache = (const uint16_t*)v_cache;
+    a.q = q;
+    a.out = out;
+    if (plan.max_splits > 1) {
+        char* ws = (char*)workspace;
+        a.counters = (int32_t*)ws;
+        a.part_ml = (float*)(ws + plan.ml_off);
+        a.part_acc = (float*)(ws + plan.acc_off);
     }
-    if (plan->max_splits > 1) {
-        // counters first (zero-filled region shared with pa_decode's
-        // convention), then per (tile, KV head, split) slot the (m, l) pairs
-        // and the accumulators of every lane of the workgroup
-        const size_t groups = plan->tiles.size() * (size_t)d->n_kv_heads;
-        const size_t slots = groups * plan->max_splits;
-        const size_t threads = (size_t)prefill_threads();
-        plan->ml_off = align256(std::max<size_t>(kDecodeCounterBytes, groups * 4));
-        plan->acc_off = plan->ml_off + align256(slots * threads * 2 * 4);
-        plan->bytes = plan->acc_off + align256(slots * threads * (size_t)d->head_dim / 2 * 4);
+    a.n_tokens = n_tokens;
+    a.n_q_heads = n_q_heads;
+    a.n_kv_heads = desc->n_kv_heads;
+    a.page_size = desc->page_size;
+    a.page_shift = log2_exact(desc->page_size);
+    a.head_dim = desc->head_dim;
+    a.split_tokens = plan.split_tokens;
+    a.max_splits = plan.max_splits;
+    a.scale_log2 = (float)((double)scale * kLog2e);
+    const int n_tiles = (int)plan.tiles.size();
+    for (int b = 0; b < n_tiles; b += kMaxTilesPerLaunch) {
+        const int nb = std::min(kMaxTilesPerLaunch, n_tiles - b);
+        a.group_base = b * desc->n_kv_heads;
+        hipError_t e = launch_prefill(a, plan.tiles.data() + b, nb, plan.max_splits,
+                                      (hipStream_t)stream);
+        if (e != hipSuccess) return hip_fail(who, e);
     }
     return PA_OK;
 }
@@ -392,44 +459,57 @@ pa_status pa_prefill(const pa_cache_desc* desc, const void* k_cache, const void*
         return fail(PA_ERR_WORKSPACE, "pa_prefill: workspace missing or too small (need " +
                                           std::to_string(plan.bytes) + " bytes)");
     PrefillArgs a{};
-    a.k_cache = (const uint16_t*)k_cache;
-    a.v_cache = (const uint16_t*)v_cache;
-    a.q = q;
-    a.out = out;
     a.block_tables = block_tables;
     a.token_row = token_row;
     a.token_kv_len = token_kv_len;
     a.token_pos = token_pos;
-    if (plan.max_splits > 1) {
-        char* ws = (char*)workspace;
-        a.counters = (int32_t*)ws;
-        a.part_ml = (float*)(ws + plan.ml_off);
-        a.part_acc = (float*)(ws + plan.acc_off);
-    }
-    a.n_tokens = n_tokens;
     a.max_pages = max_pages;
-    a.n_q_heads = n_q_heads;
-    a.n_kv_heads = desc->n_kv_heads;
-    a.page_size = desc->page_size;
-    a.page_shift = log2_exact(desc->page_size);
-    a.head_dim = desc->head_dim;
-    a.split_tokens = plan.split_tokens;
-    a.max_splits = plan.max_splits;
-    a.scale_log2 = (float)((double)scale * kLog2e);
-    const int n_tiles = (int)plan.tiles.size();
-    for (int b = 0; b < n_tiles; b += kMaxTilesPerLaunch) {
-        const int nb = std::min(kMaxTilesPerLaunch, n_tiles - b);
-        a.group_base = b * desc->n_kv_heads;
-        hipError_t e = launch_prefill(a, plan.tiles.data() + b, nb, plan.max_splits,
-                                      (hipStream_t)stream);
-        if (e != hipSuccess) return hip_fail("pa_prefill", e);
-    }
+    if ((st = run_prefill_plan("pa_prefill", desc, plan, a, k_cache, v_cache, q, out, n_tokens,
+                               n_q_heads, scale, workspace, stream)) != PA_OK)
+        return st;
     if (plan.has_padding) {
         hipError_t e = launch_zero_rows(out, token_row, n_tokens, n_q_heads * desc->head_dim,
                                         (hipStream_t)stream);
         if (e != hipSuccess) return hip_fail("pa_prefill (padding rows)", e);
     }
     return PA_OK;
+}
+
+size_t pa_unified_workspace_bytes(const pa_cache_desc* desc, int32_t n_tokens, int32_t n_q_heads,
+                                  int32_t span, int32_t kv_splits) {
+    if (check_desc("pa_unified_workspace_bytes", desc) != PA_OK) return 0;
+    if (check_heads("pa_unified_workspace_bytes", desc, n_q_heads) != PA_OK) return 0;
+    PrefillPlan plan;
+    if (plan_unified(desc, n_tokens, n_q_heads, span, kv_splits, &plan) != PA_OK) return 0;
+    return plan.bytes;
+}
+
+pa_status pa_unified_attention(const pa_cache_desc* desc, const void* k_cache, const void* v_cache,
+                               const float* q, float* out, int32_t span, const int32_t* cell_seq,
+                               const int32_t* cell_pos, const int32_t* token_seq,
+                               const int32_t* token_pos, int32_t n_tokens, int32_t n_q_heads,
+                               float scale, int32_t kv_splits, void* workspace,
+                               size_t workspace_bytes, pa_stream stream) {
+    pa_status st = check_desc("pa_unified_attention", desc);
+    if (st != PA_OK) return st;
+    if ((st = check_heads("pa_unified_attention", desc, n_q_heads)) != PA_OK) return st;
+    if (n_tokens == 0) return PA_OK;
+    if (!k_cache || !v_cache || !q || !out || !cell_seq || !cell_pos || !token_seq || !token_pos)
+        return fail(PA_ERR_INVALID, "pa_unified_attention: null pointer");
+    if (!std::isfinite(scale)) return fail(PA_ERR_INVALID, "pa_unified_attention: scale must be finite");
+    PrefillPlan plan;
+    if ((st = plan_unified(desc, n_tokens, n_q_heads, span, kv_splits, &plan)) != PA_OK) return st;
+    if (plan.bytes > 0 && (!workspace || workspace_bytes < plan.bytes))
+        return fail(PA_ERR_WORKSPACE, "pa_unified_attention: workspace missing or too small (need " +
+                                          std::to_string(plan.bytes) + " bytes)");
+    PrefillArgs a{};
+    a.token_row = token_seq;
+    a.token_pos = token_pos;
+    a.unified = 1;
+    a.cell_seq = cell_seq;
+    a.cell_pos = cell_pos;
+    return run_prefill_plan("pa_unified_attention", desc, plan, a, k_cache, v_cache, q, out,
+                            n_tokens, n_q_heads, scale, workspace, stream);
 }
 
 }  // extern "C"

@@ -103,6 +103,12 @@ struct PrefillArgs {
     int32_t n_tiles;        // tiles in the current launch (set by launch_prefill)
     int32_t group_base;     // first group of the current launch
     float scale_log2;
+    // unified-span mode (pa_unified_attention): keys are cells 0..span-1 of the
+    // pool read as one flat array; cell c holds position cell_pos[c] of
+    // sequence cell_seq[c] (-1 = free); token_row holds each token's sequence
+    int32_t unified;
+    const int32_t* cell_seq;
+    const int32_t* cell_pos;
 };
 
 int prefill_tokens_per_tile(int group);   // query tokens per tile for GQA group size

@@ -62,7 +62,8 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kRows = 32 * kWaves;          // query rows (token x head) per tile
 constexpr int kKvTile = kPrefillKvTile;     // 64 keys per iteration
 constexpr float kRescaleSlack = 8.0f;       // log2 units the max may lag by
-constexpr int kKDepth = 4;                  // K operand k-steps read ahead of the score MFMAs
+constexpr int kCellPosBits = 22;             // unified span: cell code = seq << 22 | pos
+constexpr int kKDepth = 2;                  // K operand k-steps read ahead of the score MFMAs
 constexpr int kVDepth = 1;                  // V operand k-steps read ahead of the P.V MFMAs
 
 struct TileList {
@@ -115,25 +116,33 @@ struct Smem {
     u32x4 v[2][D * kKvTile / 8];   // [buf][d][8 chunks of 8 keys], chunk swizzled by d % 8
     int32_t tok[kRows];
     int32_t last;   // this workgroup combines the tile's splits
+    int32_t kcode[2][kKvTile];  // unified span: cell code of each key of a K buffer
 };
 
 template <int D>
 struct StagingK {
     static constexpr int KC = kKvTile * D / 8 / kThreads;   // 16-byte chunks per thread
     u32x4 k[KC];
+    int kcode;   // unified span: cell code of key (tid % 64) of the tile
 };
 
 template <int D>
 struct StagingV {
     static constexpr int VC = D * kKvTile / 8 / kThreads;   // 16-byte chunks per thread
     u32x4 v[VC];
-    int t0;   // first key of the tile held
+    int t0;           // first key of the tile held
+    uint32_t vlive;   // unified span: bit e = key 8*(tid%8)+e is a written cell
 };
 
 // ONE_PAGE: the page size is a multiple of the 64-key tile, so every tile
 // lies inside one page and its addresses are one scalar page base plus fixed
 // per-thread offsets.
-template <int D, int G, bool ONE_PAGE>
+// UNIFIED: the unified-span baseline.  Tiles are runs of consecutive ubatch
+// tokens whatever their sequence, every tile scans cells 0..span-1 of the pool
+// read as one flat array (page i = cells iP..iP+P-1), and a key is visible to
+// a token iff the cell belongs to the token's sequence at a position <= the
+// token's; free cells (owner -1) have their V zeroed before the MFMA.
+template <int D, int G, bool ONE_PAGE, bool UNIFIED>
 __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, TileList tl) {
     constexpr int TPW = 32 / G;       // tokens per wave
     constexpr int KS = D / 16;        // k-steps of the score product
@@ -169,19 +178,23 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, Til
     const int page_base = kv_begin >> sh;
     const int32_t* bt = a.block_tables + (int64_t)tile.row * a.max_pages;
     const int n_pages = ((kv_end - 1) >> sh) - page_base + 1;
-    const int pt0 = tid < n_pages ? bt[page_base + tid] : 0;
+    // unified span: page i of the span is pool page i
+    const int pt0 = UNIFIED ? page_base + tid : (tid < n_pages ? bt[page_base + tid] : 0);
     // the first tile's page (entry 0), read by every lane at one address
-    const int page0 = bt[page_base];
+    const int page0 = UNIFIED ? page_base : bt[page_base];
     const int ti = wave * TPW + col / G;
     const int hq = col % G;
     const int qh = kvh * G + hq;
     int tok = -1;
-    int tok_kv_len = 0, tok_pos = 0;
+    int tok_kv_len = 0, tok_pos = 0, tok_seq = -1;
     int n_vis = 0;   // keys this lane's query token sees
     float4 qraw[2 * KS];
     auto load_token = [&]() __attribute__((always_inline)) {
         const int t = tok >= 0 ? tok : 0;
-        tok_kv_len = a.token_kv_len[t];
+        if constexpr (UNIFIED)
+            tok_seq = tok >= 0 ? a.token_row[t] : -1;
+        else
+            tok_kv_len = a.token_kv_len[t];
         tok_pos = a.token_pos[t];
         const float* qrow = a.q + ((int64_t)t * a.n_q_heads + qh) * D;
 #pragma unroll
@@ -206,7 +219,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, Til
         }
     }
     if (tid < n_pages) sm_pages[tid] = pt0;
-    for (int i = tid + kThreads; i < n_pages; i += kThreads) sm_pages[i] = bt[page_base + i];
+    for (int i = tid + kThreads; i < n_pages; i += kThreads) sm_pages[i] = UNIFIED ? page_base + i : bt[page_base + i];
     __syncthreads();
     if (!tile.dense) {
         tok = ti < tile.count ? sm.tok[ti] : -1;
@@ -241,22 +254,50 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, Til
         const int id = tid + kThreads * i;
         voff[i] = (id >> 3) * P + 8 * (id & 7);
     }
+    auto load_meta_k = [&](int t0, StagingK<D>& st) __attribute__((always_inline)) {
+        if constexpr (UNIFIED) {
+            // every lane loads (clamped, so the loads are unconditional); lanes
+            // 0..63 of the workgroup store key (tid % 64)'s owner and position
+            const int t = t0 + (tid & (kKvTile - 1));
+            const int tc = min(t, kv_end - 1);
+            const int sq = a.cell_seq[tc];
+            const int ps = a.cell_pos[tc];
+            st.kcode = (t < kv_end && sq >= 0) ? (sq << kCellPosBits) + ps : -1;
+        }
+    };
+    auto load_meta_v = [&](int t0, StagingV<D>& st) __attribute__((always_inline)) {
+        if constexpr (UNIFIED) {
+            // keys 8c..8c+7 of this thread's V chunks: live iff inside the
+            // split and written (owner >= 0)
+            const int tb = t0 + 8 * (tid & 7);
+            uint32_t live = 0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int sq = a.cell_seq[min(tb + e, kv_end - 1)];
+                live |= (tb + e < kv_end && sq >= 0) ? (1u << e) : 0u;
+            }
+            st.vlive = live;
+        }
+    };
     // one-page tiles: keys past kv_end are still inside the tile's
     // (allocated) page; K there is masked out of the scores and V is zeroed
     // at store
     auto load_k_page = [&](int t0, int page, StagingK<D>& st) __attribute__((always_inline)) {
+        load_meta_k(t0, st);
         const uint16_t* kb = kc + page * page_elems + (k_head_off + (t0 & (P - 1)) * D);
 #pragma unroll
         for (int i = 0; i < StagingK<D>::KC; ++i) st.k[i] = *reinterpret_cast<const u32x4*>(kb + koff[i]);
     };
     auto load_v_page = [&](int t0, int page, StagingV<D>& st) __attribute__((always_inline)) {
         st.t0 = t0;
+        load_meta_v(t0, st);
         const uint16_t* vb = vc + page * page_elems + (k_head_off + (t0 & (P - 1)));
 #pragma unroll
         for (int i = 0; i < StagingV<D>::VC; ++i) st.v[i] = *reinterpret_cast<const u32x4*>(vb + voff[i]);
     };
     auto load_k = [&](int t0_req, StagingK<D>& st) __attribute__((always_inline)) {
         const int t0 = min(t0_req, last_t0);
+        if constexpr (!ONE_PAGE) load_meta_k(t0, st);
         if constexpr (ONE_PAGE) {
             load_k_page(t0, __builtin_amdgcn_readfirstlane(sm_pages[(t0 >> sh) - page_base]), st);
         } else {
@@ -275,6 +316,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, Til
     auto load_v = [&](int t0_req, StagingV<D>& st) __attribute__((always_inline)) {
         const int t0 = min(t0_req, last_t0);
         st.t0 = t0;
+        if constexpr (!ONE_PAGE) load_meta_v(t0, st);
         if constexpr (ONE_PAGE) {
             load_v_page(t0, __builtin_amdgcn_readfirstlane(sm_pages[(t0 >> sh) - page_base]), st);
         } else {
@@ -298,11 +340,25 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, Til
             const int c = id % CPR;
             sm.k[buf][key * CPR + (c ^ kswz<D>(key))] = st.k[i];
         }
+        if constexpr (UNIFIED) {
+            if (tid < kKvTile) sm.kcode[buf][tid] = st.kcode;
+        }
     };
     auto store_v = [&](int buf, StagingV<D>& st) __attribute__((always_inline)) {
-        // zero the V halves of keys at or past the visible end (only the last
-        // tile of a split has any)
-        if (st.t0 + kKvTile > kv_end) {
+        if constexpr (UNIFIED) {
+            // zero the V halves of free cells and of keys past the split
+            uint32_t mk[4];
+#pragma unroll
+            for (int w = 0; w < 4; ++w)
+                mk[w] = ((st.vlive >> (2 * w)) & 1u ? 0x0000ffffu : 0u) |
+                        ((st.vlive >> (2 * w + 1)) & 1u ? 0xffff0000u : 0u);
+#pragma unroll
+            for (int i = 0; i < StagingV<D>::VC; ++i)
+#pragma unroll
+                for (int w = 0; w < 4; ++w) st.v[i][w] &= mk[w];
+        } else if (st.t0 + kKvTile > kv_end) {
+            // zero the V halves of keys at or past the visible end (only the
+            // last tile of a split has any)
             const int nvalid = max(0, min(8, kv_end - (st.t0 + 8 * (tid & 7))));
             uint32_t mk[4];
 #pragma unroll
@@ -370,7 +426,27 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, Til
     // Online softmax of the scores (keys t0..t0+63) and O^T += V^T P^T with V
     // buffer `buf`; `full` (uniform) says every query column sees all 64 keys.
     auto smpv = [&](int buf, int t0, bool full) __attribute__((always_inline)) {
-        if (!full) {
+        if constexpr (UNIFIED) {
+            // visible iff the cell is this token's sequence at a position not
+            // after the token's: its code lies in [seq << bits, (seq << bits) +
+            // pos] (free cells are -1); the lane's keys come in runs of 8
+            const uint32_t lo = (uint32_t)(tok_seq << kCellPosBits);
+            const uint32_t span_hi = tok_seq >= 0 ? (uint32_t)tok_pos : 0u;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const int k0 = 32 * kb + 16 * j + 8 * hh;
+                    const int4 c0 = *reinterpret_cast<const int4*>(&sm.kcode[buf][k0]);
+                    const int4 c1 = *reinterpret_cast<const int4*>(&sm.kcode[buf][k0 + 4]);
+                    const int cd[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const bool vis = tok_seq >= 0 && cd[e] >= 0 && (uint32_t)cd[e] - lo <= span_hi;
+                        s[kb][8 * j + e] = vis ? s[kb][8 * j + e] : -INFINITY;
+                    }
+                }
+        } else if (!full) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -443,7 +519,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, Til
 
     // smallest visible length over the tile's tokens (from the plan): tiles
     // ending at or before it need no mask
-    const int min_vis = min(tile.min_vis, kv_end);
+    const int min_vis = UNIFIED ? 0 : min(tile.min_vis, kv_end);
     const int n_tiles = (kv_end - kv_begin + kKvTile - 1) / kKvTile;
 
     // ---- main loop: two wave groups in ping-pong.  Waves 0-3 (group A) and
@@ -535,7 +611,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, Til
         return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
     };
     auto write_out = [&](float l_tot) __attribute__((always_inline)) {
-        const float inv = 1.0f / l_tot;
+        // a token that sees no key (unified span: no cell of its sequence up
+        // to its position) gets a zero row
+        const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
         float* orow = a.out + ((int64_t)tok * a.n_q_heads + qh) * D;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
@@ -636,18 +714,18 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, Til
     if (tok >= 0) write_out(l_tot);
 }
 
-template <int D, bool ONE_PAGE>
-hipError_t launch_prefill_dp(const PrefillArgs& a, const TileList& tl, int n_items, size_t lds,
-                             hipStream_t stream) {
+template <int D, bool ONE_PAGE, bool UNIFIED>
+hipError_t launch_prefill_dpu(const PrefillArgs& a, const TileList& tl, int n_items, size_t lds,
+                              hipStream_t stream) {
     const int G = a.n_q_heads / a.n_kv_heads;
     const dim3 grid((unsigned)n_items);
     const dim3 block(kThreads);
     switch (G) {
-        case 1: hipLaunchKernelGGL((prefill_kernel<D, 1, ONE_PAGE>), grid, block, lds, stream, a, tl); break;
-        case 2: hipLaunchKernelGGL((prefill_kernel<D, 2, ONE_PAGE>), grid, block, lds, stream, a, tl); break;
-        case 4: hipLaunchKernelGGL((prefill_kernel<D, 4, ONE_PAGE>), grid, block, lds, stream, a, tl); break;
-        case 8: hipLaunchKernelGGL((prefill_kernel<D, 8, ONE_PAGE>), grid, block, lds, stream, a, tl); break;
-        case 16: hipLaunchKernelGGL((prefill_kernel<D, 16, ONE_PAGE>), grid, block, lds, stream, a, tl); break;
+        case 1: hipLaunchKernelGGL((prefill_kernel<D, 1, ONE_PAGE, UNIFIED>), grid, block, lds, stream, a, tl); break;
+        case 2: hipLaunchKernelGGL((prefill_kernel<D, 2, ONE_PAGE, UNIFIED>), grid, block, lds, stream, a, tl); break;
+        case 4: hipLaunchKernelGGL((prefill_kernel<D, 4, ONE_PAGE, UNIFIED>), grid, block, lds, stream, a, tl); break;
+        case 8: hipLaunchKernelGGL((prefill_kernel<D, 8, ONE_PAGE, UNIFIED>), grid, block, lds, stream, a, tl); break;
+        case 16: hipLaunchKernelGGL((prefill_kernel<D, 16, ONE_PAGE, UNIFIED>), grid, block, lds, stream, a, tl); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -656,8 +734,13 @@ hipError_t launch_prefill_dp(const PrefillArgs& a, const TileList& tl, int n_ite
 template <int D>
 hipError_t launch_prefill_d(const PrefillArgs& a, const TileList& tl, int n_items, size_t lds,
                             hipStream_t stream) {
-    if (a.page_size % kKvTile == 0) return launch_prefill_dp<D, true>(a, tl, n_items, lds, stream);
-    return launch_prefill_dp<D, false>(a, tl, n_items, lds, stream);
+    const bool one_page = a.page_size % kKvTile == 0;
+    if (a.unified) {
+        if (one_page) return launch_prefill_dpu<D, true, true>(a, tl, n_items, lds, stream);
+        return launch_prefill_dpu<D, false, true>(a, tl, n_items, lds, stream);
+    }
+    if (one_page) return launch_prefill_dpu<D, true, false>(a, tl, n_items, lds, stream);
+    return launch_prefill_dpu<D, false, false>(a, tl, n_items, lds, stream);
 }
 
 }  // namespace
