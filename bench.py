@@ -235,6 +235,98 @@ def bench_prefill(args, pa, torch, W):
     }
 
 
+def _time_graph(torch, fn, reps):
+    """Mean ms of fn() over `reps` calls captured in one HIP graph (one warm eager call first)."""
+    fn(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            for _ in range(reps):
+                fn(torch.cuda.current_stream())
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def bench_unified(args, pa, torch, W, dec_case):
+    """Paged path against the unified-span baseline on the same pool (the comparison
+    the pages make end to end, here per kernel): the 512-token UA ubatch (8
+    sequences, 2K-16K prefixes) and the 8 x 16384 decode batch."""
+    dev = torch.device("cuda:0")
+    out = {}
+    # UA prefill ubatch
+    c = W.ua_prefill()
+    kd, vd = torch.from_numpy(c.k_pool).to(dev), torch.from_numpy(c.v_pool).to(dev)
+    pa.pa_reshape_and_cache(kd, vd, torch.from_numpy(c.k_new).to(dev), torch.from_numpy(c.v_new).to(dev),
+                            torch.from_numpy(c.slot_mapping).to(dev))
+    lens = np.zeros(c.block_tables.shape[0], dtype=np.int64)
+    for r, kl in zip(c.token_row, c.token_kv_len):
+        lens[r] = max(lens[r], kl)
+    span, cs, cp = W.unified_view(c.block_tables, lens, c.num_pages, c.page_size)
+    q = torch.from_numpy(c.q).to(dev)
+    o = torch.empty_like(q)
+    bt, row = torch.from_numpy(c.block_tables).to(dev), torch.from_numpy(c.token_row).to(dev)
+    kvl, pos = torch.from_numpy(c.token_kv_len).to(dev), torch.from_numpy(c.token_pos).to(dev)
+    css, cps = torch.from_numpy(cs).to(dev), torch.from_numpy(cp).to(dev)
+    desc = pa.cache_desc(kd, vd)
+    wsp = torch.zeros(max(1, pa.pa_prefill_workspace_bytes(desc, c.n_q_heads, c.token_row, c.token_kv_len,
+                                                           c.token_pos)), dtype=torch.uint8, device=dev)
+    wsu = torch.zeros(max(1, pa.pa_unified_workspace_bytes(desc, len(c.token_row), c.n_q_heads, span)),
+                      dtype=torch.uint8, device=dev)
+    t_p = _time_graph(torch, lambda st: pa.pa_prefill(
+        q, kd, vd, bt, row, kvl, pos, float(c.scale), token_row_host=c.token_row,
+        token_kv_len_host=c.token_kv_len, token_pos_host=c.token_pos, out=o, workspace=wsp, stream=st), 10)
+    t_u = _time_graph(torch, lambda st: pa.pa_unified_attention(
+        q, kd, vd, span, css, cps, row, pos, float(c.scale), out=o, workspace=wsu, stream=st), 10)
+    pairs = W.prefill_pairs(c.token_kv_len, c.token_pos)
+    out["ua_prefill_512"] = {
+        "paged_us": round(t_p * 1e3, 2), "unified_us": round(t_u * 1e3, 2),
+        "unified_over_paged": round(t_u / t_p, 3),
+        "useful_pairs": pairs, "unified_pairs": W.unified_pairs(span, len(c.token_row)),
+        "span_cells": int(span), "valid_cells": int(lens.sum()),
+    }
+    del kd, vd
+    # decode batch: the 8 queries scan the whole span together
+    c = dec_case
+    kd, vd = torch.from_numpy(c.k_pool).to(dev), torch.from_numpy(c.v_pool).to(dev)
+    span, cs, cp = W.unified_view(c.block_tables, c.kv_lens, c.num_pages, c.page_size)
+    S = len(c.kv_lens)
+    q = torch.from_numpy(c.q).to(dev)
+    o = torch.empty_like(q)
+    bt, kl = torch.from_numpy(c.block_tables).to(dev), torch.from_numpy(c.kv_lens).to(dev)
+    ts = torch.arange(S, dtype=torch.int32, device=dev)
+    tp = torch.from_numpy((c.kv_lens - 1).astype(np.int32)).to(dev)
+    css, cps = torch.from_numpy(cs).to(dev), torch.from_numpy(cp).to(dev)
+    desc = pa.cache_desc(kd, vd)
+    wsd = torch.zeros(max(1, pa.pa_decode_workspace_bytes(desc, S, c.n_q_heads, c.block_tables.shape[1],
+                                                          c.kv_lens)), dtype=torch.uint8, device=dev)
+    wsu = torch.zeros(max(1, pa.pa_unified_workspace_bytes(desc, S, c.n_q_heads, span)),
+                      dtype=torch.uint8, device=dev)
+    t_p = _time_graph(torch, lambda st: pa.pa_decode(q, kd, vd, bt, kl, float(c.scale), kv_lens_host=c.kv_lens,
+                                                     out=o, workspace=wsd, stream=st), 10)
+    t_u = _time_graph(torch, lambda st: pa.pa_unified_attention(
+        q, kd, vd, span, css, cps, ts, tp, float(c.scale), out=o, workspace=wsu, stream=st), 10)
+    out["decode_" + args.decode_workload] = {
+        "paged_us": round(t_p * 1e3, 2), "unified_us": round(t_u * 1e3, 2),
+        "unified_over_paged": round(t_u / t_p, 3),
+        "paged_bytes": W.decode_valid_bytes(c.kv_lens, c.n_kv_heads, c.head_dim),
+        "unified_bytes": W.unified_decode_bytes(span, c.n_kv_heads, c.head_dim),
+        "span_cells": int(span), "valid_cells": int(np.sum(c.kv_lens)),
+    }
+    return out
+
+
 def cpu_baseline_decode(c, oracle):
     t0 = time.perf_counter()
     oracle.paged_decode(c.q, c.k_pool, c.v_pool, c.block_tables, c.kv_lens, c.scale)
@@ -277,6 +369,8 @@ def main():
     ap.add_argument("--prefill-reps", type=int, default=3)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-unified", action="store_true",
+                    help="skip the paged-vs-unified-span comparison")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device-to-device copy of this many bytes (3 times): the "
                          "known-size kernel that calibrates the FETCH_SIZE / WRITE_SIZE counters")
@@ -315,6 +409,12 @@ def main():
         log("prefill: generating 8 x 16384 chunked workload")
         cp, _, pre = bench_prefill(args, pa, torch, W)
         log(f"prefill: {pre['pass_ms']:.2f} ms/pass, {pre['tflops']:.1f} TFLOP/s")
+
+    uni = None
+    if not args.no_unified:
+        log("unified span: paged vs unified on the UA ubatch and the decode batch")
+        uni = bench_unified(args, pa, torch, W, c)
+        log(f"unified span: {json.dumps(uni)}")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -378,6 +478,8 @@ def main():
             "ubatches": pre["ubatches"],
             "reps": pre["reps"],
         }
+    if uni is not None:
+        result["unified_vs_paged"] = uni
     print(json.dumps(result), flush=True)
 
 
