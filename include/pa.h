@@ -124,6 +124,46 @@ pa_status pa_block_tables(const pa_pool* pool, const int32_t* seqs, int32_t n, i
  * into refcount_out[num_pages]. */
 pa_status pa_pool_stats(const pa_pool* pool, int32_t* n_free_out, int32_t* refcount_out);
 
+/* Preemption and compaction ([CF] 内存管理策略 and 抢占与恢复机制: a preempted
+ * sequence's blocks move to a reserved CPU area and come back without
+ * recomputation; fragmented blocks are compacted into contiguous locations).
+ *
+ * pa_pool_host_reserve: the host reserve becomes n_host_pages page slots
+ * (a stack, slot 0 handed out first).  PA_ERR_STATE while any sequence is
+ * swapped out.
+ *
+ * pa_seq_swap_out: gives every page of a resident sequence, in logical order,
+ * a host slot, writes the (device page, host slot) copies to make into
+ * pairs_out[n][2] (*n_pairs_out = n, the sequence's page count) and drops the
+ * sequence's device references (pages reaching 0 are pushed as by
+ * pa_seq_free).  The caller copies with pa_swap_blocks(to_host = 1) before
+ * those device pages are written again.  The sequence keeps its id; until
+ * pa_seq_swap_in, only pa_seq_free accepts it (others: PA_ERR_STATE).
+ * PA_ERR_NO_PAGES if the reserve has too few free slots, PA_ERR_INVALID if
+ * max_pairs < n; failures change nothing.
+ *
+ * pa_seq_swap_in: takes a device page per host slot of a swapped-out
+ * sequence, in logical order, writes the (host slot, device page) copies into
+ * pairs_out (copy with pa_swap_blocks(to_host = 0) before reading the pages)
+ * and returns the slots to the reserve.  The new pages are private
+ * (refcount 1).  PA_ERR_NO_PAGES if too few device pages are free.
+ *
+ * pa_pool_compact: with n_live pages in use, moves every live page with id >=
+ * n_live (ascending) onto the free ids below n_live (ascending), rewrites
+ * every resident sequence's table and the refcounts, and leaves the free
+ * stack n_live..N-1 with n_live handed out first.  The (src, dst) moves go to
+ * pairs_out (at most num_pages); they satisfy pa_copy_blocks' rules, which
+ * performs them on the device.
+ *
+ * pa_pool_host_stats: number of free host reserve slots. */
+pa_status pa_pool_host_reserve(pa_pool* pool, int32_t n_host_pages);
+pa_status pa_seq_swap_out(pa_pool* pool, int32_t seq, int32_t* pairs_out, int32_t max_pairs,
+                          int32_t* n_pairs_out);
+pa_status pa_seq_swap_in(pa_pool* pool, int32_t seq, int32_t* pairs_out, int32_t max_pairs,
+                         int32_t* n_pairs_out);
+pa_status pa_pool_compact(pa_pool* pool, int32_t* pairs_out, int32_t max_pairs, int32_t* n_pairs_out);
+pa_status pa_pool_host_stats(const pa_pool* pool, int32_t* n_host_free_out);
+
 /* ===================================================================== */
 /* Device operations.                                                    */
 /* ===================================================================== */
@@ -154,6 +194,23 @@ pa_status pa_reshape_and_cache(const pa_cache_desc* desc, void* k_cache, void* v
 pa_status pa_copy_blocks(const pa_cache_desc* desc, void* const* k_caches_host,
                          void* const* v_caches_host, int32_t n_layers, const int32_t* pairs_host,
                          int32_t n_pairs, pa_stream stream);
+
+/* Block swap ([CF] section 3, the block copy/swap kernel; 抢占与恢复机制): for every
+ * layer l and pair i, copy one whole page between the device pool
+ * (k_caches_host[l], v_caches_host[l]: device pointers, layout of
+ * pa_cache_desc) and a host reserve of n_host_pages pages of the same layout
+ * (k_swap_host[l], v_swap_host[l]: pinned host memory mapped for the device,
+ * e.g. from hipHostMalloc or torch's pin_memory).  to_host = 1: pairs are
+ * (device page, host slot); 0: (host slot, device page).  Validated on the
+ * host: ids in range, no destination repeated, host reserves pinned and mapped
+ * (hipHostGetDevicePointer succeeds) -- PA_ERR_INVALID otherwise.  One kernel
+ * launch per 128 pairs x 32 layers reads or writes the host pages directly;
+ * bits are copied exactly. */
+pa_status pa_swap_blocks(const pa_cache_desc* desc, void* const* k_caches_host,
+                         void* const* v_caches_host, void* const* k_swap_host,
+                         void* const* v_swap_host, int32_t n_host_pages, int32_t n_layers,
+                         const int32_t* pairs_host, int32_t n_pairs, int32_t to_host,
+                         pa_stream stream);
 
 /* Workspace bytes pa_decode needs for these arguments (0 if it needs none).
  * Same meaning of arguments as pa_decode.  A decode workspace starts with

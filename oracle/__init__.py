@@ -26,11 +26,11 @@ routines, closed forms, invariants).
 """
 from .attention import (expand_per_token, gather_logical, paged_attention, paged_decode,
                         partitioned_decode, lse_combine, unified_attention)
-from .cache_ops import reshape_and_cache, copy_blocks
+from .cache_ops import reshape_and_cache, copy_blocks, swap_blocks
 from .allocator import AllocatorModel, PoolError, NoPagesError, StateError, InvalidError
 
 __all__ = [
     "expand_per_token", "gather_logical", "paged_attention", "paged_decode",
-    "partitioned_decode", "lse_combine", "unified_attention", "reshape_and_cache", "copy_blocks",
+    "partitioned_decode", "lse_combine", "unified_attention", "reshape_and_cache", "copy_blocks", "swap_blocks",
     "AllocatorModel", "PoolError", "NoPagesError", "StateError", "InvalidError",
 ]

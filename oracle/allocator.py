@@ -22,6 +22,24 @@ open; this model fixes it so block tables are unique:
 * sequence ids are the smallest non-negative integer not in use;
 * a failing call leaves the pool unchanged.
 
+Preemption and compaction (page "CacheFlow：基于 llama.cpp 的多请求 LLM 推理优化
+引擎", sections 内存管理策略 and 抢占与恢复机制: a preempted sequence's blocks go to a
+reserved CPU area and come back without recomputation; fragmented blocks are
+moved into contiguous physical locations).  The pages fix neither the slot
+choice nor the move order; this model fixes them:
+
+* the host reserve is ``n_host`` page slots kept as a second stack (slot 0 on
+  top); swap-out gives each page of the sequence, in logical order, a host
+  slot and drops the sequence's reference on the device page (pages whose
+  count reaches 0 are pushed like ``seq_free`` does); swap-in takes a device
+  page per host slot, in logical order, and pushes the host slots back in
+  logical order.  A swapped-out sequence keeps its id; only ``seq_free`` and
+  ``seq_swap_in`` accept it;
+* compaction with ``n_live`` pages in use moves every live page whose id is
+  >= ``n_live`` (ascending) onto the free ids below ``n_live`` (ascending),
+  carries refcounts and table entries along, and rebuilds the free stack as
+  ``n_live .. N-1`` with ``n_live`` on top.
+
 Pinned by invariants (page conservation, sharing only under refcount > 1,
 free-all restores every page, page counts with and without sharing) in
 tests/test_oracle.py.
@@ -62,6 +80,9 @@ class AllocatorModel:
         self.ref = [0] * num_pages
         self.pages: Dict[int, List[int]] = {}
         self.length: Dict[int, int] = {}
+        self.host: Dict[int, List[int]] = {}         # swapped-out sequences' host slots
+        self.host_free: List[int] = []
+        self.n_host = 0
 
     # -- helpers
     def _pop(self) -> int:
@@ -69,12 +90,12 @@ class AllocatorModel:
 
     def _alive(self, seq: int):
         if seq not in self.pages:
-            raise StateError(f"sequence {seq} is not live")
+            raise StateError(f"sequence {seq} is not live (or is swapped out)")
 
     # -- API mirror
     def seq_new(self) -> int:
         sid = 0
-        while sid in self.pages:
+        while sid in self.pages or sid in self.host:
             sid += 1
         self.pages[sid] = []
         self.length[sid] = 0
@@ -138,6 +159,12 @@ class AllocatorModel:
         return src, dst
 
     def seq_free(self, seq: int) -> None:
+        if seq in self.host:
+            for h in self.host[seq]:
+                self.host_free.append(h)
+            del self.host[seq]
+            del self.length[seq]
+            return
         self._alive(seq)
         for p in self.pages[seq]:
             self.ref[p] -= 1
@@ -160,3 +187,72 @@ class AllocatorModel:
 
     def stats(self):
         return len(self.free), np.asarray(self.ref, dtype=np.int32)
+
+    # -- preemption: swap to / from the host reserve
+    def host_reserve(self, n_host: int) -> None:
+        if n_host < 0:
+            raise InvalidError("n_host < 0")
+        if self.host:
+            raise StateError("sequences are swapped out")
+        self.n_host = n_host
+        self.host_free = list(range(n_host))[::-1]   # slot 0 on top
+
+    def seq_swap_out(self, seq: int) -> List[Tuple[int, int]]:
+        """Returns the (device page, host slot) copies to make, in logical order."""
+        self._alive(seq)
+        pages = self.pages[seq]
+        if len(pages) > len(self.host_free):
+            raise NoPagesError("host reserve exhausted")
+        pairs = []
+        slots = []
+        for p in pages:
+            h = self.host_free.pop()
+            pairs.append((p, h))
+            slots.append(h)
+        for p in pages:
+            self.ref[p] -= 1
+            if self.ref[p] == 0:
+                self.free.append(p)
+        del self.pages[seq]
+        self.host[seq] = slots
+        return pairs
+
+    def seq_swap_in(self, seq: int) -> List[Tuple[int, int]]:
+        """Returns the (host slot, device page) copies to make, in logical order."""
+        if seq not in self.host:
+            raise StateError("sequence is not swapped out")
+        slots = self.host[seq]
+        if len(slots) > len(self.free):
+            raise NoPagesError("pool exhausted")
+        pairs = []
+        pages = []
+        for h in slots:
+            p = self._pop()
+            self.ref[p] = 1
+            pairs.append((h, p))
+            pages.append(p)
+        for h in slots:
+            self.host_free.append(h)
+        del self.host[seq]
+        self.pages[seq] = pages
+        return pairs
+
+    # -- compaction
+    def compact(self) -> List[Tuple[int, int]]:
+        """Moves live pages into ids 0..n_live-1; returns the (src, dst) copies."""
+        n_live = sum(1 for r in self.ref if r > 0)
+        movers = [p for p in range(n_live, self.num_pages) if self.ref[p] > 0]
+        holes = [p for p in range(n_live) if self.ref[p] == 0]
+        assert len(movers) == len(holes)
+        dest = dict(zip(movers, holes))
+        for s in self.pages:
+            self.pages[s] = [dest.get(p, p) for p in self.pages[s]]
+        for src, dst in dest.items():
+            self.ref[dst] = self.ref[src]
+            self.ref[src] = 0
+        self.free = list(range(n_live, self.num_pages))[::-1]
+        return list(zip(movers, holes))
+
+    def stats_host(self):
+        return len(self.host_free)
+

@@ -57,3 +57,22 @@ def copy_blocks(k_pools, v_pools, pairs):
             ks[layer][d] = k_pools[layer][s]
             vs[layer][d] = v_pools[layer][s]
     return ks, vs
+
+
+def swap_blocks(src_k, src_v, dst_k, dst_v, pairs):
+    """Copy whole pages from one pool pair to another of the same page layout
+    (page "CacheFlow：基于 llama.cpp 的多请求 LLM 推理优化引擎", section 3, the block
+    swap between GPU and CPU memory): ``dst[d] = src[s]`` for every (s, d) pair
+    and every layer.  ``src_*``/``dst_*`` are lists (one pool per layer);
+    returns new destination lists.  A destination may appear once, so the
+    result does not depend on the order of the pairs."""
+    pairs = np.asarray(pairs, dtype=np.int64).reshape(-1, 2)
+    if np.unique(pairs[:, 1]).shape[0] != pairs.shape[0]:
+        raise ValueError("swap_blocks: a destination repeats")
+    ks = [np.array(k, copy=True) for k in dst_k]
+    vs = [np.array(v, copy=True) for v in dst_v]
+    for layer in range(len(ks)):
+        for s, d in pairs:
+            ks[layer][d] = src_k[layer][s]
+            vs[layer][d] = src_v[layer][s]
+    return ks, vs

@@ -23,7 +23,7 @@ from ._lib import CacheDesc
 __all__ = [
     "PaError", "InvalidError", "UnsupportedError", "NoPagesError", "StateError", "HipError",
     "WorkspaceError", "CacheDesc", "cache_desc", "pa_version", "pa_last_error", "Pool",
-    "pa_reshape_and_cache", "pa_copy_blocks", "pa_decode_workspace_bytes", "pa_decode",
+    "pa_reshape_and_cache", "pa_copy_blocks", "pa_swap_blocks", "pa_decode_workspace_bytes", "pa_decode",
     "pa_prefill_workspace_bytes", "pa_prefill", "pa_unified_workspace_bytes",
     "pa_unified_attention", "library_path",
 ]
@@ -186,6 +186,33 @@ class Pool:
         _check(_L().pa_block_tables(self._h, _i32p(s), len(s), int(max_pages), _i32p(bt), _i32p(kv)))
         return bt, kv
 
+    def host_reserve(self, n_host_pages: int) -> None:
+        _check(_L().pa_pool_host_reserve(self._h, int(n_host_pages)))
+
+    def _pairs_call(self, fn, *args):
+        cap = self.num_pages
+        pairs = np.zeros((cap, 2), dtype=np.int32)
+        n = ctypes.c_int32(0)
+        _check(fn(self._h, *args, _i32p(pairs), cap, ctypes.byref(n)))
+        return pairs[:n.value].copy()
+
+    def seq_swap_out(self, seq: int) -> np.ndarray:
+        """(device page, host slot) copies, in logical order; see pa_seq_swap_out."""
+        return self._pairs_call(_L().pa_seq_swap_out, int(seq))
+
+    def seq_swap_in(self, seq: int) -> np.ndarray:
+        """(host slot, device page) copies, in logical order; see pa_seq_swap_in."""
+        return self._pairs_call(_L().pa_seq_swap_in, int(seq))
+
+    def compact(self) -> np.ndarray:
+        """(src, dst) page moves for pa_copy_blocks; see pa_pool_compact."""
+        return self._pairs_call(_L().pa_pool_compact)
+
+    def host_free(self) -> int:
+        n = ctypes.c_int32(0)
+        _check(_L().pa_pool_host_stats(self._h, ctypes.byref(n)))
+        return n.value
+
     def stats(self):
         n = ctypes.c_int32()
         ref = np.empty(self.num_pages, dtype=np.int32)
@@ -230,6 +257,31 @@ def pa_copy_blocks(k_caches, v_caches, pairs, stream=None) -> None:
     kp = (ctypes.c_void_p * n_layers)(*[k.data_ptr() for k in k_caches])
     vp = (ctypes.c_void_p * n_layers)(*[v.data_ptr() for v in v_caches])
     _check(_L().pa_copy_blocks(ctypes.byref(desc), kp, vp, n_layers, _i32p(p), p.shape[0],
+                               _stream_ptr(stream)))
+
+
+def pa_swap_blocks(k_caches, v_caches, k_host, v_host, pairs, to_host: bool, stream=None) -> None:
+    """Copy whole pages between device caches and pinned host reserves of the same
+    layout, per layer (pairs: host [n][2]; to_host: (device page, host slot),
+    else (host slot, device page))."""
+    import torch
+    if not (len(k_caches) == len(v_caches) == len(k_host) == len(v_host)) or not k_caches:
+        raise ValueError("need the same non-zero number of device and host K/V caches")
+    desc = cache_desc(k_caches[0], v_caches[0])
+    n_host = int(k_host[0].shape[0])
+    for k, v, kh, vh in zip(k_caches, v_caches, k_host, v_host):
+        _dev(k, torch.float16, "k_cache", 4)
+        _dev(v, torch.float16, "v_cache", 4)
+        for h, d in ((kh, k), (vh, v)):
+            if not h.is_pinned() or h.dtype != torch.float16 or tuple(h.shape[1:]) != tuple(d.shape[1:]) \
+                    or int(h.shape[0]) != n_host or not h.is_contiguous():
+                raise ValueError("host reserves must be contiguous pinned float16 tensors of the cache's "
+                                 "page layout")
+    p = _host_i32(pairs).reshape(-1, 2)
+    n_layers = len(k_caches)
+    arr = lambda ts: (ctypes.c_void_p * n_layers)(*[t.data_ptr() for t in ts])   # noqa: E731
+    _check(_L().pa_swap_blocks(ctypes.byref(desc), arr(k_caches), arr(v_caches), arr(k_host), arr(v_host),
+                               n_host, n_layers, _i32p(p), p.shape[0], 1 if to_host else 0,
                                _stream_ptr(stream)))
 
 

@@ -37,10 +37,18 @@ SIGNATURES = {
     "pa_seq_free": (c_i32, [c_void_p, c_i32]),
     "pa_block_tables": (c_i32, [c_void_p, c_i32_p, c_i32, c_i32, c_i32_p, c_i32_p]),
     "pa_pool_stats": (c_i32, [c_void_p, c_i32_p, c_i32_p]),
+    "pa_pool_host_reserve": (c_i32, [c_void_p, c_i32]),
+    "pa_seq_swap_out": (c_i32, [c_void_p, c_i32, c_i32_p, c_i32, c_i32_p]),
+    "pa_seq_swap_in": (c_i32, [c_void_p, c_i32, c_i32_p, c_i32, c_i32_p]),
+    "pa_pool_compact": (c_i32, [c_void_p, c_i32_p, c_i32, c_i32_p]),
+    "pa_pool_host_stats": (c_i32, [c_void_p, c_i32_p]),
     "pa_reshape_and_cache": (c_i32, [CacheDesc_p, c_void_p, c_void_p, c_void_p, c_void_p, c_i32,
                                      c_void_p, c_i32, c_void_p]),
     "pa_copy_blocks": (c_i32, [CacheDesc_p, ctypes.POINTER(c_void_p), ctypes.POINTER(c_void_p),
                                c_i32, c_i32_p, c_i32, c_void_p]),
+    "pa_swap_blocks": (c_i32, [CacheDesc_p, ctypes.POINTER(c_void_p), ctypes.POINTER(c_void_p),
+                               ctypes.POINTER(c_void_p), ctypes.POINTER(c_void_p), c_i32, c_i32,
+                               c_i32_p, c_i32, c_i32, c_void_p]),
     "pa_decode_workspace_bytes": (c_size_t, [CacheDesc_p, c_i32, c_i32, c_i32, c_i32_p, c_i32]),
     "pa_decode": (c_i32, [CacheDesc_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                           c_i32_p, c_i32, c_i32, c_i32, c_float, c_i32, c_void_p, c_size_t,

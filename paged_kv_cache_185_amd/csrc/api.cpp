@@ -361,6 +361,51 @@ pa_status pa_copy_blocks(const pa_cache_desc* desc, void* const* k_caches_host,
     return e == hipSuccess ? PA_OK : hip_fail("pa_copy_blocks", e);
 }
 
+pa_status pa_swap_blocks(const pa_cache_desc* desc, void* const* k_caches_host,
+                         void* const* v_caches_host, void* const* k_swap_host,
+                         void* const* v_swap_host, int32_t n_host_pages, int32_t n_layers,
+                         const int32_t* pairs_host, int32_t n_pairs, int32_t to_host,
+                         pa_stream stream) {
+    pa_status st = check_desc("pa_swap_blocks", desc);
+    if (st != PA_OK) return st;
+    if (n_layers < 0 || n_pairs < 0 || n_host_pages < 0)
+        return fail(PA_ERR_INVALID, "pa_swap_blocks: negative count");
+    if (to_host != 0 && to_host != 1) return fail(PA_ERR_INVALID, "pa_swap_blocks: to_host must be 0 or 1");
+    if (n_layers == 0 || n_pairs == 0) return PA_OK;
+    if (!k_caches_host || !v_caches_host || !k_swap_host || !v_swap_host || !pairs_host)
+        return fail(PA_ERR_INVALID, "pa_swap_blocks: null pointer");
+    for (int32_t l = 0; l < n_layers; ++l)
+        if (!k_caches_host[l] || !v_caches_host[l] || !k_swap_host[l] || !v_swap_host[l])
+            return fail(PA_ERR_INVALID, "pa_swap_blocks: null cache pointer");
+    const int32_t n_src = to_host ? desc->num_pages : n_host_pages;
+    const int32_t n_dst = to_host ? n_host_pages : desc->num_pages;
+    std::vector<char> is_dst(n_dst, 0);
+    for (int32_t i = 0; i < n_pairs; ++i) {
+        const int32_t s = pairs_host[2 * i], dpg = pairs_host[2 * i + 1];
+        if (s < 0 || s >= n_src || dpg < 0 || dpg >= n_dst)
+            return fail(PA_ERR_INVALID, "pa_swap_blocks: page or slot id out of range");
+        if (is_dst[dpg]) return fail(PA_ERR_INVALID, "pa_swap_blocks: a destination repeats");
+        is_dst[dpg] = 1;
+    }
+    const int64_t page_bytes =
+        (int64_t)desc->n_kv_heads * desc->page_size * desc->head_dim * 2;
+    // the kernel reaches the host reserve through its device mapping; memory
+    // that is not pinned and mapped is rejected here, never dereferenced
+    std::vector<void*> kh(n_layers), vh(n_layers);
+    for (int32_t l = 0; l < n_layers; ++l) {
+        if (hipHostGetDevicePointer(&kh[l], k_swap_host[l], 0) != hipSuccess ||
+            hipHostGetDevicePointer(&vh[l], v_swap_host[l], 0) != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(PA_ERR_INVALID, "pa_swap_blocks: host reserve is not pinned, mapped memory");
+        }
+    }
+    hipError_t e = to_host ? launch_copy_pages(k_caches_host, kh.data(), v_caches_host, vh.data(),
+                                               n_layers, pairs_host, n_pairs, page_bytes, (hipStream_t)stream)
+                           : launch_copy_pages(kh.data(), k_caches_host, vh.data(), v_caches_host,
+                                               n_layers, pairs_host, n_pairs, page_bytes, (hipStream_t)stream);
+    return e == hipSuccess ? PA_OK : hip_fail("pa_swap_blocks", e);
+}
+
 size_t pa_decode_workspace_bytes(const pa_cache_desc* desc, int32_t n_seqs, int32_t n_q_heads,
                                  int32_t max_pages, const int32_t* kv_lens_host,
                                  int32_t partition_tokens) {

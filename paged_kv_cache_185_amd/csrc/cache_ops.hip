@@ -107,21 +107,28 @@ __global__ __launch_bounds__(kRcThreads) void reshape_and_cache_kernel(
     }
 }
 
-struct CopyBlocksArgs {
-    uint16_t* k[kMaxCopyLayers];
-    uint16_t* v[kMaxCopyLayers];
+// Page copies between two page arrays of the same layout (src and dst base per
+// layer for K and V): the same array for copy-on-write, the device pool and a
+// pinned host reserve for swap.
+struct CopyPagesArgs {
+    const uint16_t* src_k[kMaxCopyLayers];
+    uint16_t* dst_k[kMaxCopyLayers];
+    const uint16_t* src_v[kMaxCopyLayers];
+    uint16_t* dst_v[kMaxCopyLayers];
     int32_t pairs[2 * kMaxCopyPairs];
 };
 
 constexpr int kCopyBytesPerBlock = 16384;
 
 // grid: (ceil(page_bytes / 16 KiB), n_pairs, 2 * n_layers); 16-byte vector copies.
-__global__ __launch_bounds__(256) void copy_blocks_kernel(CopyBlocksArgs args, int64_t page_bytes) {
+__global__ __launch_bounds__(256) void copy_pages_kernel(CopyPagesArgs args, int64_t page_bytes) {
     const int pair = blockIdx.y;
     const int layer = blockIdx.z >> 1;
-    uint16_t* base = (blockIdx.z & 1) ? args.v[layer] : args.k[layer];
-    const char* src = reinterpret_cast<const char*>(base) + (int64_t)args.pairs[2 * pair] * page_bytes;
-    char* dst = reinterpret_cast<char*>(base) + (int64_t)args.pairs[2 * pair + 1] * page_bytes;
+    const bool is_v = blockIdx.z & 1;
+    const char* src = reinterpret_cast<const char*>(is_v ? args.src_v[layer] : args.src_k[layer]) +
+                      (int64_t)args.pairs[2 * pair] * page_bytes;
+    char* dst = reinterpret_cast<char*>(is_v ? args.dst_v[layer] : args.dst_k[layer]) +
+                (int64_t)args.pairs[2 * pair + 1] * page_bytes;
     const int64_t begin = (int64_t)blockIdx.x * kCopyBytesPerBlock;
     const int64_t end = begin + kCopyBytesPerBlock < page_bytes ? begin + kCopyBytesPerBlock : page_bytes;
     for (int64_t off = begin + (int64_t)threadIdx.x * 16; off < end; off += 256 * 16)
@@ -167,27 +174,36 @@ hipError_t launch_reshape_and_cache(void* k_cache, void* v_cache, const void* k_
     return hipGetLastError();
 }
 
-hipError_t launch_copy_blocks(void* const* k_caches, void* const* v_caches, int32_t n_layers,
-                              const int32_t* pairs, int32_t n_pairs, int64_t page_bytes,
-                              hipStream_t stream) {
+hipError_t launch_copy_pages(void* const* src_k, void* const* dst_k, void* const* src_v,
+                             void* const* dst_v, int32_t n_layers, const int32_t* pairs, int32_t n_pairs,
+                             int64_t page_bytes, hipStream_t stream) {
     for (int32_t l0 = 0; l0 < n_layers; l0 += kMaxCopyLayers) {
         const int32_t nl = n_layers - l0 < kMaxCopyLayers ? n_layers - l0 : kMaxCopyLayers;
         for (int32_t p0 = 0; p0 < n_pairs; p0 += kMaxCopyPairs) {
             const int32_t np = n_pairs - p0 < kMaxCopyPairs ? n_pairs - p0 : kMaxCopyPairs;
-            CopyBlocksArgs args{};
+            CopyPagesArgs args{};
             for (int32_t l = 0; l < nl; ++l) {
-                args.k[l] = (uint16_t*)k_caches[l0 + l];
-                args.v[l] = (uint16_t*)v_caches[l0 + l];
+                args.src_k[l] = (const uint16_t*)src_k[l0 + l];
+                args.dst_k[l] = (uint16_t*)dst_k[l0 + l];
+                args.src_v[l] = (const uint16_t*)src_v[l0 + l];
+                args.dst_v[l] = (uint16_t*)dst_v[l0 + l];
             }
             for (int32_t i = 0; i < 2 * np; ++i) args.pairs[i] = pairs[2 * p0 + i];
             const dim3 grid((unsigned)((page_bytes + kCopyBytesPerBlock - 1) / kCopyBytesPerBlock),
                             (unsigned)np, (unsigned)(2 * nl));
-            hipLaunchKernelGGL(copy_blocks_kernel, grid, dim3(256), 0, stream, args, page_bytes);
+            hipLaunchKernelGGL(copy_pages_kernel, grid, dim3(256), 0, stream, args, page_bytes);
             hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
     }
     return hipSuccess;
+}
+
+hipError_t launch_copy_blocks(void* const* k_caches, void* const* v_caches, int32_t n_layers,
+                              const int32_t* pairs, int32_t n_pairs, int64_t page_bytes,
+                              hipStream_t stream) {
+    return launch_copy_pages(k_caches, k_caches, v_caches, v_caches, n_layers, pairs, n_pairs,
+                             page_bytes, stream);
 }
 
 hipError_t launch_zero_rows(float* out, const int32_t* token_row, int32_t n_tokens,

@@ -17,6 +17,10 @@ hipError_t launch_reshape_and_cache(void* k_cache, void* v_cache, const void* k_
 // Copies up to kMaxCopyPairs pairs for up to kMaxCopyLayers layers per launch.
 constexpr int kMaxCopyPairs = 128;
 constexpr int kMaxCopyLayers = 32;
+// Page copies from src to dst page arrays of one layout (pairs: src page, dst page).
+hipError_t launch_copy_pages(void* const* src_k, void* const* dst_k, void* const* src_v,
+                             void* const* dst_v, int32_t n_layers, const int32_t* pairs, int32_t n_pairs,
+                             int64_t page_bytes, hipStream_t stream);
 hipError_t launch_copy_blocks(void* const* k_caches, void* const* v_caches, int32_t n_layers,
                               const int32_t* pairs, int32_t n_pairs, int64_t page_bytes,
                               hipStream_t stream);

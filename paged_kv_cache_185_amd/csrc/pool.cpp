@@ -12,6 +12,14 @@
 // a stack of free pages seeded so that free_order[0] is handed out first; freed
 // pages are pushed in logical order; ids are the smallest unused; every call
 // checks all its preconditions before changing anything.
+//
+// Preemption and compaction ("CacheFlow", sections 内存管理策略 and 抢占与恢复机制:
+// blocks of a preempted sequence go to a reserved CPU area and return without
+// recomputation; fragmented blocks are compacted into contiguous locations):
+// the host reserve is a second stack of page slots (slot 0 on top); swap-out
+// and swap-in walk the sequence's pages in logical order; compaction moves the
+// live pages with ids >= n_live (ascending) onto the free ids below n_live
+// (ascending) and leaves the free stack n_live..N-1 with n_live on top.
 #include <algorithm>
 #include <cstring>
 #include <new>
@@ -29,10 +37,14 @@ struct pa_pool {
     int32_t page_size = 0;
     std::vector<int32_t> free_stack;   // back() is the top
     std::vector<int32_t> ref;
+    std::vector<int32_t> host_free;    // host reserve slots, back() is the top
+    int32_t n_host = 0;
+    int32_t n_swapped = 0;
     struct Seq {
-        bool live = false;
+        bool live = false;      // id in use
+        bool swapped = false;   // pages are in the host reserve
         int64_t len = 0;
-        std::vector<int32_t> pages;
+        std::vector<int32_t> pages;   // device pages, or host slots while swapped
     };
     std::vector<Seq> seqs;
 
@@ -41,9 +53,11 @@ struct pa_pool {
         free_stack.pop_back();
         return p;
     }
-    bool live(int32_t s) const {
+    bool in_use(int32_t s) const {
         return s >= 0 && s < (int32_t)seqs.size() && seqs[s].live;
     }
+    // live and resident on the device
+    bool live(int32_t s) const { return in_use(s) && !seqs[s].swapped; }
     int32_t new_id() {
         for (size_t i = 0; i < seqs.size(); ++i)
             if (!seqs[i].live) return (int32_t)i;
@@ -96,6 +110,7 @@ pa_status pa_seq_new(pa_pool* pool, int32_t* seq_out) {
     if (!pool || !seq_out) return fail(PA_ERR_INVALID, "pa_seq_new: null argument");
     int32_t id = pool->new_id();
     pool->seqs[id].live = true;
+    pool->seqs[id].swapped = false;
     pool->seqs[id].len = 0;
     pool->seqs[id].pages.clear();
     *seq_out = id;
@@ -150,6 +165,7 @@ pa_status pa_seq_fork(pa_pool* pool, int32_t src_seq, int32_t* dst_seq_out) {
     auto& d = pool->seqs[id];
     const auto& s = pool->seqs[src_seq];
     d.live = true;
+    d.swapped = false;
     d.len = s.len;
     d.pages = s.pages;
     for (int32_t p : d.pages) pool->ref[p] += 1;
@@ -177,11 +193,17 @@ pa_status pa_seq_cow(pa_pool* pool, int32_t seq, int32_t logical_page, int32_t p
 
 pa_status pa_seq_free(pa_pool* pool, int32_t seq) {
     if (!pool) return fail(PA_ERR_INVALID, "pa_seq_free: pool is null");
-    if (!pool->live(seq)) return fail(PA_ERR_STATE, "pa_seq_free: sequence is not live");
+    if (!pool->in_use(seq)) return fail(PA_ERR_STATE, "pa_seq_free: sequence is not live");
     auto& s = pool->seqs[seq];
-    for (int32_t p : s.pages) {
-        if (--pool->ref[p] == 0) pool->free_stack.push_back(p);
+    if (s.swapped) {
+        for (int32_t h : s.pages) pool->host_free.push_back(h);
+        pool->n_swapped -= 1;
+    } else {
+        for (int32_t p : s.pages) {
+            if (--pool->ref[p] == 0) pool->free_stack.push_back(p);
+        }
     }
+    s.swapped = false;
     s.pages.clear();
     s.len = 0;
     s.live = false;
@@ -213,6 +235,107 @@ pa_status pa_pool_stats(const pa_pool* pool, int32_t* n_free_out, int32_t* refco
     if (!pool || !n_free_out) return fail(PA_ERR_INVALID, "pa_pool_stats: null argument");
     *n_free_out = (int32_t)pool->free_stack.size();
     if (refcount_out) std::copy(pool->ref.begin(), pool->ref.end(), refcount_out);
+    return PA_OK;
+}
+
+pa_status pa_pool_host_reserve(pa_pool* pool, int32_t n_host_pages) {
+    if (!pool || n_host_pages < 0) return fail(PA_ERR_INVALID, "pa_pool_host_reserve: bad argument");
+    if (pool->n_swapped > 0)
+        return fail(PA_ERR_STATE, "pa_pool_host_reserve: sequences are swapped out");
+    pool->n_host = n_host_pages;
+    pool->host_free.resize(n_host_pages);
+    for (int32_t i = 0; i < n_host_pages; ++i) pool->host_free[i] = n_host_pages - 1 - i;
+    return PA_OK;
+}
+
+pa_status pa_seq_swap_out(pa_pool* pool, int32_t seq, int32_t* pairs_out, int32_t max_pairs,
+                          int32_t* n_pairs_out) {
+    if (!pool || !n_pairs_out) return fail(PA_ERR_INVALID, "pa_seq_swap_out: null argument");
+    if (!pool->live(seq)) return fail(PA_ERR_STATE, "pa_seq_swap_out: sequence is not resident");
+    auto& s = pool->seqs[seq];
+    const int32_t n = (int32_t)s.pages.size();
+    if (n > max_pairs || (n > 0 && !pairs_out))
+        return fail(PA_ERR_INVALID, "pa_seq_swap_out: pairs_out too small");
+    if (n > (int32_t)pool->host_free.size())
+        return fail(PA_ERR_NO_PAGES, "pa_seq_swap_out: host reserve exhausted");
+    std::vector<int32_t> slots(n);
+    for (int32_t j = 0; j < n; ++j) {
+        slots[j] = pool->host_free.back();
+        pool->host_free.pop_back();
+        pairs_out[2 * j] = s.pages[j];
+        pairs_out[2 * j + 1] = slots[j];
+    }
+    for (int32_t p : s.pages) {
+        if (--pool->ref[p] == 0) pool->free_stack.push_back(p);
+    }
+    s.pages = std::move(slots);
+    s.swapped = true;
+    pool->n_swapped += 1;
+    *n_pairs_out = n;
+    return PA_OK;
+}
+
+pa_status pa_seq_swap_in(pa_pool* pool, int32_t seq, int32_t* pairs_out, int32_t max_pairs,
+                         int32_t* n_pairs_out) {
+    if (!pool || !n_pairs_out) return fail(PA_ERR_INVALID, "pa_seq_swap_in: null argument");
+    if (!pool->in_use(seq) || !pool->seqs[seq].swapped)
+        return fail(PA_ERR_STATE, "pa_seq_swap_in: sequence is not swapped out");
+    auto& s = pool->seqs[seq];
+    const int32_t n = (int32_t)s.pages.size();
+    if (n > max_pairs || (n > 0 && !pairs_out))
+        return fail(PA_ERR_INVALID, "pa_seq_swap_in: pairs_out too small");
+    if (n > (int32_t)pool->free_stack.size())
+        return fail(PA_ERR_NO_PAGES, "pa_seq_swap_in: page pool exhausted");
+    std::vector<int32_t> pages(n);
+    for (int32_t j = 0; j < n; ++j) {
+        pages[j] = pool->pop();
+        pool->ref[pages[j]] = 1;
+        pairs_out[2 * j] = s.pages[j];
+        pairs_out[2 * j + 1] = pages[j];
+    }
+    for (int32_t h : s.pages) pool->host_free.push_back(h);
+    s.pages = std::move(pages);
+    s.swapped = false;
+    pool->n_swapped -= 1;
+    *n_pairs_out = n;
+    return PA_OK;
+}
+
+pa_status pa_pool_compact(pa_pool* pool, int32_t* pairs_out, int32_t max_pairs, int32_t* n_pairs_out) {
+    if (!pool || !n_pairs_out) return fail(PA_ERR_INVALID, "pa_pool_compact: null argument");
+    int32_t n_live = 0;
+    for (int32_t r : pool->ref) n_live += r > 0;
+    std::vector<int32_t> movers, holes;
+    for (int32_t p = n_live; p < pool->num_pages; ++p)
+        if (pool->ref[p] > 0) movers.push_back(p);
+    for (int32_t p = 0; p < n_live; ++p)
+        if (pool->ref[p] == 0) holes.push_back(p);
+    const int32_t n = (int32_t)movers.size();
+    if (n > max_pairs || (n > 0 && !pairs_out))
+        return fail(PA_ERR_INVALID, "pa_pool_compact: pairs_out too small");
+    std::vector<int32_t> dest(pool->num_pages);
+    for (int32_t p = 0; p < pool->num_pages; ++p) dest[p] = p;
+    for (int32_t i = 0; i < n; ++i) {
+        dest[movers[i]] = holes[i];
+        pairs_out[2 * i] = movers[i];
+        pairs_out[2 * i + 1] = holes[i];
+    }
+    for (auto& s : pool->seqs)
+        if (s.live && !s.swapped)
+            for (int32_t& p : s.pages) p = dest[p];
+    for (int32_t i = 0; i < n; ++i) {
+        pool->ref[holes[i]] = pool->ref[movers[i]];
+        pool->ref[movers[i]] = 0;
+    }
+    pool->free_stack.clear();
+    for (int32_t p = pool->num_pages - 1; p >= n_live; --p) pool->free_stack.push_back(p);
+    *n_pairs_out = n;
+    return PA_OK;
+}
+
+pa_status pa_pool_host_stats(const pa_pool* pool, int32_t* n_host_free_out) {
+    if (!pool || !n_host_free_out) return fail(PA_ERR_INVALID, "pa_pool_host_stats: null argument");
+    *n_host_free_out = (int32_t)pool->host_free.size();
     return PA_OK;
 }
 

@@ -81,8 +81,11 @@ def test_pool_matches_model_bit_for_bit(seed):
     model = oracle.AllocatorModel(N, P, order)
     lib = pa.Pool(N, P, order)
     live = []
+    swapped = []
+    model.host_reserve(24)
+    lib.host_reserve(24)
     for _ in range(600):
-        op = int(rng.integers(0, 6))
+        op = int(rng.integers(0, 9))
         if op == 0 or not live:
             a, b = _both(model.seq_new, lib.seq_new)
             assert a == b
@@ -107,11 +110,31 @@ def test_pool_matches_model_bit_for_bit(seed):
         elif op == 4:
             s = live.pop(int(rng.integers(len(live))))
             _both(lambda: model.seq_free(s), lambda: lib.seq_free(s))
-        else:
-            s = int(rng.integers(0, 10))   # may be dead: both must reject alike
+        elif op == 5:
+            s = int(rng.integers(0, 10))   # may be dead or swapped: both must agree
             _both(lambda: model.seq_free(s), lambda: lib.seq_free(s))
             if s in live:
                 live.remove(s)
+            if s in swapped:
+                swapped.remove(s)
+        elif op == 6:
+            s = live[int(rng.integers(len(live)))]
+            a, b = _both(lambda: model.seq_swap_out(s), lambda: lib.seq_swap_out(s))
+            if a is not None:
+                assert np.array_equal(np.asarray(a, dtype=np.int32).reshape(-1, 2), b)
+                live.remove(s)
+                swapped.append(s)
+        elif op == 7 and swapped:
+            s = swapped[int(rng.integers(len(swapped)))]
+            a, b = _both(lambda: model.seq_swap_in(s), lambda: lib.seq_swap_in(s))
+            if a is not None:
+                assert np.array_equal(np.asarray(a, dtype=np.int32).reshape(-1, 2), b)
+                swapped.remove(s)
+                live.append(s)
+        elif op == 8:
+            a, b = _both(model.compact, lib.compact)
+            assert np.array_equal(np.asarray(a, dtype=np.int32).reshape(-1, 2), b)
+        assert model.stats_host() == lib.host_free()
         nm, rm = model.stats()
         nl, rl = lib.stats()
         assert nm == nl and np.array_equal(rm, rl)

@@ -552,3 +552,131 @@ def test_unified_page_order_and_poison_invariance():
     v3[np.isnan(v3)] = rng.standard_normal(int(np.isnan(v3).sum())).astype(np.float16)
     out3 = oracle.unified_attention(c.q, k3, v3, span, cs, cp, np.arange(S), c.kv_lens - 1, c.scale)
     np.testing.assert_array_equal(out3, out)
+
+
+# ---------------------------------------------------------------- swap / compaction
+
+class _Content:
+    """Simulated page contents: device page -> label, host slot -> label, moved by
+    the model's copy lists exactly as the device kernels move bytes."""
+
+    def __init__(self, m):
+        self.dev = {}
+        self.host = {}
+        self.m = m
+
+    def write(self, seq):
+        for j, p in enumerate(self.m.pages[seq]):
+            self.dev[p] = (seq, j)
+
+    def logical(self, seq):
+        return [self.dev.get(p) for p in self.m.pages[seq]]
+
+    def to_host(self, pairs):
+        for p, h in pairs:
+            self.host[h] = self.dev[p]
+
+    def to_dev(self, pairs):
+        for h, p in pairs:
+            self.dev[p] = self.host[h]
+
+    def copy(self, pairs):
+        snap = dict(self.dev)
+        for s, d in pairs:
+            self.dev[d] = snap[s]
+
+
+def test_swap_out_in_round_trip_and_conservation():
+    m = oracle.AllocatorModel(24, 4, np.random.default_rng(3).permutation(24))
+    m.host_reserve(10)
+    C = _Content(m)
+    a, b = m.seq_new(), m.seq_new()
+    m.seq_append(a, 17)
+    m.seq_append(b, 9)
+    C.write(a)
+    C.write(b)
+    before = C.logical(a)
+    pairs = m.seq_swap_out(a)
+    assert [h for _, h in pairs] == m.host[a] == [0, 1, 2, 3, 4]
+    C.to_host(pairs)
+    assert m.stats_host() == 10 - 5 and len(m.free) == 24 - 3
+    with pytest.raises(oracle.StateError):
+        m.seq_append(a, 1)
+    with pytest.raises(oracle.StateError):
+        m.seq_fork(a)
+    with pytest.raises(oracle.StateError):
+        m.block_tables([a], 8)
+    c = m.seq_new()                      # reuses the freed device pages
+    assert c not in (a, b)
+    m.seq_append(c, 20)
+    C.write(c)
+    back = m.seq_swap_in(a)
+    C.to_dev(back)
+    assert C.logical(a) == before
+    assert m.stats_host() == 10
+    used = set(p for s in m.pages for p in m.pages[s])
+    assert len(used) + len(m.free) == 24 and not (used & set(m.free))
+
+
+def test_swap_failures_are_atomic():
+    m = oracle.AllocatorModel(8, 4)
+    m.host_reserve(2)
+    a = m.seq_new()
+    m.seq_append(a, 12)                  # 3 pages, only 2 host slots
+    snap = (list(m.free), list(m.ref), {k: list(v) for k, v in m.pages.items()}, list(m.host_free))
+    with pytest.raises(oracle.NoPagesError):
+        m.seq_swap_out(a)
+    assert (m.free, m.ref, m.pages, m.host_free) == snap
+    m.host_reserve(3)
+    m.seq_swap_out(a)
+    b = m.seq_new()
+    m.seq_append(b, 24)                  # takes 6 of the 8 pages
+    snap = (list(m.free), list(m.ref), {k: list(v) for k, v in m.pages.items()}, list(m.host_free))
+    with pytest.raises(oracle.NoPagesError):
+        m.seq_swap_in(a)                 # needs 3, 2 free
+    assert (m.free, m.ref, m.pages, m.host_free) == snap
+    m.seq_free(a)                        # a swapped-out sequence can be freed
+    assert m.stats_host() == 3
+
+
+def test_swap_out_of_shared_pages_keeps_sharers():
+    m = oracle.AllocatorModel(12, 4)
+    m.host_reserve(4)
+    a = m.seq_new()
+    m.seq_append(a, 8)
+    f = m.seq_fork(a)
+    C = _Content(m)
+    C.write(a)
+    pairs = m.seq_swap_out(a)
+    C.to_host(pairs)
+    assert all(m.ref[p] == 1 for p in m.pages[f]) and len(m.free) == 10
+    m.seq_append(f, 1)                   # the sharer still owns its pages
+    C.to_dev(m.seq_swap_in(a))
+    assert C.logical(a) == [(a, 0), (a, 1)]
+    assert not (set(m.pages[a]) & set(m.pages[f]))
+
+
+def test_compaction_moves_live_pages_down_and_preserves_content():
+    rng = np.random.default_rng(12)
+    m = oracle.AllocatorModel(32, 4, rng.permutation(32))
+    C = _Content(m)
+    seqs = [m.seq_new() for _ in range(5)]
+    for s, n in zip(seqs, [9, 30, 4, 17, 13]):
+        m.seq_append(s, n)
+        C.write(s)
+    f = m.seq_fork(seqs[1])
+    m.seq_free(seqs[0])
+    m.seq_free(seqs[3])
+    before = {s: C.logical(s) for s in m.pages}
+    refs = sorted(r for r in m.ref if r > 0)
+    pairs = m.compact()
+    dsts = [d for _, d in pairs]
+    assert len(set(dsts)) == len(dsts) and not (set(dsts) & {s for s, _ in pairs})
+    C.copy(pairs)
+    n_live = len(refs)
+    assert all(p < n_live for s in m.pages for p in m.pages[s])
+    assert sorted(r for r in m.ref if r > 0) == refs
+    assert m.free == list(range(n_live, 32))[::-1]
+    assert {s: C.logical(s) for s in m.pages} == before
+    assert m.pages[f] == m.pages[seqs[1]]
+    assert m.compact() == []             # already compact

@@ -1,0 +1,134 @@
+"""Block swap (device <-> pinned host reserve) and pool compaction on the GPU:
+bit-exact against the oracle, and attention unchanged after preemption and
+after compaction."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_185_amd as pa
+import workloads as W
+from gpu_util import bits16, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def pinned_like(pool, n_pages):
+    shape = (n_pages,) + tuple(pool.shape[1:])
+    t = torch.empty(shape, dtype=torch.float16, pin_memory=True)
+    t.view(torch.int16).fill_(0x5555)
+    return t
+
+
+@pytest.mark.parametrize("n_layers", [1, 3])
+def test_swap_blocks_bitwise_round_trip(n_layers):
+    rng = np.random.default_rng(70 + n_layers)
+    N, H, P, D, NH = 24, 4, 32, 128, 10
+    ks = [rng.standard_normal((N, H, P, D)).astype(np.float16) for _ in range(n_layers)]
+    vs = [rng.standard_normal((N, H, D, P)).astype(np.float16) for _ in range(n_layers)]
+    kd, vd = [to_dev(k) for k in ks], [to_dev(v) for v in vs]
+    kh = [pinned_like(k, NH) for k in kd]
+    vh = [pinned_like(v, NH) for v in vd]
+    host0 = [k.numpy().copy() for k in kh], [v.numpy().copy() for v in vh]
+    out_pairs = np.array([[5, 0], [17, 3], [2, 9], [23, 4]], dtype=np.int32)
+    pa.pa_swap_blocks(kd, vd, kh, vh, out_pairs, to_host=True)
+    torch.cuda.synchronize()
+    hk, hv = oracle.swap_blocks(ks, vs, host0[0], host0[1], out_pairs)
+    for l in range(n_layers):
+        assert np.array_equal(bits16(kh[l].numpy()), bits16(hk[l]))
+        assert np.array_equal(bits16(vh[l].numpy()), bits16(hv[l]))
+    in_pairs = np.array([[3, 1], [0, 20], [9, 11], [4, 6]], dtype=np.int32)
+    pa.pa_swap_blocks(kd, vd, kh, vh, in_pairs, to_host=False)
+    dk, dv = oracle.swap_blocks(hk, hv, ks, vs, in_pairs)
+    for l in range(n_layers):
+        assert np.array_equal(bits16(to_host(kd[l])), bits16(dk[l]))
+        assert np.array_equal(bits16(to_host(vd[l])), bits16(dv[l]))
+
+
+def test_swap_blocks_rejects_bad_pairs():
+    k, v = W.nan_pools(8, 2, 16, 64)
+    kd, vd = to_dev(k), to_dev(v)
+    kh, vh = pinned_like(kd, 4), pinned_like(vd, 4)
+    with pytest.raises(pa.InvalidError):
+        pa.pa_swap_blocks([kd], [vd], [kh], [vh], [[1, 0], [2, 0]], to_host=True)   # repeated slot
+    with pytest.raises(pa.InvalidError):
+        pa.pa_swap_blocks([kd], [vd], [kh], [vh], [[1, 4]], to_host=True)           # slot out of range
+    with pytest.raises(pa.InvalidError):
+        pa.pa_swap_blocks([kd], [vd], [kh], [vh], [[4, 1]], to_host=False)          # slot out of range
+    # pageable host memory is rejected by the library (never handed to a kernel)
+    import ctypes
+    plain = np.zeros(kh.numel(), dtype=np.float16)
+    arr = lambda *ps: (ctypes.c_void_p * 1)(*ps)   # noqa: E731
+    pairs = np.array([[1, 0]], dtype=np.int32)
+    st = pa._lib.load().pa_swap_blocks(ctypes.byref(pa.cache_desc(kd, vd)), arr(kd.data_ptr()), arr(vd.data_ptr()),
+                                       arr(plain.ctypes.data), arr(plain.ctypes.data), 4, 1,
+                                       pairs.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), 1, 1, None)
+    assert st == -1
+
+
+def _decode(kd, vd, pool, seqs, q, scale, max_pages):
+    bt, kl = pool.block_tables(seqs, max_pages)
+    return to_host(pa.pa_decode(to_dev(q), kd, vd, to_dev(bt), to_dev(kl), float(scale), kv_lens_host=kl))
+
+
+def test_preemption_swap_out_reuse_swap_in_keeps_decode_bitwise():
+    """Decode two sequences; swap one out, let a new sequence take (and
+    overwrite) its pages, swap it back into other pages: its decode output is
+    bitwise what it was."""
+    rng = np.random.default_rng(81)
+    N, H, Hq, P, D = 40, 8, 32, 64, 128
+    kc, vc = W.nan_pools(N, H, P, D)
+    kd, vd = to_dev(kc), to_dev(vc)
+    pool = pa.Pool(N, P, rng.permutation(N))
+    pool.host_reserve(16)
+    kh, vh = pinned_like(kd, 16), pinned_like(vd, 16)
+    seqs = [pool.seq_new(), pool.seq_new()]
+    for s, n in zip(seqs, [700, 333]):
+        slots, _ = pool.seq_append(s, n)
+        pa.pa_reshape_and_cache(kd, vd, to_dev(rng.standard_normal((n, H, D)).astype(np.float16)),
+                                to_dev(rng.standard_normal((n, H, D)).astype(np.float16)), to_dev(slots))
+    q = rng.standard_normal((2, Hq, D)).astype(np.float32)
+    scale = W.fp32_scale(D)
+    before = _decode(kd, vd, pool, seqs, q, scale, 16)
+    pages_before = pool.block_tables([seqs[0]], 16)[0][0]
+    pa.pa_swap_blocks([kd], [vd], [kh], [vh], pool.seq_swap_out(seqs[0]), to_host=True)
+    other = pool.seq_new()
+    slots, _ = pool.seq_append(other, 900)      # reuses the freed pages
+    pa.pa_reshape_and_cache(kd, vd, to_dev(rng.standard_normal((900, H, D)).astype(np.float16)),
+                            to_dev(rng.standard_normal((900, H, D)).astype(np.float16)), to_dev(slots))
+    pa.pa_swap_blocks([kd], [vd], [kh], [vh], pool.seq_swap_in(seqs[0]), to_host=False)
+    pages_after = pool.block_tables([seqs[0]], 16)[0][0]
+    assert not np.array_equal(pages_before[:11], pages_after[:11])
+    after = _decode(kd, vd, pool, seqs, q, scale, 16)
+    assert np.array_equal(before, after)
+
+
+def test_compaction_keeps_decode_bitwise_and_packs_pages():
+    rng = np.random.default_rng(82)
+    N, H, Hq, P, D = 64, 4, 16, 32, 64
+    kc, vc = W.nan_pools(N, H, P, D)
+    kd, vd = to_dev(kc), to_dev(vc)
+    pool = pa.Pool(N, P, rng.permutation(N))
+    seqs = []
+    for n in [100, 257, 31, 400, 64, 150]:
+        s = pool.seq_new()
+        slots, _ = pool.seq_append(s, n)
+        pa.pa_reshape_and_cache(kd, vd, to_dev(rng.standard_normal((n, H, D)).astype(np.float16)),
+                                to_dev(rng.standard_normal((n, H, D)).astype(np.float16)), to_dev(slots))
+        seqs.append(s)
+    seqs.append(pool.seq_fork(seqs[1]))
+    pool.seq_free(seqs[0])
+    pool.seq_free(seqs[3])
+    live = [seqs[i] for i in (1, 2, 4, 5, 6)]
+    q = rng.standard_normal((len(live), Hq, D)).astype(np.float32)
+    scale = W.fp32_scale(D)
+    before = _decode(kd, vd, pool, live, q, scale, 16)
+    moves = pool.compact()
+    assert len(moves) > 0
+    pa.pa_copy_blocks([kd], [vd], moves)
+    n_free, ref = pool.stats()
+    n_live = int((ref > 0).sum())
+    bt, _ = pool.block_tables(live, 16)
+    assert bt.max() < n_live and n_free == N - n_live
+    after = _decode(kd, vd, pool, live, q, scale, 16)
+    assert np.array_equal(before, after)
