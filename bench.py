@@ -327,6 +327,76 @@ def bench_unified(args, pa, torch, W, dec_case):
     return out
 
 
+def bench_swap_compact(args, pa, torch, W):
+    """Preemption swap of one 16384-token sequence (128 pages of 512 KiB K+V) to a
+    pinned host reserve and back, against a plain device<->pinned copy of the same
+    bytes; and compaction of a fragmented 2048-page pool (pa_pool_compact moves,
+    performed by pa_copy_blocks)."""
+    dev = torch.device("cuda:0")
+    P, H, D, N = 128, 8, 128, 2048
+    rng = np.random.default_rng(185009)
+    kd = torch.empty((N, H, P, D), dtype=torch.float16, device=dev).normal_()
+    vd = torch.empty((N, H, D, P), dtype=torch.float16, device=dev).normal_()
+    pool = pa.Pool(N, P, rng.permutation(N))
+    pool.host_reserve(256)
+    seqs = [pool.seq_new() for _ in range(8)]
+    for s in seqs:
+        pool.seq_append(s, 16384)
+    kh = torch.empty((256, H, P, D), dtype=torch.float16, pin_memory=True)
+    vh = torch.empty((256, H, D, P), dtype=torch.float16, pin_memory=True)
+    page_bytes = 2 * H * P * D * 2
+    stream = torch.cuda.current_stream()
+    ev = lambda: torch.cuda.Event(enable_timing=True)   # noqa: E731
+    out_pairs = pool.seq_swap_out(seqs[0])
+    pa.pa_swap_blocks([kd], [vd], [kh], [vh], out_pairs, to_host=True)       # warm
+    torch.cuda.synchronize()
+    e0, e1, e2 = ev(), ev(), ev()
+    e0.record(stream)
+    pa.pa_swap_blocks([kd], [vd], [kh], [vh], out_pairs, to_host=True)
+    e1.record(stream)
+    in_pairs = pool.seq_swap_in(seqs[0])
+    pa.pa_swap_blocks([kd], [vd], [kh], [vh], in_pairs, to_host=False)
+    e2.record(stream)
+    torch.cuda.synchronize()
+    nbytes = len(out_pairs) * page_bytes
+    t_out, t_in = e0.elapsed_time(e1) * 1e-3, e1.elapsed_time(e2) * 1e-3
+    # reference: torch's copies of the same bytes between contiguous device and pinned buffers
+    dbuf = torch.empty(nbytes // 2, dtype=torch.float16, device=dev)
+    hbuf = torch.empty(nbytes // 2, dtype=torch.float16, pin_memory=True)
+    hbuf.copy_(dbuf, non_blocking=True)
+    torch.cuda.synchronize()
+    r0, r1, r2 = ev(), ev(), ev()
+    r0.record(stream)
+    hbuf.copy_(dbuf, non_blocking=True)
+    r1.record(stream)
+    dbuf.copy_(hbuf, non_blocking=True)
+    r2.record(stream)
+    torch.cuda.synchronize()
+    ref_out, ref_in = r0.elapsed_time(r1) * 1e-3, r1.elapsed_time(r2) * 1e-3
+    res = {"swap": {
+        "pages": len(out_pairs), "bytes": nbytes,
+        "to_host_GBps": round(nbytes / t_out / 1e9, 2), "to_device_GBps": round(nbytes / t_in / 1e9, 2),
+        "plain_copy_to_host_GBps": round(nbytes / ref_out / 1e9, 2),
+        "plain_copy_to_device_GBps": round(nbytes / ref_in / 1e9, 2),
+    }}
+    # compaction: free every other sequence of a pool filled in random page order
+    for s in seqs[1::2]:
+        pool.seq_free(s)
+    moves = pool.compact()
+    pa.pa_copy_blocks([kd], [vd], moves[:1])    # warm
+    torch.cuda.synchronize()
+    c0, c1 = ev(), ev()
+    c0.record(stream)
+    pa.pa_copy_blocks([kd], [vd], moves)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    t = c0.elapsed_time(c1) * 1e-3
+    moved = len(moves) * page_bytes
+    res["compaction"] = {"live_pages": int((pool.stats()[1] > 0).sum()), "moves": len(moves),
+                         "bytes_moved": moved, "GBps_read_plus_write": round(2 * moved / t / 1e9, 1)}
+    return res
+
+
 def cpu_baseline_decode(c, oracle):
     t0 = time.perf_counter()
     oracle.paged_decode(c.q, c.k_pool, c.v_pool, c.block_tables, c.kv_lens, c.scale)
@@ -371,6 +441,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-unified", action="store_true",
                     help="skip the paged-vs-unified-span comparison")
+    ap.add_argument("--no-swap", action="store_true", help="skip the swap / compaction measurement")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device-to-device copy of this many bytes (3 times): the "
                          "known-size kernel that calibrates the FETCH_SIZE / WRITE_SIZE counters")
@@ -415,6 +486,12 @@ def main():
         log("unified span: paged vs unified on the UA ubatch and the decode batch")
         uni = bench_unified(args, pa, torch, W, c)
         log(f"unified span: {json.dumps(uni)}")
+
+    swp = None
+    if not args.no_swap:
+        log("swap / compaction")
+        swp = bench_swap_compact(args, pa, torch, W)
+        log(f"swap / compaction: {json.dumps(swp)}")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -480,6 +557,8 @@ def main():
         }
     if uni is not None:
         result["unified_vs_paged"] = uni
+    if swp is not None:
+        result.update(swp)
     print(json.dumps(result), flush=True)
 
 
