@@ -150,7 +150,8 @@ pa_status pa_pool_stats(const pa_pool* pool, int32_t* n_free_out, int32_t* refco
  *
  * pa_pool_compact: with n_live pages in use, moves every live page with id >=
  * n_live (ascending) onto the free ids below n_live (ascending), rewrites
- * every resident sequence's table and the refcounts, and leaves the free
+ * every resident sequence's table, the prefix cache's pages (below) and the
+ * refcounts, and leaves the free
  * stack n_live..N-1 with n_live handed out first.  The (src, dst) moves go to
  * pairs_out (at most num_pages); they satisfy pa_copy_blocks' rules, which
  * performs them on the device.
@@ -163,6 +164,47 @@ pa_status pa_seq_swap_in(pa_pool* pool, int32_t seq, int32_t* pairs_out, int32_t
                          int32_t* n_pairs_out);
 pa_status pa_pool_compact(pa_pool* pool, int32_t* pairs_out, int32_t max_pairs, int32_t* n_pairs_out);
 pa_status pa_pool_host_stats(const pa_pool* pool, int32_t* n_host_free_out);
+
+/* Prefix cache: "CacheFlow：基于 llama.cpp 的多请求 LLM 推理优化引擎", section
+ * 核心架构与技术贡献 item 2 and section 前缀缓存优化 (a trie lookup reuses the KV
+ * blocks of shared prefixes, such as a common system prompt), and
+ * "面向边缘智能体推理的 llama.cpp KV Cache 共享与复用优化", section 主要功能与技术路线
+ * (longest-prefix match over a token prefix tree, LRU reclaim of its leaves).
+ * The tree's edges are whole pages of token ids (page_size int32 tokens), the
+ * page being what two sequences can share without a copy; every cached node
+ * holds one reference on its physical page.  Token ids are opaque int32.
+ * Token arrays are host memory read during the call only.
+ *
+ * pa_prefix_insert: walks the first n_tokens / page_size full pages of
+ * tokens (which must be the sequence's first tokens, n_tokens <= its length)
+ * and caches each one not yet in the tree with the sequence's page at that
+ * position (refcount + 1).  *n_cached_out (may be null) = cached pages on the
+ * path.  Stamps the path as most recently used, then evicts over capacity.
+ * PA_ERR_INVALID if a page to cache is already cached under another path (the
+ * same sequence inserted with different tokens); failures change nothing.
+ *
+ * pa_prefix_match: follows full pages of tokens as far as the tree holds
+ * them, stamps that path, and creates a new sequence (*seq_out) whose table is
+ * those pages (refcount + 1 each) and whose length *n_matched_out is the
+ * matched page count * page_size (0 if nothing matched).  The caller appends
+ * the rest of its tokens to it; the length is page-aligned, so no shared page
+ * is ever written.  The cache never pins a sequence: freeing it drops only
+ * its own references.
+ *
+ * Eviction removes the leaf with the oldest stamp among leaves whose page no
+ * sequence holds, so each removal frees exactly one page; a cached page that a
+ * live or matched sequence still uses is not evicted.
+ * pa_prefix_evict: frees up to n_pages pages this way (*n_freed_out).
+ * pa_prefix_capacity: caps the cached page count (default num_pages) and
+ * evicts down to it as far as eviction can; *n_freed_out may be null.
+ * pa_prefix_stats: cached page count. */
+pa_status pa_prefix_insert(pa_pool* pool, int32_t seq, const int32_t* tokens, int32_t n_tokens,
+                           int32_t* n_cached_out);
+pa_status pa_prefix_match(pa_pool* pool, const int32_t* tokens, int32_t n_tokens, int32_t* seq_out,
+                          int32_t* n_matched_out);
+pa_status pa_prefix_evict(pa_pool* pool, int32_t n_pages, int32_t* n_freed_out);
+pa_status pa_prefix_capacity(pa_pool* pool, int32_t max_pages, int32_t* n_freed_out);
+pa_status pa_prefix_stats(const pa_pool* pool, int32_t* n_cached_out);
 
 /* ===================================================================== */
 /* Device operations.                                                    */

@@ -37,8 +37,29 @@ choice nor the move order; this model fixes them:
   ``seq_swap_in`` accept it;
 * compaction with ``n_live`` pages in use moves every live page whose id is
   >= ``n_live`` (ascending) onto the free ids below ``n_live`` (ascending),
-  carries refcounts and table entries along, and rebuilds the free stack as
-  ``n_live .. N-1`` with ``n_live`` on top.
+  carries refcounts and table entries along (prefix-index pages included), and
+  rebuilds the free stack as ``n_live .. N-1`` with ``n_live`` on top.
+
+Prefix cache (page "CacheFlow：基于 llama.cpp 的多请求 LLM 推理优化引擎", section
+核心架构与技术贡献 item 2 and section 前缀缓存优化: a trie lookup reuses the blocks of
+shared prefixes; page "面向边缘智能体推理的 llama.cpp KV Cache 共享与复用优化",
+section 主要功能与技术路线: longest-prefix match over a token prefix tree, with LRU
+reclaim of its leaves).  Page-aligned reading: the tree's edges are whole pages
+of token ids, since a page is the unit that two sequences can share without a
+copy; each node holds one physical page and one reference on it.
+
+* ``prefix_insert(seq, tokens)`` walks the sequence's full pages (tokens
+  ``jP .. jP+P-1`` for ``(j+1)P <= len(tokens)``, which must not exceed the
+  sequence's length); a missing node takes the sequence's page ``j`` (ref + 1),
+  an existing node keeps its page; every node on the path gets the current
+  clock value, then the clock advances;
+* ``prefix_match(tokens)`` follows full pages as far as they match, stamps the
+  matched path, advances the clock and returns a new sequence sharing those
+  pages (ref + 1 each) with length ``matched_pages * P``;
+* when more than ``capacity`` pages are cached (after an insert), and on
+  ``prefix_evict(n)``, the leaf with the oldest stamp is removed (its index
+  reference dropped, the page pushed if its count reaches 0), repeatedly;
+  stamps of leaves are unique because one call stamps one path.
 
 Pinned by invariants (page conservation, sharing only under refcount > 1,
 free-all restores every page, page counts with and without sharing) in
@@ -83,6 +104,12 @@ class AllocatorModel:
         self.host: Dict[int, List[int]] = {}         # swapped-out sequences' host slots
         self.host_free: List[int] = []
         self.n_host = 0
+        # prefix trie: node id -> [parent, key tuple, page, stamp]; children by (parent, key)
+        self.trie: Dict[int, list] = {}
+        self.child: Dict[Tuple[int, tuple], int] = {}
+        self.next_node = 1                           # node 0 is the root
+        self.clock = 0
+        self.capacity = num_pages
 
     # -- helpers
     def _pop(self) -> int:
@@ -247,6 +274,8 @@ class AllocatorModel:
         dest = dict(zip(movers, holes))
         for s in self.pages:
             self.pages[s] = [dest.get(p, p) for p in self.pages[s]]
+        for node in self.trie.values():
+            node[2] = dest.get(node[2], node[2])
         for src, dst in dest.items():
             self.ref[dst] = self.ref[src]
             self.ref[src] = 0
@@ -256,3 +285,98 @@ class AllocatorModel:
     def stats_host(self):
         return len(self.host_free)
 
+    # -- prefix cache
+    def prefix_capacity(self, max_pages: int) -> int:
+        """Sets the cached-page budget; returns the pages freed to meet it."""
+        if max_pages < 0:
+            raise InvalidError("capacity < 0")
+        self.capacity = max_pages
+        return self._evict(lambda: len(self.trie) > self.capacity)
+
+    def _evict(self, more) -> int:
+        """Removes least recently stamped evictable leaves while more() holds.
+        A leaf is evictable when the index's reference is its page's only one,
+        so every removal frees exactly one page."""
+        freed = 0
+        while more():
+            parents = {v[0] for v in self.trie.values()}
+            cand = [n for n, v in self.trie.items() if n not in parents and self.ref[v[2]] == 1]
+            if not cand:
+                break
+            n = min(cand, key=lambda x: self.trie[x][3])
+            parent, key, page, _ = self.trie.pop(n)
+            del self.child[(parent, key)]
+            self.ref[page] = 0
+            self.free.append(page)
+            freed += 1
+        return freed
+
+    def prefix_insert(self, seq: int, tokens: Sequence[int]) -> int:
+        """Returns the number of pages cached along the sequence's path."""
+        self._alive(seq)
+        P = self.page_size
+        tokens = [int(t) for t in tokens]
+        if len(tokens) > self.length[seq]:
+            raise InvalidError("more tokens than the sequence holds")
+        cached = {v[2] for v in self.trie.values()}
+        node, path, new = 0, [], []
+        for j in range(len(tokens) // P):
+            key = tuple(tokens[j * P:(j + 1) * P])
+            nxt = self.child.get((node, key)) if node >= 0 else None
+            if nxt is None:
+                page = self.pages[seq][j]
+                if page in cached:
+                    raise InvalidError("page already cached under another prefix")
+                new.append((j, key))
+                node = -1
+            else:
+                path.append(nxt)
+                node = nxt
+        node = path[-1] if path else 0
+        for j, key in new:
+            nxt = self.next_node
+            self.next_node += 1
+            page = self.pages[seq][j]
+            self.ref[page] += 1
+            self.trie[nxt] = [node, key, page, 0]
+            self.child[(node, key)] = nxt
+            path.append(nxt)
+            node = nxt
+        for n in path:
+            self.trie[n][3] = self.clock
+        self.clock += 1
+        self._evict(lambda: len(self.trie) > self.capacity)
+        return len(path)
+
+    def prefix_match(self, tokens: Sequence[int]) -> Tuple[int, int]:
+        """Returns (new sequence sharing the longest cached page-aligned prefix,
+        matched tokens)."""
+        P = self.page_size
+        tokens = [int(t) for t in tokens]
+        node, path = 0, []
+        for j in range(len(tokens) // P):
+            nxt = self.child.get((node, tuple(tokens[j * P:(j + 1) * P])))
+            if nxt is None:
+                break
+            path.append(nxt)
+            node = nxt
+        for n in path:
+            self.trie[n][3] = self.clock
+        self.clock += 1
+        seq = self.seq_new()
+        pages = [self.trie[n][2] for n in path]
+        for p in pages:
+            self.ref[p] += 1
+        self.pages[seq] = pages
+        self.length[seq] = len(pages) * P
+        return seq, len(pages) * P
+
+    def prefix_evict(self, n_pages: int) -> int:
+        """Frees up to n_pages cached pages in LRU order; returns how many."""
+        if n_pages < 0:
+            raise InvalidError("n_pages < 0")
+        target = len(self.free) + n_pages
+        return self._evict(lambda: len(self.free) < target)
+
+    def prefix_pages(self) -> int:
+        return len(self.trie)

@@ -213,6 +213,35 @@ class Pool:
         _check(_L().pa_pool_host_stats(self._h, ctypes.byref(n)))
         return n.value
 
+    def prefix_insert(self, seq: int, tokens: Sequence[int]) -> int:
+        """Caches the sequence's full pages under their tokens; see pa_prefix_insert."""
+        t = _host_i32(tokens)
+        n = ctypes.c_int32(0)
+        _check(_L().pa_prefix_insert(self._h, int(seq), _i32p(t), len(t), ctypes.byref(n)))
+        return n.value
+
+    def prefix_match(self, tokens: Sequence[int]):
+        """(new sequence sharing the longest cached prefix, matched tokens)."""
+        t = _host_i32(tokens)
+        s, m = ctypes.c_int32(), ctypes.c_int32()
+        _check(_L().pa_prefix_match(self._h, _i32p(t), len(t), ctypes.byref(s), ctypes.byref(m)))
+        return s.value, m.value
+
+    def prefix_evict(self, n_pages: int) -> int:
+        n = ctypes.c_int32(0)
+        _check(_L().pa_prefix_evict(self._h, int(n_pages), ctypes.byref(n)))
+        return n.value
+
+    def prefix_capacity(self, max_pages: int) -> int:
+        n = ctypes.c_int32(0)
+        _check(_L().pa_prefix_capacity(self._h, int(max_pages), ctypes.byref(n)))
+        return n.value
+
+    def prefix_pages(self) -> int:
+        n = ctypes.c_int32(0)
+        _check(_L().pa_prefix_stats(self._h, ctypes.byref(n)))
+        return n.value
+
     def stats(self):
         n = ctypes.c_int32()
         ref = np.empty(self.num_pages, dtype=np.int32)

@@ -42,6 +42,11 @@ SIGNATURES = {
     "pa_seq_swap_in": (c_i32, [c_void_p, c_i32, c_i32_p, c_i32, c_i32_p]),
     "pa_pool_compact": (c_i32, [c_void_p, c_i32_p, c_i32, c_i32_p]),
     "pa_pool_host_stats": (c_i32, [c_void_p, c_i32_p]),
+    "pa_prefix_insert": (c_i32, [c_void_p, c_i32, c_i32_p, c_i32, c_i32_p]),
+    "pa_prefix_match": (c_i32, [c_void_p, c_i32_p, c_i32, c_i32_p, c_i32_p]),
+    "pa_prefix_evict": (c_i32, [c_void_p, c_i32, c_i32_p]),
+    "pa_prefix_capacity": (c_i32, [c_void_p, c_i32, c_i32_p]),
+    "pa_prefix_stats": (c_i32, [c_void_p, c_i32_p]),
     "pa_reshape_and_cache": (c_i32, [CacheDesc_p, c_void_p, c_void_p, c_void_p, c_void_p, c_i32,
                                      c_void_p, c_i32, c_void_p]),
     "pa_copy_blocks": (c_i32, [CacheDesc_p, ctypes.POINTER(c_void_p), ctypes.POINTER(c_void_p),

@@ -20,10 +20,22 @@
 // and swap-in walk the sequence's pages in logical order; compaction moves the
 // live pages with ids >= n_live (ascending) onto the free ids below n_live
 // (ascending) and leaves the free stack n_live..N-1 with n_live on top.
+//
+// Prefix cache ("CacheFlow", section 核心架构与技术贡献 item 2 and section 前缀缓存优化:
+// a trie lookup reuses the blocks of shared prefixes; "面向边缘智能体推理的 llama.cpp
+// KV Cache 共享与复用优化", section 主要功能与技术路线: longest-prefix match and LRU
+// reclaim of leaves).  The tree's edges are whole pages of token ids, a page being
+// the unit two sequences can share without a copy; each node holds one reference
+// on its page.  Every insert and match stamps the nodes on its root path with a
+// clock that then advances, so a parent's stamp is never below its children's
+// and no two leaves share a stamp.  Eviction removes the least recently stamped
+// leaf whose page nobody else holds, so each removal frees one page.
 #include <algorithm>
 #include <cstring>
+#include <map>
 #include <new>
 #include <string>
+#include <unordered_map>
 #include <vector>
 
 #include "pa.h"
@@ -47,6 +59,98 @@ struct pa_pool {
         std::vector<int32_t> pages;   // device pages, or host slots while swapped
     };
     std::vector<Seq> seqs;
+
+    // prefix tree; node 0 is the root and holds no page
+    struct Node {
+        int32_t parent = -1;
+        int32_t page = -1;
+        int32_t n_children = 0;
+        uint64_t stamp = 0;
+        std::string key;   // parent id then the page's tokens, as raw bytes
+    };
+    std::vector<Node> nodes{Node{}};
+    std::vector<int32_t> free_nodes;
+    std::unordered_map<std::string, int32_t> child;   // Node::key -> node
+    std::map<uint64_t, int32_t> leaves;               // stamp -> leaf node
+    std::vector<int32_t> node_of_page;                // page -> node, or -1
+    int32_t n_cached = 0;
+    int32_t capacity = 0;
+    uint64_t clock = 0;
+
+    std::string edge(int32_t parent, const int32_t* toks) const {
+        std::string k(sizeof(int32_t) * (1 + (size_t)page_size), '\0');
+        std::memcpy(&k[0], &parent, sizeof(int32_t));
+        std::memcpy(&k[sizeof(int32_t)], toks, sizeof(int32_t) * (size_t)page_size);
+        return k;
+    }
+    int32_t find_child(int32_t parent, const int32_t* toks) const {
+        auto it = child.find(edge(parent, toks));
+        return it == child.end() ? -1 : it->second;
+    }
+    void restamp(int32_t n, uint64_t c) {
+        Node& x = nodes[n];
+        if (x.n_children == 0) leaves.erase(x.stamp);
+        x.stamp = c;
+        if (x.n_children == 0) leaves[c] = n;
+    }
+    int32_t add_node(int32_t parent, const int32_t* toks, int32_t page, uint64_t c) {
+        int32_t n;
+        if (!free_nodes.empty()) {
+            n = free_nodes.back();
+            free_nodes.pop_back();
+        } else {
+            nodes.emplace_back();
+            n = (int32_t)nodes.size() - 1;
+        }
+        Node& x = nodes[n];
+        x.parent = parent;
+        x.page = page;
+        x.n_children = 0;
+        x.stamp = c;
+        x.key = edge(parent, toks);
+        child[x.key] = n;
+        // the parent stops being a leaf before the child, which may carry the
+        // same stamp, enters the leaf set
+        if (parent != 0 && nodes[parent].n_children == 0) leaves.erase(nodes[parent].stamp);
+        nodes[parent].n_children++;
+        leaves[c] = n;
+        node_of_page[page] = n;
+        ref[page] += 1;
+        n_cached += 1;
+        return n;
+    }
+    // Frees cached pages in LRU order while more() holds; returns how many.
+    // Leaves below the cursor were found held by someone else; removing one
+    // leaf changes no other page's count, and a parent that becomes a leaf has
+    // a stamp at least the cursor's, so the scan never has to go back.
+    template <class More>
+    int32_t evict(More more) {
+        int32_t freed = 0;
+        uint64_t cur = 0;
+        while (more()) {
+            auto it = leaves.lower_bound(cur);
+            while (it != leaves.end() && ref[nodes[it->second].page] != 1) ++it;
+            if (it == leaves.end()) break;
+            cur = it->first;
+            const int32_t n = it->second;
+            leaves.erase(it);
+            Node& x = nodes[n];
+            child.erase(x.key);
+            node_of_page[x.page] = -1;
+            ref[x.page] = 0;
+            free_stack.push_back(x.page);
+            const int32_t parent = x.parent;
+            x = Node{};
+            free_nodes.push_back(n);
+            n_cached -= 1;
+            if (--nodes[parent].n_children == 0 && parent != 0) leaves[nodes[parent].stamp] = parent;
+            freed += 1;
+        }
+        return freed;
+    }
+    int32_t evict_over_capacity() {
+        return evict([this] { return n_cached > capacity; });
+    }
 
     int32_t pop() {
         int32_t p = free_stack.back();
@@ -100,6 +204,8 @@ pa_status pa_pool_create(int32_t num_pages, int32_t page_size, const int32_t* fr
     pool->page_size = page_size;
     pool->free_stack.assign(order.rbegin(), order.rend());
     pool->ref.assign(num_pages, 0);
+    pool->node_of_page.assign(num_pages, -1);
+    pool->capacity = num_pages;
     *out = pool;
     return PA_OK;
 }
@@ -323,6 +429,13 @@ pa_status pa_pool_compact(pa_pool* pool, int32_t* pairs_out, int32_t max_pairs, 
     for (auto& s : pool->seqs)
         if (s.live && !s.swapped)
             for (int32_t& p : s.pages) p = dest[p];
+    std::fill(pool->node_of_page.begin(), pool->node_of_page.end(), -1);
+    for (size_t n = 1; n < pool->nodes.size(); ++n) {
+        auto& x = pool->nodes[n];
+        if (x.page < 0) continue;
+        x.page = dest[x.page];
+        pool->node_of_page[x.page] = (int32_t)n;
+    }
     for (int32_t i = 0; i < n; ++i) {
         pool->ref[holes[i]] = pool->ref[movers[i]];
         pool->ref[movers[i]] = 0;
@@ -336,6 +449,91 @@ pa_status pa_pool_compact(pa_pool* pool, int32_t* pairs_out, int32_t max_pairs, 
 pa_status pa_pool_host_stats(const pa_pool* pool, int32_t* n_host_free_out) {
     if (!pool || !n_host_free_out) return fail(PA_ERR_INVALID, "pa_pool_host_stats: null argument");
     *n_host_free_out = (int32_t)pool->host_free.size();
+    return PA_OK;
+}
+
+pa_status pa_prefix_capacity(pa_pool* pool, int32_t max_pages, int32_t* n_freed_out) {
+    if (!pool || max_pages < 0) return fail(PA_ERR_INVALID, "pa_prefix_capacity: bad argument");
+    pool->capacity = max_pages;
+    int32_t freed = pool->evict_over_capacity();
+    if (n_freed_out) *n_freed_out = freed;
+    return PA_OK;
+}
+
+pa_status pa_prefix_insert(pa_pool* pool, int32_t seq, const int32_t* tokens, int32_t n_tokens,
+                           int32_t* n_cached_out) {
+    if (!pool || n_tokens < 0 || (n_tokens > 0 && !tokens))
+        return fail(PA_ERR_INVALID, "pa_prefix_insert: bad argument");
+    if (!pool->live(seq)) return fail(PA_ERR_STATE, "pa_prefix_insert: sequence is not live");
+    const auto& s = pool->seqs[seq];
+    if (n_tokens > s.len)
+        return fail(PA_ERR_INVALID, "pa_prefix_insert: more tokens than the sequence holds");
+    const int32_t P = pool->page_size;
+    const int32_t full = n_tokens / P;
+    std::vector<int32_t> path;
+    int32_t node = 0;
+    int32_t j = 0;
+    for (; j < full; ++j) {
+        int32_t nx = pool->find_child(node, tokens + (int64_t)j * P);
+        if (nx < 0) break;
+        path.push_back(nx);
+        node = nx;
+    }
+    for (int32_t k = j; k < full; ++k)
+        if (pool->node_of_page[s.pages[k]] >= 0)
+            return fail(PA_ERR_INVALID, "pa_prefix_insert: page already cached under another prefix");
+    const uint64_t c = pool->clock++;
+    for (int32_t n : path) pool->restamp(n, c);
+    for (; j < full; ++j) {
+        node = pool->add_node(node, tokens + (int64_t)j * P, s.pages[j], c);
+        path.push_back(node);
+    }
+    pool->evict_over_capacity();
+    if (n_cached_out) *n_cached_out = (int32_t)path.size();
+    return PA_OK;
+}
+
+pa_status pa_prefix_match(pa_pool* pool, const int32_t* tokens, int32_t n_tokens, int32_t* seq_out,
+                          int32_t* n_matched_out) {
+    if (!pool || !seq_out || !n_matched_out || n_tokens < 0 || (n_tokens > 0 && !tokens))
+        return fail(PA_ERR_INVALID, "pa_prefix_match: bad argument");
+    const int32_t P = pool->page_size;
+    std::vector<int32_t> path;
+    int32_t node = 0;
+    for (int32_t j = 0; j < n_tokens / P; ++j) {
+        int32_t nx = pool->find_child(node, tokens + (int64_t)j * P);
+        if (nx < 0) break;
+        path.push_back(nx);
+        node = nx;
+    }
+    const uint64_t c = pool->clock++;
+    for (int32_t n : path) pool->restamp(n, c);
+    int32_t id = pool->new_id();
+    auto& d = pool->seqs[id];
+    d.live = true;
+    d.swapped = false;
+    d.pages.clear();
+    for (int32_t n : path) {
+        int32_t p = pool->nodes[n].page;
+        d.pages.push_back(p);
+        pool->ref[p] += 1;
+    }
+    d.len = (int64_t)path.size() * P;
+    *seq_out = id;
+    *n_matched_out = (int32_t)d.len;
+    return PA_OK;
+}
+
+pa_status pa_prefix_evict(pa_pool* pool, int32_t n_pages, int32_t* n_freed_out) {
+    if (!pool || !n_freed_out || n_pages < 0) return fail(PA_ERR_INVALID, "pa_prefix_evict: bad argument");
+    const size_t target = pool->free_stack.size() + (size_t)n_pages;
+    *n_freed_out = pool->evict([pool, target] { return pool->free_stack.size() < target; });
+    return PA_OK;
+}
+
+pa_status pa_prefix_stats(const pa_pool* pool, int32_t* n_cached_out) {
+    if (!pool || !n_cached_out) return fail(PA_ERR_INVALID, "pa_prefix_stats: null argument");
+    *n_cached_out = pool->n_cached;
     return PA_OK;
 }
 

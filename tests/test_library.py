@@ -211,3 +211,108 @@ def test_workspace_sizes():
     pos = np.arange(15872, 16384, dtype=np.int32)
     assert pa.pa_prefill_workspace_bytes(d, 32, row, kv, pos, 1) == 0
     assert pa.pa_prefill_workspace_bytes(d, 32, row, kv, pos, 4) >= n * 32 * 4 * 130 * 4
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_prefix_cache_matches_model_bit_for_bit(seed):
+    """Prefix insert / match / evict / capacity, interleaved with the pool's
+    other calls (fork, copy-on-write, swap, compaction), on the model and on the
+    library: every result, error class, refcount and table must agree."""
+    rng = np.random.default_rng(200 + seed)
+    N, P = 64, [2, 4, 16][seed]
+    order = rng.permutation(N)
+    model = oracle.AllocatorModel(N, P, order)
+    lib = pa.Pool(N, P, order)
+    model.host_reserve(16)
+    lib.host_reserve(16)
+    head = list(rng.integers(0, 5, 3 * P))
+    docs = [head + list(rng.integers(0, 5, 6 * P)) for _ in range(3)] + [list(rng.integers(0, 5, 9 * P))]
+
+    def stream(prefix):
+        """A sequence's tokens: a document's (or a match's) prefix, then its own."""
+        return list(prefix) + list(rng.integers(0, 5, 8 * P))
+
+    toks = {}          # sequence -> (its token stream, tokens it holds)
+    live, swapped = [], []
+    for _ in range(1500):
+        op = int(rng.integers(0, 12))
+        if len(live) > 6 and rng.random() < 0.5:
+            op = 3                                     # keep few holders, so eviction frees
+        if op == 0 or not live:
+            a, b = _both(model.seq_new, lib.seq_new)
+            assert a == b
+            live.append(a)
+            d = docs[int(rng.integers(len(docs)))]
+            toks[a] = (stream(d[:int(rng.integers(0, len(d) + 1))]), 0)
+        elif op == 1:
+            s = live[int(rng.integers(len(live)))]
+            t, L = toks[s]
+            n = min(int(rng.integers(0, 4 * P)), len(t) - L)
+            a, b = _both(lambda: model.seq_append(s, n), lambda: lib.seq_append(s, n))
+            if a is not None:
+                assert np.array_equal(a[0], b[0]) and a[1] == b[1]
+                toks[s] = (t, L + n)
+        elif op == 2:
+            s = live[int(rng.integers(len(live)))]
+            a, b = _both(lambda: model.seq_fork(s), lambda: lib.seq_fork(s))
+            assert a == b
+            live.append(a)
+            t, L = toks[s]
+            toks[a] = (t[:L] + stream([])[:len(t) - L], L)   # same past, own future
+        elif op == 3:
+            s = live.pop(int(rng.integers(len(live))))
+            _both(lambda: model.seq_free(s), lambda: lib.seq_free(s))
+        elif op in (4, 5):
+            s = live[int(rng.integers(len(live)))]
+            t, L = toks[s]
+            cut = L + 1 if rng.random() < 0.05 else L - int(rng.integers(0, 2 * P)) if L else 0
+            q = list(t[:max(cut, 0)])
+            if rng.random() < 0.05 and q:
+                q[int(rng.integers(len(q)))] = 7       # tokens the pages do not hold
+            a, b = _both(lambda: model.prefix_insert(s, q), lambda: lib.prefix_insert(s, q))
+            assert a == b
+        elif op in (6, 7):
+            d = docs[int(rng.integers(len(docs)))]
+            q = d[:int(rng.integers(0, len(d) + 1))]
+            if live and rng.random() < 0.5:             # a sequence's own history
+                t, L = toks[live[int(rng.integers(len(live)))]]
+                q = t[:L]
+            a, b = _both(lambda: model.prefix_match(q), lambda: lib.prefix_match(q))
+            assert a == b
+            live.append(a[0])
+            toks[a[0]] = (stream(q[:a[1]]), a[1])
+        elif op == 8:
+            n = int(rng.integers(0, 6))
+            a, b = _both(lambda: model.prefix_evict(n), lambda: lib.prefix_evict(n))
+            assert a == b
+        elif op == 9:
+            c = int(rng.integers(0, 12)) if rng.random() < 0.7 else N
+            a, b = _both(lambda: model.prefix_capacity(c), lambda: lib.prefix_capacity(c))
+            assert a == b
+        elif op == 10:
+            if swapped and rng.random() < 0.5:
+                s = swapped[int(rng.integers(len(swapped)))]
+                a, b = _both(lambda: model.seq_swap_in(s), lambda: lib.seq_swap_in(s))
+                if a is not None:
+                    assert np.array_equal(np.asarray(a, dtype=np.int32).reshape(-1, 2), b)
+                    swapped.remove(s)
+                    live.append(s)
+            else:
+                s = live[int(rng.integers(len(live)))]
+                a, b = _both(lambda: model.seq_swap_out(s), lambda: lib.seq_swap_out(s))
+                if a is not None:
+                    assert np.array_equal(np.asarray(a, dtype=np.int32).reshape(-1, 2), b)
+                    live.remove(s)
+                    swapped.append(s)
+        elif op == 11:
+            a, b = _both(model.compact, lib.compact)
+            assert np.array_equal(np.asarray(a, dtype=np.int32).reshape(-1, 2), b)
+        assert model.prefix_pages() == lib.prefix_pages()
+        nm, rm = model.stats()
+        nl, rl = lib.stats()
+        assert nm == nl and np.array_equal(rm, rl)
+        if live:
+            mp = max(1, max(len(model.pages[x]) for x in live))
+            bm, km = model.block_tables(live, mp)
+            bl, kl = lib.block_tables(live, mp)
+            assert np.array_equal(bm, bl) and np.array_equal(km, kl)

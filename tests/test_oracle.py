@@ -680,3 +680,183 @@ def test_compaction_moves_live_pages_down_and_preserves_content():
     assert {s: C.logical(s) for s in m.pages} == before
     assert m.pages[f] == m.pages[seqs[1]]
     assert m.compact() == []             # already compact
+
+
+# ---------------------------------------------------------------- prefix cache
+# The prefix index's model is pinned against facts that do not come from the
+# model's own trie: a brute-force longest common page prefix over every token
+# list inserted so far, the token content each physical page really holds (a
+# shared page must hold the query's tokens), conservation of references, and a
+# hand-worked LRU order.
+
+def _fill(m, content, seq, toks):
+    """Appends toks to seq and records each touched page's token content."""
+    P = m.page_size
+    L = m.length[seq]
+    _, pair = m.seq_append(seq, len(toks))
+    if pair is not None:
+        content[pair[1]] = content[pair[0]]
+    prev = list(content.get("seq", {}).get(seq, []))[:L]   # ids are reused after a free
+    assert len(prev) == L
+    allt = prev + list(toks)
+    content.setdefault("seq", {})[seq] = allt
+    for j in range(L // P, -(-len(allt) // P)):
+        content[m.pages[seq][j]] = tuple(allt[j * P:(j + 1) * P])
+
+
+def _prefix_invariants(m):
+    count = {}
+    for pages in m.pages.values():
+        for p in pages:
+            count[p] = count.get(p, 0) + 1
+    trie_pages = [v[2] for v in m.trie.values()]
+    assert len(set(trie_pages)) == len(trie_pages)          # a page is cached once
+    for p in trie_pages:
+        count[p] = count.get(p, 0) + 1
+    for p in range(m.num_pages):
+        assert m.ref[p] == count.get(p, 0)
+    assert sorted(m.free) == [p for p in range(m.num_pages) if count.get(p, 0) == 0]
+
+
+def test_prefix_match_is_the_longest_cached_page_prefix():
+    rng = np.random.default_rng(21)
+    P = 4
+    m = oracle.AllocatorModel(400, P, rng.permutation(400))
+    content = {}
+    # three documents sharing a 12-token head, two of them a further 8 tokens
+    head = list(rng.integers(0, 50, 12))
+    docs = [head + list(rng.integers(0, 50, 30)),
+            head + list(rng.integers(0, 50, 30)),
+            list(rng.integers(0, 50, 42))]
+    docs[1][12:20] = docs[0][12:20]
+    inserted = []
+    for _ in range(30):
+        d = docs[int(rng.integers(3))]
+        n = int(rng.integers(0, len(d) + 1))
+        s = m.seq_new()
+        if n:
+            _fill(m, content, s, d[:n])
+        cut = int(rng.integers(0, n + 1))
+        m.prefix_insert(s, d[:cut])
+        inserted.append(d[:cut // P * P])
+        if rng.random() < 0.5:
+            m.seq_free(s)
+        _prefix_invariants(m)
+    for _ in range(60):
+        d = docs[int(rng.integers(3))]
+        q = d[:int(rng.integers(0, len(d) + 1))]
+        if rng.random() < 0.3 and q:
+            q = list(q)
+            q[int(rng.integers(len(q)))] = 99          # a token no document holds
+        best = 0
+        for t in inserted:
+            j = 0
+            while (j + 1) * P <= min(len(t), len(q)) and t[j * P:(j + 1) * P] == q[j * P:(j + 1) * P]:
+                j += 1
+            best = max(best, j * P)
+        s, matched = m.prefix_match(q)
+        assert matched == best and m.length[s] == best
+        for j, p in enumerate(m.pages[s]):
+            assert content[p] == tuple(q[j * P:(j + 1) * P])
+        _prefix_invariants(m)
+        if rng.random() < 0.5:
+            m.seq_free(s)
+
+
+def test_prefix_eviction_order_is_least_recently_used():
+    m = oracle.AllocatorModel(16, 2)        # pages handed out 0, 1, 2, ...
+    seqs = {}
+    for name, toks in [("a", [1, 2, 3, 4]), ("b", [5, 6, 7, 8]), ("c", [9, 10])]:
+        s = m.seq_new()
+        m.seq_append(s, len(toks))
+        m.prefix_insert(s, toks)
+        seqs[name] = s
+    # a holds pages 0, 1; b holds 2, 3; c holds 4
+    for s in seqs.values():
+        m.seq_free(s)
+    assert m.prefix_pages() == 5 and len(m.free) == 11
+    t, _ = m.prefix_match([1, 2, 3, 4, 0, 0])    # a's path becomes the newest
+
+    def evict_one():
+        before = set(m.free)
+        assert m.prefix_evict(1) == 1
+        return (set(m.free) - before).pop()
+
+    # b's leaf, then b's head (a leaf now, stamped with b), then c
+    assert [evict_one() for _ in range(3)] == [3, 2, 4]
+    assert m.prefix_evict(1) == 0                # a's pages are held by t
+    m.seq_free(t)
+    assert [evict_one() for _ in range(2)] == [1, 0]
+    assert m.prefix_evict(1) == 0 and m.prefix_pages() == 0
+
+
+def test_prefix_cache_never_evicts_a_page_in_use():
+    m = oracle.AllocatorModel(12, 4)
+    a = m.seq_new()
+    m.seq_append(a, 16)
+    m.prefix_insert(a, list(range(16)))
+    b, n = m.prefix_match(list(range(8)) + [7, 7, 7, 7])
+    assert n == 8 and m.pages[b] == m.pages[a][:2]
+    m.seq_free(a)
+    assert m.prefix_evict(10) == 2               # only a's last two pages
+    assert m.prefix_pages() == 2
+    assert m.prefix_capacity(0) == 0 and m.prefix_pages() == 2
+    m.seq_free(b)
+    assert m.prefix_pages() == 2                 # freeing b does not evict by itself
+    assert m.prefix_capacity(1) == 1 and m.prefix_pages() == 1
+    _prefix_invariants(m)
+    assert m.prefix_capacity(0) == 1 and len(m.free) == 12
+
+
+def test_prefix_capacity_bounds_the_cache_on_insert():
+    m = oracle.AllocatorModel(20, 2)
+    m.prefix_capacity(3)
+    for k in range(4):
+        s = m.seq_new()
+        m.seq_append(s, 4)
+        m.prefix_insert(s, [10 * k, 1, 2, 3])
+        m.seq_free(s)
+        assert m.prefix_pages() <= 3
+        _prefix_invariants(m)
+    # the newest path survives whole; older leaves went first
+    _, n = m.prefix_match([30, 1, 2, 3])
+    assert n == 4
+
+
+def test_prefix_insert_rejects_a_page_cached_under_other_tokens():
+    m = oracle.AllocatorModel(8, 2)
+    a = m.seq_new()
+    m.seq_append(a, 4)
+    m.prefix_insert(a, [1, 2, 3, 4])
+    snap = (list(m.free), list(m.ref), dict(m.trie), m.clock)
+    with pytest.raises(oracle.InvalidError):
+        m.prefix_insert(a, [1, 2, 9, 9])         # a's second page is cached as [3, 4]
+    with pytest.raises(oracle.InvalidError):
+        m.prefix_insert(a, [1, 2, 3, 4, 5])      # more tokens than a holds
+    assert (m.free, m.ref, dict(m.trie), m.clock) == snap
+
+
+def test_compaction_keeps_the_prefix_cache_consistent():
+    rng = np.random.default_rng(22)
+    P = 4
+    m = oracle.AllocatorModel(40, P, rng.permutation(40))
+    content = {}
+    doc = list(rng.integers(0, 30, 40))
+    for n in [40, 13, 27, 6]:
+        s = m.seq_new()
+        _fill(m, content, s, doc[:n] if n != 13 else list(rng.integers(0, 30, 13)))
+        m.prefix_insert(s, content["seq"][s])
+        if n != 27:
+            m.seq_free(s)
+    pairs = m.compact()
+    snap = {}
+    for sp, dp in pairs:
+        snap[dp] = content[sp]
+    content.update(snap)
+    n_live = sum(1 for r in m.ref if r > 0)
+    assert all(v[2] < n_live for v in m.trie.values())
+    _prefix_invariants(m)
+    s, matched = m.prefix_match(doc)
+    assert matched == 40
+    for j, p in enumerate(m.pages[s]):
+        assert content[p] == tuple(doc[j * P:(j + 1) * P])
