@@ -397,6 +397,102 @@ def bench_swap_compact(args, pa, torch, W):
     return res
 
 
+def bench_prefix(args, pa, torch, W):
+    """Admission of 16 requests that share an 8192-token prefix, each with a
+    private 1024-token suffix (GQA 32/8, D 128, pages of 128 tokens), in
+    512-token ubatches of reshape_and_cache + pa_prefill.  With the prefix cache,
+    request 0 prefills everything and is inserted, and requests 1..15 match the
+    prefix and prefill only their suffix; without it every request prefills all
+    of its tokens.  Pool work (match, append, insert, tables) is host time,
+    measured apart; each arm's launches are one HIP graph.  Both arms end with the
+    same ubatch of the last request (same queries, lengths and K/V, different
+    pages), so their outputs must be bitwise equal."""
+    dev = torch.device("cuda:0")
+    n_req, Lp, Ls, P, chunk = 16, 8192, 1024, 128, 512
+    Hq, Hkv, D, N, vocab = 32, 8, 128, 2048, 4096
+    L = Lp + Ls
+    rng = np.random.default_rng(185010)
+    prefix = rng.integers(0, vocab, Lp)
+    tokens = [np.concatenate([prefix, rng.integers(0, vocab, Ls)]) for _ in range(n_req)]
+    tkv = W.token_kv(185011, vocab, L, Hkv, D)
+    ek, ev_, pk, pv = (torch.from_numpy(x).to(dev) for x in (tkv.ek, tkv.ev, tkv.pk, tkv.pv))
+    tok_d = torch.from_numpy(np.stack(tokens)).to(dev)
+    kn = (ek[tok_d] + pk[None]).half()               # [n_req][L][Hkv][D], as TokenKV.kv
+    vn = (ev_[tok_d] + pv[None]).half()
+    del ek, ev_, pk, pv
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(185012)
+    qd = torch.randn((n_req, L, Hq, D), generator=gen, device=dev, dtype=torch.float32)
+    kd = torch.full((N, Hkv, P, D), float("nan"), dtype=torch.float16, device=dev)
+    vd = torch.full((N, Hkv, D, P), float("nan"), dtype=torch.float16, device=dev)
+    desc = pa.cache_desc(kd, vd)
+    free_order = rng.permutation(N)
+    scale = float(W.fp32_scale(D))
+
+    def plan(use_prefix):
+        pool = pa.Pool(N, P, free_order)
+        launches, host_s, pairs = [], 0.0, 0
+        for r in range(n_req):
+            t0 = time.perf_counter()
+            if use_prefix:
+                s, m = pool.prefix_match(tokens[r])
+            else:
+                s, m = pool.seq_new(), 0
+            host_s += time.perf_counter() - t0
+            for p0 in range(m, L, chunk):
+                n = min(chunk, L - p0)
+                t0 = time.perf_counter()
+                slots, cow = pool.seq_append(s, n)
+                bt, _ = pool.block_tables([s], L // P)
+                host_s += time.perf_counter() - t0
+                assert cow is None
+                row = np.zeros(n, dtype=np.int32)
+                kvl = np.full(n, p0 + n, dtype=np.int32)
+                pos = np.arange(p0, p0 + n, dtype=np.int32)
+                pairs += W.prefill_pairs(kvl, pos)
+                launches.append(dict(r=r, p0=p0, n=n, slots=torch.from_numpy(slots).to(dev),
+                                     bt=torch.from_numpy(bt).to(dev), row=torch.from_numpy(row).to(dev),
+                                     kvl=torch.from_numpy(kvl).to(dev), pos=torch.from_numpy(pos).to(dev),
+                                     row_h=row, kvl_h=kvl, pos_h=pos,
+                                     ws=pa.pa_prefill_workspace_bytes(desc, Hq, row, kvl, pos, 0)))
+            if use_prefix:
+                t0 = time.perf_counter()
+                pool.prefix_insert(s, tokens[r])
+                host_s += time.perf_counter() - t0
+        return launches, N - pool.stats()[0], host_s, pairs
+
+    res = {"requests": n_req, "shared_prefix": Lp, "private_suffix": Ls, "ubatch": chunk}
+    outs = {}
+    for name, use in (("with_cache", True), ("without_cache", False)):
+        launches, pages, host_s, pairs = plan(use)
+        ws = torch.zeros(max(max(x["ws"] for x in launches), 1), dtype=torch.uint8, device=dev)
+        out = torch.empty(chunk, Hq, D, dtype=torch.float32, device=dev)
+
+        def one_pass(stream, launches=launches, ws=ws, out=out):
+            for x in launches:
+                r, p0, n = x["r"], x["p0"], x["n"]
+                pa.pa_reshape_and_cache(kd, vd, kn[r, p0:p0 + n], vn[r, p0:p0 + n], x["slots"],
+                                        stream=stream)
+                pa.pa_prefill(qd[r, p0:p0 + n], kd, vd, x["bt"], x["row"], x["kvl"], x["pos"], scale,
+                              token_row_host=x["row_h"], token_kv_len_host=x["kvl_h"],
+                              token_pos_host=x["pos_h"], out=out[:n], workspace=ws, stream=stream)
+
+        ms = _time_graph(torch, one_pass, 1)
+        outs[name] = out.clone()
+        flops = W.attention_flops(pairs, Hq, D)
+        res[name] = {"ms": round(ms, 3), "ubatches": len(launches),
+                     "tokens_prefilled": int(sum(x["n"] for x in launches)),
+                     "pages_in_use": int(pages), "host_ms_pool_calls": round(host_s * 1e3, 3),
+                     "attention_tflop": round(flops / 1e12, 3),
+                     "tflops": round(flops / (ms * 1e-3) / 1e12, 1)}
+        del ws
+    res["speedup"] = round(res["without_cache"]["ms"] / res["with_cache"]["ms"], 2)
+    res["pages_saved"] = res["without_cache"]["pages_in_use"] - res["with_cache"]["pages_in_use"]
+    res["last_ubatch_bitwise_equal"] = bool(torch.equal(outs["with_cache"].view(torch.int32),
+                                                        outs["without_cache"].view(torch.int32)))
+    return res
+
+
 def cpu_baseline_decode(c, oracle):
     t0 = time.perf_counter()
     oracle.paged_decode(c.q, c.k_pool, c.v_pool, c.block_tables, c.kv_lens, c.scale)
@@ -442,6 +538,7 @@ def main():
     ap.add_argument("--no-unified", action="store_true",
                     help="skip the paged-vs-unified-span comparison")
     ap.add_argument("--no-swap", action="store_true", help="skip the swap / compaction measurement")
+    ap.add_argument("--no-prefix", action="store_true", help="skip the prefix-cache admission measurement")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device-to-device copy of this many bytes (3 times): the "
                          "known-size kernel that calibrates the FETCH_SIZE / WRITE_SIZE counters")
@@ -492,6 +589,12 @@ def main():
         log("swap / compaction")
         swp = bench_swap_compact(args, pa, torch, W)
         log(f"swap / compaction: {json.dumps(swp)}")
+
+    pfx = None
+    if not args.no_prefix:
+        log("prefix cache: 16 requests sharing an 8192-token prefix, with and without the cache")
+        pfx = bench_prefix(args, pa, torch, W)
+        log(f"prefix cache: {json.dumps(pfx)}")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -559,6 +662,8 @@ def main():
         result["unified_vs_paged"] = uni
     if swp is not None:
         result.update(swp)
+    if pfx is not None:
+        result["prefix_cache"] = pfx
     print(json.dumps(result), flush=True)
 
 

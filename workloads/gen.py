@@ -402,3 +402,38 @@ def unified_pairs(span, n_tokens_real) -> int:
 
 
 __all__ += ["unified_view", "unified_decode_bytes", "unified_pairs"]
+
+
+# ---------------------------------------------------------------- token-keyed K/V
+
+@dataclass
+class TokenKV:
+    """A seeded stand-in for a model's K/V projections in which a token's K and V
+    depend only on its id and its position: two requests whose leading tokens are
+    equal then hold equal K/V there, which is what lets one reuse the other's
+    cached pages.  Tables are float32; ``kv`` rounds their sum to float16."""
+    ek: np.ndarray      # float32 [vocab][Hkv][D]
+    ev: np.ndarray
+    pk: np.ndarray      # float32 [max_pos][Hkv][D]
+    pv: np.ndarray
+
+    def kv(self, tokens, positions):
+        t = np.asarray(tokens, dtype=np.int64)
+        p = np.asarray(positions, dtype=np.int64)
+        k = (self.ek[t] + self.pk[p]).astype(np.float16)
+        v = (self.ev[t] + self.pv[p]).astype(np.float16)
+        return k, v
+
+
+def token_kv(seed, vocab, max_pos, n_kv_heads=8, head_dim=128) -> TokenKV:
+    """Draw order: token K, token V, position K, position V; N(0,1)*0.8 for the
+    token part and N(0,1)*0.6 for the position part (unit variance overall)."""
+    rng = np.random.default_rng(seed)
+    ek = _normal(rng, (vocab, n_kv_heads, head_dim), 0.8)
+    ev = _normal(rng, (vocab, n_kv_heads, head_dim), 0.8)
+    pk = _normal(rng, (max_pos, n_kv_heads, head_dim), 0.6)
+    pv = _normal(rng, (max_pos, n_kv_heads, head_dim), 0.6)
+    return TokenKV(ek, ev, pk, pv)
+
+
+__all__ += ["TokenKV", "token_kv"]
