@@ -314,7 +314,9 @@ size_t pa_prefill_workspace_bytes(const pa_cache_desc* desc, int32_t n_tokens, i
  * t < min(token_kv_len[i], token_pos[i] + 1) of that row.
  *   q            device fp32 [n_tokens][n_q_heads][head_dim]; rounded to
  *                binary16 (nearest even) for the matrix products, which
- *                accumulate in fp32
+ *                accumulate in fp32; a split KV range's partial output
+ *                (normalised by its own row sum) is rounded to binary16
+ *                before the splits are combined in fp32
  *   out          device fp32 [n_tokens][n_q_heads][head_dim]
  *   block_tables device int32 [n_rows][max_pages]
  *   token_row, token_kv_len, token_pos   device int32 [n_tokens]

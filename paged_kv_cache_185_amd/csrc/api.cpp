@@ -175,13 +175,14 @@ pa_status finish_prefill_plan(const pa_cache_desc* d, int32_t kv_splits, int64_t
     if (plan->max_splits > 1) {
         // counters first (zero-filled region shared with pa_decode's
         // convention), then per (tile, KV head, split) slot the (m, l) pairs
-        // and the accumulators of every lane of the workgroup
+        // and the binary16 normalised outputs of every lane of the workgroup
         const size_t groups = plan->tiles.size() * (size_t)d->n_kv_heads;
         const size_t slots = groups * plan->max_splits;
         const size_t threads = (size_t)prefill_threads();
         plan->ml_off = align256(std::max<size_t>(kDecodeCounterBytes, groups * 4));
         plan->acc_off = plan->ml_off + align256(slots * threads * 2 * 4);
-        plan->bytes = plan->acc_off + align256(slots * threads * (size_t)d->head_dim / 2 * 4);
+        // per lane: head_dim/2 outputs in binary16 (head_dim bytes)
+        plan->bytes = plan->acc_off + align256(slots * threads * (size_t)d->head_dim);
     }
     return PA_OK;
 }

@@ -93,8 +93,8 @@ struct PrefillArgs {
     // split partials (null when no tile splits), slot = group*max_splits+split
     // with group = tile*Hkv + kvh over all tiles of the call:
     int32_t* counters;  // [groups], zero between calls
-    float* part_ml;     // [slot][threads][2]  (m, half-wave l)
-    float* part_acc;    // [slot][D/8][threads][4]  accumulators in lane order
+    float* part_ml;     // [slot][threads][2]  (m, the column l)
+    float* part_acc;    // [slot][D/16][threads] 16-byte pieces of binary16 o = acc / l, lane order
     int32_t n_tokens;
     int32_t max_pages;
     int32_t n_q_heads;

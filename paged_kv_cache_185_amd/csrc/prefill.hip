@@ -635,12 +635,16 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, Til
     }
 
     // ---- split tile: fused log-sum-exp combine.  Each split stores its
-    // partial (m, half-wave l, unnormalised acc) in the lanes' register order
-    // with device-scope stores (written through past the per-XCD L2s), waits
-    // until they are acknowledged, and bumps the (tile, KV head) counter; the
-    // split that brings it to n_splits reads the others' partials with
-    // device-scope loads, writes the output and zeroes the counter again.
-    constexpr int NV = 4 * DB;   // 16-byte accumulator pieces per lane
+    // partial as the normalised output o = acc / l rounded to binary16 (its
+    // magnitude is bounded by |V|, so the rounding costs about 2^-11
+    // relative, and it halves the bytes written and read back) plus (m, l)
+    // in fp32, in the lanes' register order, with device-scope stores
+    // (written through past the per-XCD L2s); waits until they are
+    // acknowledged, and bumps the (tile, KV head) counter.  The split that
+    // brings it to n_splits reads the others' partials with device-scope
+    // loads and forms sum(w l o) / sum(w l), w = exp2(m - max m), folding the
+    // splits in ascending order; it writes the output and zeroes the counter.
+    constexpr int NP = 2 * DB;   // 16-byte pieces (8 halves) of binary16 output per lane
     const int64_t grp = (int64_t)a.group_base + (int64_t)tile_idx * Hkv + kvh;
     const int64_t slot0 = grp * a.max_splits;
     const int nsp = tile.n_splits;
@@ -648,24 +652,30 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, Til
     // 16) makes the accesses coherent across the XCDs' L2s
     constexpr int kCoherent = 16;
     const __amdgpu_buffer_rsrc_t racc = __builtin_amdgcn_make_buffer_rsrc(
-        a.part_acc + slot0 * NV * kThreads * 4, 0, 0x7fffffff, 0x00020000);
+        a.part_acc + slot0 * NP * kThreads * 4, 0, 0x7fffffff, 0x00020000);
     const __amdgpu_buffer_rsrc_t rml = __builtin_amdgcn_make_buffer_rsrc(
         a.part_ml + slot0 * kThreads * 2, 0, 0x7fffffff, 0x00020000);
-    auto acc_off = [&](int sp, int j) __attribute__((always_inline)) { return ((sp * NV + j) * kThreads + tid) * 16; };
+    auto acc_off = [&](int sp, int j) __attribute__((always_inline)) { return ((sp * NP + j) * kThreads + tid) * 16; };
     auto ml_off = [&](int sp) __attribute__((always_inline)) { return (sp * kThreads + tid) * 8; };
-    // own partial: 8-byte device-scope stores (sc1, like the loads below)
     {
-        uint64_t* pacc = reinterpret_cast<uint64_t*>(a.part_acc + slot0 * NV * kThreads * 4);
+        // the column's total l adds the partner half-wave's
+        const float l_col = pair_sum(l_run);
+        const float inv = l_col > 0.0f ? 1.0f / l_col : 0.0f;
+        uint64_t* pacc = reinterpret_cast<uint64_t*>(a.part_acc + slot0 * NP * kThreads * 4);
 #pragma unroll
-        for (int j = 0; j < NV; ++j) {
-            const f32x16& x = acc[j >> 2];
-            const int r = 4 * (j & 3);
+        for (int j = 0; j < NP; ++j) {
+            const f32x16& x = acc[j >> 1];
+            const int r0 = 8 * (j & 1);
+            f16x8 h;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) h[e] = (_Float16)(x[r0 + e] * inv);
+            const u32x4 u = __builtin_bit_cast(u32x4, h);
             uint64_t* pp = pacc + acc_off(split, j) / 8;
-            store_device2(pp, x[r], x[r + 1]);
-            store_device2(pp + 1, x[r + 2], x[r + 3]);
+            store_device2(pp, __uint_as_float(u[0]), __uint_as_float(u[1]));
+            store_device2(pp + 1, __uint_as_float(u[2]), __uint_as_float(u[3]));
         }
         store_device2(reinterpret_cast<uint64_t*>(a.part_ml + slot0 * kThreads * 2) + ml_off(split) / 8,
-                      m_run, l_run);
+                      m_run, l_col);
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -674,8 +684,30 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, Til
     if (!sm.last) return;
     if (tid == 0) __hip_atomic_store(a.counters + grp, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
-    // maximum over the splits' m, four splits' loads in flight at a time
     float M = -INFINITY;
+    float L = 0.0f;
+    auto fold = [&](const u32x2& ml, const u32x4 (&x)[NP]) __attribute__((always_inline)) {
+        const float w = M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(__uint_as_float(ml[0]) - M);
+        const float wl = w * __uint_as_float(ml[1]);
+        L += wl;
+#pragma unroll
+        for (int j = 0; j < NP; ++j) {
+            const f16x8 h = __builtin_bit_cast(f16x8, x[j]);
+            f32x16& t = acc[j >> 1];
+            const int r0 = 8 * (j & 1);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) t[r0 + e] = __builtin_fmaf(wl, (float)h[e], t[r0 + e]);
+        }
+    };
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[db][r] = 0.0f;
+    // the maximum over the splits' m (four splits' loads in flight at a
+    // time), then the splits folded in ascending order, two per round trip,
+    // this one's own partial re-read like the others, so the result does not
+    // depend on which split finishes last; a column that no split saw
+    // (padding) keeps M = -inf: weights 0
 #pragma unroll 1
     for (int sp0 = 0; sp0 < nsp; sp0 += 4) {
         u32x2 ml[4];
@@ -685,33 +717,21 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, Til
 #pragma unroll
         for (int u = 0; u < 4; ++u) M = fmaxf(M, __uint_as_float(ml[u][0]));
     }
-    // fold the splits in ascending order, this one's own partial re-read
-    // like the others, so the result does not depend on which split finishes
-    // last; a column that no split saw (padding) keeps M = -inf: weights 0.
-    // All of one split's loads are issued before any of them is used.
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[db][r] = 0.0f;
-    float L = 0.0f;
 #pragma unroll 1
-    for (int sp = 0; sp < nsp; ++sp) {
-        u32x4 x[NV];
-        const u32x2 ml = __builtin_amdgcn_raw_buffer_load_b64(rml, ml_off(sp), 0, kCoherent);
+    for (int sp = 0; sp < nsp; sp += 2) {
+        const int sp1 = min(sp + 1, nsp - 1);
+        u32x4 x0[NP], x1[NP];
+        const u32x2 ml0 = __builtin_amdgcn_raw_buffer_load_b64(rml, ml_off(sp), 0, kCoherent);
+        const u32x2 ml1 = __builtin_amdgcn_raw_buffer_load_b64(rml, ml_off(sp1), 0, kCoherent);
 #pragma unroll
-        for (int j = 0; j < NV; ++j) x[j] = __builtin_amdgcn_raw_buffer_load_b128(racc, acc_off(sp, j), 0, kCoherent);
-        const float w = M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(__uint_as_float(ml[0]) - M);
-        L = __builtin_fmaf(w, __uint_as_float(ml[1]), L);
+        for (int j = 0; j < NP; ++j) x0[j] = __builtin_amdgcn_raw_buffer_load_b128(racc, acc_off(sp, j), 0, kCoherent);
 #pragma unroll
-        for (int j = 0; j < NV; ++j) {
-            f32x16& t = acc[j >> 2];
-            const int r = 4 * (j & 3);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) t[r + e] = __builtin_fmaf(w, __uint_as_float(x[j][e]), t[r + e]);
-        }
+        for (int j = 0; j < NP; ++j) x1[j] = __builtin_amdgcn_raw_buffer_load_b128(racc, acc_off(sp1, j), 0, kCoherent);
+        fold(ml0, x0);
+        if (sp + 1 < nsp) fold(ml1, x1);
     }
-    const float l_tot = pair_sum(L);
-    if (tok >= 0) write_out(l_tot);
+    // L is already the column's total (each split stored its column l)
+    if (tok >= 0) write_out(L);
 }
 
 template <int D, bool ONE_PAGE, bool UNIFIED>

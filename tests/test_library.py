@@ -210,7 +210,9 @@ def test_workspace_sizes():
     kv = np.full(n, 16384, np.int32)
     pos = np.arange(15872, 16384, dtype=np.int32)
     assert pa.pa_prefill_workspace_bytes(d, 32, row, kv, pos, 1) == 0
-    assert pa.pa_prefill_workspace_bytes(d, 32, row, kv, pos, 4) >= n * 32 * 4 * 130 * 4
+    # each (token, head, split) row keeps its normalised output in binary16
+    # (2 * head_dim bytes) and the (m, l) pairs of its two lanes in fp32
+    assert pa.pa_prefill_workspace_bytes(d, 32, row, kv, pos, 4) >= n * 32 * 4 * (2 * 128 + 16)
 
 
 @pytest.mark.parametrize("seed", [0, 1, 2])
