@@ -281,9 +281,12 @@ size_t pa_decode_workspace_bytes(const pa_cache_desc* desc, int32_t n_seqs, int3
  *   kv_lens      device int32 [n_seqs]; each in [1, max_pages*page_size]
  *   kv_lens_host host copy of kv_lens or NULL; used only to size the split
  *   scale        softmax scale (e.g. 1/sqrt(head_dim))
- *   partition_tokens  0 = choose; -1 = one pass per sequence (no split);
- *                >0 = split every sequence into partitions of this many
- *                tokens (a multiple of 256), combined by a log-sum-exp reduce.
+ *   partition_tokens  0 = choose (about one workgroup per compute unit
+ *                when all lengths are equal, partitions of at most 4096
+ *                tokens otherwise; needs kv_lens_host); -1 = one pass per
+ *                sequence (no split); >0 = split every sequence into
+ *                partitions of this many tokens (a multiple of 256),
+ *                combined by a log-sum-exp reduce.
  * The result does not depend on the physical page ids, and cells past a
  * sequence's length are never used, whatever they hold. */
 pa_status pa_decode(const pa_cache_desc* desc, const void* k_cache, const void* v_cache,

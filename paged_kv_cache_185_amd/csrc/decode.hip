@@ -76,9 +76,15 @@ template <int D>
 __global__ __launch_bounds__(256, 2) void decode_partition_kernel(DecodeArgs a) {
     constexpr int KS = D / 32;
     constexpr int NB = D / 16;
-    const int part = blockIdx.x;
-    const int kvh = blockIdx.y;
-    const int seq = blockIdx.z;
+    // workgroups are numbered KV-head fastest, then sequence, then partition:
+    // the dispatcher deals consecutive workgroups to the XCDs in turn, so
+    // every XCD gets an even share of each partition index (with variable
+    // lengths the high partitions exist only for long sequences), and the
+    // empty partitions of short sequences come last
+    const int kvh = blockIdx.x % a.n_kv_heads;
+    const int rest = blockIdx.x / a.n_kv_heads;
+    const int seq = rest % a.n_seqs;
+    const int part = rest / a.n_seqs;
     const int L = a.kv_lens[seq];
     const int t0 = part * a.partition_tokens;
     if (t0 >= L) return;
@@ -356,12 +362,33 @@ __global__ __launch_bounds__(256, 2) void decode_partition_kernel(DecodeArgs a) 
                 }
             }
         } else {
+            // the maximum first, then the fold in ascending partition order,
+            // kFast partitions' loads in flight per round trip
             float M = -INFINITY;
-            for (int p = 0; p < np; ++p) M = fmaxf(M, load_device(a.part_m + base + p));
-            for (int p = 0; p < np; ++p) {
-                const float f = __builtin_amdgcn_exp2f(load_device(a.part_m + base + p) - M);
-                num += f * load_device(a.part_acc + (base + p) * D + d);
-                den += f * load_device(a.part_l + base + p);
+            for (int p0 = 0; p0 < np; p0 += kFast) {
+                float pm[kFast];
+#pragma unroll
+                for (int p = 0; p < kFast; ++p) pm[p] = load_device(a.part_m + base + min(p0 + p, np - 1));
+#pragma unroll
+                for (int p = 0; p < kFast; ++p) M = fmaxf(M, pm[p]);
+            }
+            for (int p0 = 0; p0 < np; p0 += kFast) {
+                float pm[kFast], pl[kFast], px[kFast];
+#pragma unroll
+                for (int p = 0; p < kFast; ++p) {
+                    const int q = min(p0 + p, np - 1);
+                    pm[p] = load_device(a.part_m + base + q);
+                    pl[p] = load_device(a.part_l + base + q);
+                    px[p] = load_device(a.part_acc + (base + q) * D + d);
+                }
+#pragma unroll
+                for (int p = 0; p < kFast; ++p) {
+                    if (p0 + p < np) {
+                        const float f = __builtin_amdgcn_exp2f(pm[p] - M);
+                        num += f * px[p];
+                        den += f * pl[p];
+                    }
+                }
             }
         }
         a.out[((int64_t)seq * a.n_q_heads + qh) * D + d] = num / den;
@@ -379,7 +406,7 @@ int decode_page_table_entries(int partition_tokens, int page_size) {
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
-    const dim3 grid((unsigned)a.n_part, (unsigned)a.n_kv_heads, (unsigned)a.n_seqs);
+    const dim3 grid((unsigned)((int64_t)a.n_part * a.n_kv_heads * a.n_seqs));
     const size_t lds = sizeof(int32_t) * (size_t)decode_page_table_entries(a.partition_tokens, a.page_size);
     if (a.head_dim == 128)
         hipLaunchKernelGGL(decode_partition_kernel<128>, grid, dim3(256), lds, stream, a);
