@@ -166,13 +166,23 @@ pa_status finish_prefill_plan(const pa_cache_desc* d, int32_t kv_splits, int64_t
     } else if (kv_splits > 1) {
         split_tokens = round_up(std::max<int64_t>((max_kv + kv_splits - 1) / kv_splits, 1), KT);
     } else {
-        // one 8-wave workgroup per compute unit (256 CUs): enough (tile, split)
-        // pairs per KV head to cover them, splits no shorter than 256 keys
-        const int64_t need = (256 + d->n_kv_heads - 1) / d->n_kv_heads;
-        if ((int64_t)plan->tiles.size() >= need)
+        // one 8-wave workgroup fits a compute unit (256 CUs): about 256 / Hkv
+        // (tile, split) pairs per KV head cover them, splits no shorter than
+        // 256 keys.  Each tile rounds its split count up, so the split is
+        // widened until the total stays within one workgroup per CU: a grid
+        // beyond that runs the excess as a second round of workgroups
+        const int64_t need = std::max<int64_t>(1, 256 / d->n_kv_heads);
+        if ((int64_t)plan->tiles.size() >= need) {
             split_tokens = round_up(std::max<int64_t>(max_kv, 1), KT);
-        else
+        } else {
             split_tokens = std::max<int64_t>(256, round_up((sum_kv + need - 1) / need, KT));
+            for (;;) {
+                int64_t pairs = 0;
+                for (const auto& t : plan->tiles) pairs += (t.kv_end + split_tokens - 1) / split_tokens;
+                if (pairs <= need || split_tokens >= max_kv) break;
+                split_tokens += KT;
+            }
+        }
     }
     split_tokens = std::min<int64_t>(split_tokens, round_up(std::max<int64_t>(max_kv, 1), KT));
     // the kernel stages one split's page ids in LDS: very long ranges are split
@@ -308,8 +318,7 @@ pa_status run_prefill_plan(const char* who, const pa_cache_desc* desc, const Pre
     for (int b = 0; b < n_tiles; b += kMaxTilesPerLaunch) {
         const int nb = std::min(kMaxTilesPerLaunch, n_tiles - b);
         a.group_base = b * desc->n_kv_heads;
-        hipError_t e = launch_prefill(a, plan.tiles.data() + b, nb, plan.max_splits,
-                                      (hipStream_t)stream);
+        hipError_t e = launch_prefill(a, plan.tiles.data() + b, nb, (hipStream_t)stream);
         if (e != hipSuccess) return hip_fail(who, e);
     }
     return PA_OK;

@@ -79,6 +79,7 @@ struct PrefillTile {
     int32_t min_vis;    // smallest visible length of any token in the tile
     int32_t n_splits;   // KV splits used by this tile (<= grid splits)
     int32_t dense;      // 1: the tile's tokens are first, first+1, ..., last
+    int32_t item0;      // first (tile, split) item of the tile in its launch (set at launch)
 };
 
 constexpr int kMaxTilesPerLaunch = 128;
@@ -125,7 +126,7 @@ int prefill_page_table_entries(int split_tokens, int page_size);
 constexpr int kPrefillMaxPageEntries = 8192;
 
 hipError_t launch_prefill(const PrefillArgs& a, const PrefillTile* tiles, int n_tiles,
-                          int grid_splits, hipStream_t stream);
+                          hipStream_t stream);
 
 // Zero the output rows of padding tokens (token_row < 0).
 hipError_t launch_zero_rows(float* out, const int32_t* token_row, int32_t n_tokens,

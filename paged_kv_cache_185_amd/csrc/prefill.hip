@@ -149,12 +149,21 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, Til
     constexpr int DB = D / 32;        // 32-row output blocks
     constexpr int CPR = D / 8;        // 16-byte chunks per K row
 
+    // the grid holds exactly the launch's (tile, split) items, numbered tile
+    // by tile, times the KV heads (KV head fastest): no workgroup is empty,
+    // so none holds a compute unit that a live one could use
     const int Hkv = a.n_kv_heads;
     const int kvh = blockIdx.x % Hkv;
-    const int rest = blockIdx.x / Hkv;
-    const int tile_idx = rest % a.n_tiles;
-    const int split = rest / a.n_tiles;
+    const int item = blockIdx.x / Hkv;
+    int lo = 0, hi = a.n_tiles - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (tl.t[mid].item0 <= item) lo = mid;
+        else hi = mid - 1;
+    }
+    const int tile_idx = lo;
     const PrefillTile tile = tl.t[tile_idx];
+    const int split = item - tile.item0;
     if (split >= tile.n_splits) return;
     const int kv_begin = split * a.split_tokens;
     const int kv_end = min(tile.kv_end, kv_begin + a.split_tokens);
@@ -776,14 +785,19 @@ int prefill_page_table_entries(int split_tokens, int page_size) {
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, const PrefillTile* tiles, int n_tiles,
-                          int grid_splits, hipStream_t stream) {
+                          hipStream_t stream) {
     if (n_tiles <= 0) return hipSuccess;
     if (n_tiles > kMaxTilesPerLaunch) return hipErrorInvalidValue;
     TileList tl;
-    for (int i = 0; i < n_tiles; ++i) tl.t[i] = tiles[i];
+    int items = 0;
+    for (int i = 0; i < n_tiles; ++i) {
+        tl.t[i] = tiles[i];
+        tl.t[i].item0 = items;
+        items += tiles[i].n_splits;
+    }
     PrefillArgs b = a;
     b.n_tiles = n_tiles;
-    const int n_items = n_tiles * grid_splits * a.n_kv_heads;
+    const int n_items = items * a.n_kv_heads;
     const size_t lds = sizeof(int32_t) * (size_t)prefill_page_table_entries(a.split_tokens, a.page_size);
     if (a.head_dim == 128) return launch_prefill_d<128>(b, tl, n_items, lds, stream);
     return launch_prefill_d<64>(b, tl, n_items, lds, stream);
