@@ -156,42 +156,59 @@ struct PrefillPlan {
     size_t ml_off = 0, acc_off = 0, bytes = 0;
 };
 
-// KV split size, per-tile split counts and workspace layout, given the tiles.
+// Per-tile KV split lengths and counts and the workspace layout, given the tiles.
 pa_status finish_prefill_plan(const pa_cache_desc* d, int32_t kv_splits, int64_t sum_kv,
                               int64_t max_kv, PrefillPlan* plan) {
+    (void)sum_kv;
     const int64_t KT = kPrefillKvTile;
-    int64_t split_tokens;
-    if (kv_splits == 1) {
-        split_tokens = round_up(std::max<int64_t>(max_kv, 1), KT);
-    } else if (kv_splits > 1) {
-        split_tokens = round_up(std::max<int64_t>((max_kv + kv_splits - 1) / kv_splits, 1), KT);
-    } else {
-        // one 8-wave workgroup fits a compute unit (256 CUs): about 256 / Hkv
-        // (tile, split) pairs per KV head cover them, splits no shorter than
-        // 256 keys.  Each tile rounds its split count up, so the split is
-        // widened until the total stays within one workgroup per CU: a grid
-        // beyond that runs the excess as a second round of workgroups
-        const int64_t need = std::max<int64_t>(1, 256 / d->n_kv_heads);
-        if ((int64_t)plan->tiles.size() >= need) {
-            split_tokens = round_up(std::max<int64_t>(max_kv, 1), KT);
-        } else {
-            split_tokens = std::max<int64_t>(256, round_up((sum_kv + need - 1) / need, KT));
-            for (;;) {
-                int64_t pairs = 0;
-                for (const auto& t : plan->tiles) pairs += (t.kv_end + split_tokens - 1) / split_tokens;
-                if (pairs <= need || split_tokens >= max_kv) break;
-                split_tokens += KT;
-            }
-        }
-    }
-    split_tokens = std::min<int64_t>(split_tokens, round_up(std::max<int64_t>(max_kv, 1), KT));
     // the kernel stages one split's page ids in LDS: very long ranges are split
     const int64_t lds_cap = (int64_t)(kPrefillMaxPageEntries - 1) * d->page_size / KT * KT;
-    split_tokens = std::min(split_tokens, lds_cap);
-    plan->split_tokens = (int32_t)split_tokens;
+    auto kv_of = [](const PrefillTile& t) { return std::max<int64_t>(t.kv_end, 1); };
+    if (kv_splits >= 1) {
+        // the same split length for every tile
+        int64_t split = kv_splits == 1 ? round_up(std::max<int64_t>(max_kv, 1), KT)
+                                       : round_up(std::max<int64_t>((max_kv + kv_splits - 1) / kv_splits, 1), KT);
+        split = std::min(split, lds_cap);
+        for (auto& t : plan->tiles) {
+            t.split_len = (int32_t)split;
+            t.n_splits = (int32_t)((kv_of(t) + split - 1) / split);
+        }
+    } else {
+        // one 8-wave workgroup fits a compute unit (256 CUs): at most
+        // 256 / Hkv (tile, split) pairs per KV head keep the grid to one
+        // round of workgroups (the excess of a larger grid runs as a second
+        // round).  The pairs go one at a time to the tile whose splits are
+        // longest, splits no shorter than 256 keys; each tile's range is
+        // then cut into equal splits, so no tile carries a short remainder
+        // split beside full ones.
+        const int64_t need = std::max<int64_t>(1, 256 / d->n_kv_heads);
+        const size_t n = plan->tiles.size();
+        std::vector<int64_t> cnt(n);
+        int64_t pairs = 0;
+        for (size_t i = 0; i < n; ++i) {
+            cnt[i] = (kv_of(plan->tiles[i]) + lds_cap - 1) / lds_cap;
+            pairs += cnt[i];
+        }
+        auto len = [&](size_t i, int64_t c) { return (kv_of(plan->tiles[i]) + c - 1) / c; };
+        while (pairs < need) {
+            size_t best = n;
+            for (size_t i = 0; i < n; ++i)
+                if (best == n || len(i, cnt[i]) > len(best, cnt[best])) best = i;
+            if (best == n || len(best, cnt[best] + 1) < 256) break;
+            ++cnt[best];
+            ++pairs;
+        }
+        for (size_t i = 0; i < n; ++i) {
+            auto& t = plan->tiles[i];
+            const int64_t split = std::min(lds_cap, round_up(len(i, cnt[i]), KT));
+            t.split_len = (int32_t)split;
+            t.n_splits = (int32_t)((kv_of(t) + split - 1) / split);
+        }
+    }
+    plan->split_tokens = 0;
     plan->max_splits = 1;
-    for (auto& t : plan->tiles) {
-        t.n_splits = (int32_t)((t.kv_end + split_tokens - 1) / split_tokens);
+    for (const auto& t : plan->tiles) {
+        plan->split_tokens = std::max(plan->split_tokens, t.split_len);
         plan->max_splits = std::max(plan->max_splits, t.n_splits);
     }
     if (plan->max_splits > 1) {

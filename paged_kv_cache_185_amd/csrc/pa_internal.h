@@ -80,6 +80,7 @@ struct PrefillTile {
     int32_t n_splits;   // KV splits used by this tile (<= grid splits)
     int32_t dense;      // 1: the tile's tokens are first, first+1, ..., last
     int32_t item0;      // first (tile, split) item of the tile in its launch (set at launch)
+    int32_t split_len;  // keys per split of this tile (multiple of the KV tile)
 };
 
 constexpr int kMaxTilesPerLaunch = 128;
@@ -105,7 +106,7 @@ struct PrefillArgs {
     int32_t page_size;  // a power of two
     int32_t page_shift; // log2(page_size)
     int32_t head_dim;
-    int32_t split_tokens;   // KV keys per split (multiple of the KV tile)
+    int32_t split_tokens;   // the longest split of any tile (sizes the LDS page table)
     int32_t max_splits;     // split slots per (token, head) in the partials
     int32_t n_tiles;        // tiles in the current launch (set by launch_prefill)
     int32_t group_base;     // first group of the current launch

@@ -165,8 +165,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, Til
     const PrefillTile tile = tl.t[tile_idx];
     const int split = item - tile.item0;
     if (split >= tile.n_splits) return;
-    const int kv_begin = split * a.split_tokens;
-    const int kv_end = min(tile.kv_end, kv_begin + a.split_tokens);
+    const int kv_begin = split * tile.split_len;
+    const int kv_end = min(tile.kv_end, kv_begin + tile.split_len);
 
     __shared__ Smem<D> sm;
     extern __shared__ int32_t sm_pages[];
