@@ -500,7 +500,23 @@ pa_status pa_decode(const pa_cache_desc* desc, const void* k_cache, const void* 
     a.partition_tokens = plan.partition_tokens;
     a.n_part = plan.n_part;
     a.scale_log2 = (float)((double)scale * kLog2e);
-    hipError_t e = launch_decode(a, (hipStream_t)stream);
+    // live (sequence, partition) items only, when the lengths are known here
+    // and the table fits the kernel argument
+    static thread_local DecodeItems items;
+    int64_t n_workgroups = (int64_t)plan.n_part * desc->n_kv_heads * n_seqs;
+    items.n_seqs = 0;
+    if (kv_lens_host && n_seqs > 0 && n_seqs <= kDecodeItemSeqs) {
+        int64_t total = 0;
+        for (int32_t i = 0; i < n_seqs; ++i) {
+            items.item0[i] = (int32_t)total;
+            total += ((int64_t)kv_lens_host[i] + plan.partition_tokens - 1) / plan.partition_tokens;
+        }
+        items.item0[n_seqs] = (int32_t)total;
+        items.n_seqs = n_seqs;
+        n_workgroups = total * desc->n_kv_heads;
+    }
+    if (n_workgroups == 0) return PA_OK;
+    hipError_t e = launch_decode(a, items, n_workgroups, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail("pa_decode", e);
     return PA_OK;
 }

@@ -73,18 +73,33 @@ struct ChunkRegs {
 };
 
 template <int D>
-__global__ __launch_bounds__(256, 2) void decode_partition_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256, 2) void decode_partition_kernel(DecodeArgs a, DecodeItems items) {
     constexpr int KS = D / 32;
     constexpr int NB = D / 16;
-    // workgroups are numbered KV-head fastest, then sequence, then partition:
-    // the dispatcher deals consecutive workgroups to the XCDs in turn, so
-    // every XCD gets an even share of each partition index (with variable
-    // lengths the high partitions exist only for long sequences), and the
-    // empty partitions of short sequences come last
+    // Workgroups are numbered KV-head fastest: the dispatcher deals
+    // consecutive workgroups to the XCDs in turn, so every XCD gets an even
+    // share of the work whatever the lengths.  With an item table the grid
+    // holds only live (sequence, partition) items, numbered sequence by
+    // sequence (an empty workgroup would hold a compute unit that a live one
+    // could use); without one it holds every (sequence, partition) pair,
+    // partition slowest, so that the empty partitions of short sequences
+    // come last.
     const int kvh = blockIdx.x % a.n_kv_heads;
     const int rest = blockIdx.x / a.n_kv_heads;
-    const int seq = rest % a.n_seqs;
-    const int part = rest / a.n_seqs;
+    int seq, part;
+    if (items.n_seqs > 0) {
+        int lo = 0, hi = items.n_seqs - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (items.item0[mid] <= rest) lo = mid;
+            else hi = mid - 1;
+        }
+        seq = lo;
+        part = rest - items.item0[lo];
+    } else {
+        seq = rest % a.n_seqs;
+        part = rest / a.n_seqs;
+    }
     const int L = a.kv_lens[seq];
     const int t0 = part * a.partition_tokens;
     if (t0 >= L) return;
@@ -405,13 +420,14 @@ int decode_page_table_entries(int partition_tokens, int page_size) {
     return (partition_tokens + page_size - 1) / page_size + 1;
 }
 
-hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
-    const dim3 grid((unsigned)((int64_t)a.n_part * a.n_kv_heads * a.n_seqs));
+hipError_t launch_decode(const DecodeArgs& a, const DecodeItems& items, int64_t n_workgroups,
+                         hipStream_t stream) {
+    const dim3 grid((unsigned)n_workgroups);
     const size_t lds = sizeof(int32_t) * (size_t)decode_page_table_entries(a.partition_tokens, a.page_size);
     if (a.head_dim == 128)
-        hipLaunchKernelGGL(decode_partition_kernel<128>, grid, dim3(256), lds, stream, a);
+        hipLaunchKernelGGL(decode_partition_kernel<128>, grid, dim3(256), lds, stream, a, items);
     else
-        hipLaunchKernelGGL(decode_partition_kernel<64>, grid, dim3(256), lds, stream, a);
+        hipLaunchKernelGGL(decode_partition_kernel<64>, grid, dim3(256), lds, stream, a, items);
     return hipGetLastError();
 }
 

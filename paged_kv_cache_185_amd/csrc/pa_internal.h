@@ -53,7 +53,18 @@ struct DecodeArgs {
     float scale_log2;   // scale * log2(e)
 };
 
-hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+// Batches of up to kDecodeItemSeqs sequences launch only their live
+// (sequence, partition) items: item0[s] is the first item of sequence s
+// (items numbered sequence by sequence); n_seqs = 0 launches every
+// (partition, sequence) pair and lets the empty ones exit.
+constexpr int kDecodeItemSeqs = 1024;
+struct DecodeItems {
+    int32_t n_seqs;
+    int32_t item0[kDecodeItemSeqs + 1];
+};
+
+hipError_t launch_decode(const DecodeArgs& a, const DecodeItems& items, int64_t n_workgroups,
+                         hipStream_t stream);
 // LDS entries the decode kernel needs for one partition's page ids.
 int decode_page_table_entries(int partition_tokens, int page_size);
 // Largest page-id table the decode kernel stages in LDS (32 KiB).
