@@ -282,7 +282,7 @@ size_t pa_decode_workspace_bytes(const pa_cache_desc* desc, int32_t n_seqs, int3
  *   kv_lens_host host copy of kv_lens or NULL; used only to size the split
  *   scale        softmax scale (e.g. 1/sqrt(head_dim))
  *   partition_tokens  0 = choose (about one workgroup per compute unit
- *                when all lengths are equal, partitions of at most 4096
+ *                when all lengths are equal, partitions of at most 2048
  *                tokens otherwise; needs kv_lens_host); -1 = one pass per
  *                sequence (no split); >0 = split every sequence into
  *                partitions of this many tokens (a multiple of 256),

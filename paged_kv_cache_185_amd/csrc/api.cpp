@@ -116,8 +116,9 @@ pa_status plan_decode(const pa_cache_desc* d, int32_t n_seqs, int32_t n_q_heads,
         // with unequal lengths the workgroups differ in size and the largest
         // ones end last: partitions of at most kDecodeVarlenPartition tokens
         // let the dispatcher even the load out (measured on mixed batches of
-        // 256..32768 tokens: 4096-token partitions 25% faster than one
-        // partition per compute unit's share)
+        // 256..32768 tokens with the live-only grid: 2048-token partitions
+        // 3-4% faster than 4096, and a third faster than one partition per
+        // compute unit's share)
         if (shortest != longest) T = std::min<int64_t>(T, kDecodeVarlenPartition);
         if (T >= longest) T = round_up(longest, Q);
     } else {

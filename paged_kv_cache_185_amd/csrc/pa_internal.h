@@ -70,7 +70,7 @@ int decode_page_table_entries(int partition_tokens, int page_size);
 // Largest page-id table the decode kernel stages in LDS (32 KiB).
 constexpr int kDecodeMaxPageEntries = 8192;
 // Largest automatic decode partition when the batch's lengths differ.
-constexpr int64_t kDecodeVarlenPartition = 4096;
+constexpr int64_t kDecodeVarlenPartition = 2048;
 // Minimum size of the completion-counter region at the start of a decode
 // workspace (16384 counters).
 constexpr size_t kDecodeCounterBytes = 65536;
