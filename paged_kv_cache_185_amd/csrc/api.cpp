@@ -158,9 +158,8 @@ struct PrefillPlan {
 };
 
 // Per-tile KV split lengths and counts and the workspace layout, given the tiles.
-pa_status finish_prefill_plan(const pa_cache_desc* d, int32_t kv_splits, int64_t sum_kv,
-                              int64_t max_kv, PrefillPlan* plan) {
-    (void)sum_kv;
+pa_status finish_prefill_plan(const pa_cache_desc* d, int32_t kv_splits, int64_t max_kv,
+                              PrefillPlan* plan) {
     const int64_t KT = kPrefillKvTile;
     // the kernel stages one split's page ids in LDS: very long ranges are split
     const int64_t lds_cap = (int64_t)(kPrefillMaxPageEntries - 1) * d->page_size / KT * KT;
@@ -252,7 +251,7 @@ pa_status plan_prefill(const pa_cache_desc* d, int32_t n_tokens, int32_t n_q_hea
     }
     std::stable_sort(order.begin(), order.end(),
                      [&](int32_t x, int32_t y) { return row[x] < row[y]; });
-    int64_t sum_kv = 0, max_kv = 0;
+    int64_t max_kv = 0;
     for (size_t b = 0; b < order.size();) {
         size_t e = b;
         while (e < order.size() && row[order[e]] == row[order[b]]) ++e;
@@ -274,12 +273,11 @@ pa_status plan_prefill(const pa_cache_desc* d, int32_t n_tokens, int32_t n_q_hea
             t.min_vis = kmin;
             t.dense = (t.last - t.first + 1 == t.count) ? 1 : 0;
             plan->tiles.push_back(t);
-            sum_kv += ke;
             max_kv = std::max<int64_t>(max_kv, ke);
         }
         b = e;
     }
-    return finish_prefill_plan(d, kv_splits, sum_kv, max_kv, plan);
+    return finish_prefill_plan(d, kv_splits, max_kv, plan);
 }
 
 // Unified span: tiles are runs of consecutive ubatch tokens, each scanning all
@@ -291,7 +289,6 @@ pa_status plan_unified(const pa_cache_desc* d, int32_t n_tokens, int32_t n_q_hea
     if (span < 1 || (int64_t)span > (int64_t)d->num_pages * d->page_size)
         return fail(PA_ERR_INVALID, "pa_unified_attention: span must be in [1, num_pages*page_size]");
     const int tpt = prefill_tokens_per_tile(n_q_heads / d->n_kv_heads);
-    int64_t sum_kv = 0;
     for (int32_t b = 0; b < n_tokens; b += tpt) {
         PrefillTile t{};
         t.row = 0;
@@ -302,9 +299,8 @@ pa_status plan_unified(const pa_cache_desc* d, int32_t n_tokens, int32_t n_q_hea
         t.min_vis = 0;
         t.dense = 1;
         plan->tiles.push_back(t);
-        sum_kv += span;
     }
-    return finish_prefill_plan(d, kv_splits, sum_kv, span, plan);
+    return finish_prefill_plan(d, kv_splits, span, plan);
 }
 
 // Fill the common launch arguments from a plan and launch its tiles (at most
