@@ -236,3 +236,31 @@ def test_graph_replay_matches_eager():
                              partition_tokens=256)
         torch.cuda.synchronize()
         assert_attention_close(to_host(other), eager.astype(np.float64), "eager between replays")
+
+
+def test_more_sequences_than_the_item_table():
+    """Above 1024 sequences the grid holds every (sequence, partition) pair and
+    the empty ones exit: same results as the oracle, mixed lengths."""
+    rng = np.random.default_rng(31)
+    lens = [int(x) for x in rng.integers(1, 300, 1100)]
+    lens[7] = 5000                     # some sequences split into partitions
+    lens[1000] = 4097
+    N = int(1.25 * sum((L + 15) // 16 for L in lens)) + 8
+    c = W.make_decode_case(rng, "many", 8, 2, 64, 16, lens, N)
+    got = run_decode(c, 0)
+    assert_attention_close(got, ref_decode(c), "1100 sequences, automatic partitions")
+
+
+def test_mixed_lengths_many_partitions_combine():
+    """Automatic plan on unequal lengths (partitions of at most 2048 tokens,
+    here 1536): a 40000-token sequence gets 27 partitions, more than one round
+    of the combine's loads; the rest of the batch is short."""
+    rng = np.random.default_rng(32)
+    lens = [40000, 300, 2049, 17, 6000]
+    N = int(1.2 * sum((L + 127) // 128 for L in lens)) + 4
+    c = W.make_decode_case(rng, "many_parts", 32, 8, 128, 128, lens, N)
+    got = run_decode(c, 0)
+    assert_attention_close(got, ref_decode(c), "mixed lengths, many-partition combine")
+    # the live-only grid and the fixed fold order make repeats bitwise equal
+    again = run_decode(c, 0)
+    assert np.array_equal(got.view(np.uint32), again.view(np.uint32))
