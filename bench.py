@@ -17,7 +17,13 @@ Prefill workload (reported beside it): 8 fresh sequences x 16384 tokens
 prefilled in 512-token ubatches, chunk-major; each ubatch is one
 pa_reshape_and_cache + one pa_prefill.  Host-side page allocation and block
 tables are prepared before timing; the 256 ubatches are captured once in a HIP
-graph and replayed.
+graph and replayed.  Sequence s runs on stream s % --prefill-streams (default 2;
+the streams fork from and join the replay stream inside the graph): a
+sequence's chunks run in order, and launches of different sequences, which
+share no pages, may overlap, so one launch's ramp-up and split-combine tail is
+filled by another's work.  The one-stream pass (every launch after the
+previous one) is timed and reported beside it, and the last sequence's last
+ubatch is compared bitwise between the two schedules.
 
 cpu_baseline: the float64 CPU oracle on the machine's host cores, timed on the full
 decode batch (one step) and on one prefill ubatch.
@@ -191,48 +197,76 @@ def bench_prefill(args, pa, torch, W):
                           bt=torch.from_numpy(bt).to(dev), row=torch.from_numpy(row).to(dev),
                           kvl=torch.from_numpy(kvl).to(dev), pos=torch.from_numpy(pos).to(dev),
                           row_h=row, kvl_h=kvl, pos_h=pos))
-    ws = torch.zeros(max(ws_need, 1), dtype=torch.uint8, device=dev)
-    out = torch.empty(cp.chunk, cp.n_q_heads, D, dtype=torch.float32, device=dev)
+    n_str = max(1, args.prefill_streams)
+    # one workspace (split partials and counters) and one output per stream:
+    # launches on different streams may run at the same time
+    wss = [torch.zeros(max(ws_need, 1), dtype=torch.uint8, device=dev) for _ in range(n_str)]
+    outs = [torch.empty(cp.chunk, cp.n_q_heads, D, dtype=torch.float32, device=dev) for _ in range(n_str)]
     flops = W.attention_flops(pairs, cp.n_q_heads, D)
 
-    def one_pass(stream):
+    def one_pass(streams):
+        # sequence s runs on stream s % len(streams): a sequence's chunks stay
+        # in order, different sequences' ubatches may overlap
         for pl in plans:
             s, p0, n = pl["s"], pl["p0"], pl["n"]
+            j = s % len(streams)
             pa.pa_reshape_and_cache(kd, vd, knd[s, p0:p0 + n], vnd[s, p0:p0 + n], pl["slots"],
-                                    stream=stream)
+                                    stream=streams[j])
             pa.pa_prefill(qd[s, p0:p0 + n], kd, vd, pl["bt"], pl["row"], pl["kvl"], pl["pos"],
                           float(cp.scale), token_row_host=pl["row_h"], token_kv_len_host=pl["kvl_h"],
-                          token_pos_host=pl["pos_h"], out=out, workspace=ws, stream=stream)
+                          token_pos_host=pl["pos_h"], out=outs[j], workspace=wss[j], stream=streams[j])
+
+    def capture(n):
+        """The pass over n streams, forked from and joined back into one, as one graph."""
+        streams = [torch.cuda.Stream() for _ in range(n)]
+        g = torch.cuda.CUDAGraph()
+        s0 = streams[0]
+        s0.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s0):
+            with torch.cuda.graph(g, stream=s0):
+                for st in streams[1:]:
+                    st.wait_stream(s0)
+                one_pass(streams)
+                for st in streams[1:]:
+                    s0.wait_stream(st)
+        torch.cuda.current_stream().wait_stream(s0)
+        torch.cuda.synchronize()
+        return g
+
+    def time_pass(g):
+        g.replay()   # warm replay
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for _ in range(args.prefill_reps):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return e0.elapsed_time(e1) / args.prefill_reps, wall * 1e3 / args.prefill_reps
 
     # eager pass once (warms the code paths and fills the cache)
-    one_pass(torch.cuda.current_stream())
+    one_pass([torch.cuda.current_stream()])
     torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        with torch.cuda.graph(g, stream=side):
-            one_pass(torch.cuda.current_stream())
-    torch.cuda.current_stream().wait_stream(side)
-    torch.cuda.synchronize()
-    g.replay()
-    torch.cuda.synchronize()
-    reps = args.prefill_reps
-    stream = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    e0.record(stream)
-    for _ in range(reps):
-        g.replay()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    pass_ms = e0.elapsed_time(e1) / reps
-    return cp, plans, {
-        "ubatches": len(plans), "flops": flops, "pairs": pairs, "pass_ms": pass_ms,
-        "wall_ms_per_pass": wall * 1e3 / reps, "reps": reps,
-        "tflops": flops / (pass_ms * 1e-3) / 1e12,
-    }
+    # one stream: every launch waits for the previous one
+    g1 = capture(1)
+    ms1, wall1 = time_pass(g1)
+    last_seq = cp.n_seqs - 1
+    ref_last = outs[0].clone()   # the last ubatch of the pass: the last sequence's last chunk
+    del g1
+    res = {"ubatches": len(plans), "flops": flops, "pairs": pairs, "reps": args.prefill_reps,
+           "streams": n_str, "one_stream_ms": ms1, "one_stream_tflops": flops / (ms1 * 1e-3) / 1e12}
+    if n_str > 1:
+        g = capture(n_str)
+        ms, wall = time_pass(g)
+        res["schedules_bitwise_equal"] = bool(torch.equal(ref_last, outs[last_seq % n_str]))
+        del g
+    else:
+        ms, wall = ms1, wall1
+    res.update(pass_ms=ms, wall_ms_per_pass=wall, tflops=flops / (ms * 1e-3) / 1e12)
+    return cp, plans, res
 
 
 def _time_graph(torch, fn, reps):
@@ -533,6 +567,8 @@ def main():
                     help="qwen3 = the 8 x 16384 headline batch; varlen* = 64 log-uniform sequences")
     ap.add_argument("--prefill-len", type=int, default=16384)
     ap.add_argument("--prefill-reps", type=int, default=3)
+    ap.add_argument("--prefill-streams", type=int, default=2,
+                    help="streams the prefill pass's sequences are spread over (1 = every launch in order)")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-unified", action="store_true",
@@ -576,7 +612,8 @@ def main():
     if not args.no_prefill:
         log("prefill: generating 8 x 16384 chunked workload")
         cp, _, pre = bench_prefill(args, pa, torch, W)
-        log(f"prefill: {pre['pass_ms']:.2f} ms/pass, {pre['tflops']:.1f} TFLOP/s")
+        log(f"prefill: {pre['pass_ms']:.2f} ms/pass, {pre['tflops']:.1f} TFLOP/s over {pre['streams']} "
+            f"stream(s); one stream {pre['one_stream_ms']:.2f} ms/pass, {pre['one_stream_tflops']:.1f} TFLOP/s")
 
     uni = None
     if not args.no_unified:
@@ -651,13 +688,19 @@ def main():
         result["prefill"] = {
             "workload": f"8 fresh sequences x {args.prefill_len} tokens in 512-token ubatches "
                         "(reshape_and_cache + pa_prefill each), HIP-graph replay",
+            "schedule": f"sequence s on stream s % {pre['streams']}, chunks of a sequence in order",
             "tflops": round(pre["tflops"], 2),
             "frac_of_mfma_f16_peak": round(pre["tflops"] / MFMA_F16_PEAK_TFLOPS, 4),
             "ms_per_pass": round(pre["pass_ms"], 4),
+            "one_stream": {"tflops": round(pre["one_stream_tflops"], 2),
+                           "frac_of_mfma_f16_peak": round(pre["one_stream_tflops"] / MFMA_F16_PEAK_TFLOPS, 4),
+                           "ms_per_pass": round(pre["one_stream_ms"], 4)},
             "flops_per_pass": pre["flops"],
             "ubatches": pre["ubatches"],
             "reps": pre["reps"],
         }
+        if "schedules_bitwise_equal" in pre:
+            result["prefill"]["schedules_bitwise_equal"] = pre["schedules_bitwise_equal"]
     if uni is not None:
         result["unified_vs_paged"] = uni
     if swp is not None:
