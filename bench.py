@@ -17,13 +17,18 @@ Prefill workload (reported beside it): 8 fresh sequences x 16384 tokens
 prefilled in 512-token ubatches, chunk-major; each ubatch is one
 pa_reshape_and_cache + one pa_prefill.  Host-side page allocation and block
 tables are prepared before timing; the 256 ubatches are captured once in a HIP
-graph and replayed.  Sequence s runs on stream s % --prefill-streams (default 2;
-the streams fork from and join the replay stream inside the graph): a
-sequence's chunks run in order, and launches of different sequences, which
-share no pages, may overlap, so one launch's ramp-up and split-combine tail is
-filled by another's work.  The one-stream pass (every launch after the
-previous one) is timed and reported beside it, and the last sequence's last
-ubatch is compared bitwise between the two schedules.
+graph and replayed.  Sequence s runs on stream s % --prefill-streams (default 8,
+one stream per sequence; the streams fork from and join the replay stream
+inside the graph): a sequence's chunks run in order, and launches of
+different sequences, which share no pages, may overlap.  Each launch of this
+schedule takes --prefill-splits KV splits (default 1: every (tile, KV head)
+workgroup walks its whole visible range, so no launch pays split partial
+stores or a combine, and the concurrent launches of other sequences fill the
+compute units instead).  The last sequence's last ubatch is re-run eagerly
+with the same plan after the timed replays and compared bitwise (concurrency
+must not change a result).  The one-stream pass (every launch after the
+previous one, with the library's automatic split plan, which fills the GPU
+from one launch) is timed and reported beside it.
 
 cpu_baseline: the float64 CPU oracle on the machine's host cores, timed on the full
 decode batch (one step) and on one prefill ubatch.
@@ -190,21 +195,30 @@ def bench_prefill(args, pa, torch, W):
         row = np.full(n, s, dtype=np.int32)
         kvl = np.full(n, p0 + n, dtype=np.int32)
         pos = np.arange(p0, p0 + n, dtype=np.int32)
-        ws_need = max(ws_need, pa.pa_prefill_workspace_bytes(pa.cache_desc(kd, vd), cp.n_q_heads,
-                                                              row, kvl, pos, 0))
         pairs += W.prefill_pairs(kvl, pos)
         plans.append(dict(s=s, p0=p0, n=n, slots=torch.from_numpy(slots).to(dev),
                           bt=torch.from_numpy(bt).to(dev), row=torch.from_numpy(row).to(dev),
                           kvl=torch.from_numpy(kvl).to(dev), pos=torch.from_numpy(pos).to(dev),
                           row_h=row, kvl_h=kvl, pos_h=pos))
     n_str = max(1, args.prefill_streams)
+    desc = pa.cache_desc(kd, vd)
+    for pl in plans:
+        for sp in (0, args.prefill_splits):
+            ws_need = max(ws_need, pa.pa_prefill_workspace_bytes(desc, cp.n_q_heads, pl["row_h"], pl["kvl_h"],
+                                                                  pl["pos_h"], sp))
     # one workspace (split partials and counters) and one output per stream:
     # launches on different streams may run at the same time
     wss = [torch.zeros(max(ws_need, 1), dtype=torch.uint8, device=dev) for _ in range(n_str)]
     outs = [torch.empty(cp.chunk, cp.n_q_heads, D, dtype=torch.float32, device=dev) for _ in range(n_str)]
     flops = W.attention_flops(pairs, cp.n_q_heads, D)
 
-    def one_pass(streams):
+    def prefill(pl, splits, out, ws, stream):
+        s, p0, n = pl["s"], pl["p0"], pl["n"]
+        pa.pa_prefill(qd[s, p0:p0 + n], kd, vd, pl["bt"], pl["row"], pl["kvl"], pl["pos"],
+                      float(cp.scale), token_row_host=pl["row_h"], token_kv_len_host=pl["kvl_h"],
+                      token_pos_host=pl["pos_h"], kv_splits=splits, out=out, workspace=ws, stream=stream)
+
+    def one_pass(streams, splits):
         # sequence s runs on stream s % len(streams): a sequence's chunks stay
         # in order, different sequences' ubatches may overlap
         for pl in plans:
@@ -212,11 +226,9 @@ def bench_prefill(args, pa, torch, W):
             j = s % len(streams)
             pa.pa_reshape_and_cache(kd, vd, knd[s, p0:p0 + n], vnd[s, p0:p0 + n], pl["slots"],
                                     stream=streams[j])
-            pa.pa_prefill(qd[s, p0:p0 + n], kd, vd, pl["bt"], pl["row"], pl["kvl"], pl["pos"],
-                          float(cp.scale), token_row_host=pl["row_h"], token_kv_len_host=pl["kvl_h"],
-                          token_pos_host=pl["pos_h"], out=outs[j], workspace=wss[j], stream=streams[j])
+            prefill(pl, splits, outs[j], wss[j], streams[j])
 
-    def capture(n):
+    def capture(n, splits):
         """The pass over n streams, forked from and joined back into one, as one graph."""
         streams = [torch.cuda.Stream() for _ in range(n)]
         g = torch.cuda.CUDAGraph()
@@ -226,7 +238,7 @@ def bench_prefill(args, pa, torch, W):
             with torch.cuda.graph(g, stream=s0):
                 for st in streams[1:]:
                     st.wait_stream(s0)
-                one_pass(streams)
+                one_pass(streams, splits)
                 for st in streams[1:]:
                     s0.wait_stream(st)
         torch.cuda.current_stream().wait_stream(s0)
@@ -248,23 +260,29 @@ def bench_prefill(args, pa, torch, W):
         return e0.elapsed_time(e1) / args.prefill_reps, wall * 1e3 / args.prefill_reps
 
     # eager pass once (warms the code paths and fills the cache)
-    one_pass([torch.cuda.current_stream()])
+    one_pass([torch.cuda.current_stream()], 0)
     torch.cuda.synchronize()
-    # one stream: every launch waits for the previous one
-    g1 = capture(1)
+    # one stream, automatic split plan: every launch waits for the previous one
+    g1 = capture(1, 0)
     ms1, wall1 = time_pass(g1)
     last_seq = cp.n_seqs - 1
-    ref_last = outs[0].clone()   # the last ubatch of the pass: the last sequence's last chunk
+    ref_auto = outs[0].clone()   # the last ubatch of the pass: the last sequence's last chunk
     del g1
     res = {"ubatches": len(plans), "flops": flops, "pairs": pairs, "reps": args.prefill_reps,
-           "streams": n_str, "one_stream_ms": ms1, "one_stream_tflops": flops / (ms1 * 1e-3) / 1e12}
-    if n_str > 1:
-        g = capture(n_str)
-        ms, wall = time_pass(g)
-        res["schedules_bitwise_equal"] = bool(torch.equal(ref_last, outs[last_seq % n_str]))
-        del g
-    else:
-        ms, wall = ms1, wall1
+           "streams": n_str, "splits": args.prefill_splits, "one_stream_ms": ms1,
+           "one_stream_tflops": flops / (ms1 * 1e-3) / 1e12}
+    g = capture(n_str, args.prefill_splits)
+    ms, wall = time_pass(g)
+    del g
+    # the last ubatch again, alone and eager, with the same plan: concurrency
+    # must not change it; against the automatic plan it differs only by the
+    # split combine's rounding
+    got = outs[last_seq % n_str].clone()
+    ref = torch.empty_like(got)
+    prefill(plans[-1], args.prefill_splits, ref, wss[0], torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    res["last_ubatch_bitwise_equal_eager"] = bool(torch.equal(ref, got))
+    res["last_ubatch_max_abs_diff_vs_auto_plan"] = float((got - ref_auto).abs().max())
     res.update(pass_ms=ms, wall_ms_per_pass=wall, tflops=flops / (ms * 1e-3) / 1e12)
     return cp, plans, res
 
@@ -567,8 +585,11 @@ def main():
                     help="qwen3 = the 8 x 16384 headline batch; varlen* = 64 log-uniform sequences")
     ap.add_argument("--prefill-len", type=int, default=16384)
     ap.add_argument("--prefill-reps", type=int, default=3)
-    ap.add_argument("--prefill-streams", type=int, default=2,
+    ap.add_argument("--prefill-streams", type=int, default=8,
                     help="streams the prefill pass's sequences are spread over (1 = every launch in order)")
+    ap.add_argument("--prefill-splits", type=int, default=1,
+                    help="kv_splits of the multi-stream prefill schedule (0: the library's plan, which "
+                         "fills the GPU from one launch; the one-stream pass always uses it)")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-unified", action="store_true",
@@ -688,19 +709,21 @@ def main():
         result["prefill"] = {
             "workload": f"8 fresh sequences x {args.prefill_len} tokens in 512-token ubatches "
                         "(reshape_and_cache + pa_prefill each), HIP-graph replay",
-            "schedule": f"sequence s on stream s % {pre['streams']}, chunks of a sequence in order",
+            "schedule": f"sequence s on stream s % {pre['streams']}, chunks of a sequence in order, "
+                        f"kv_splits={pre['splits']}",
             "tflops": round(pre["tflops"], 2),
             "frac_of_mfma_f16_peak": round(pre["tflops"] / MFMA_F16_PEAK_TFLOPS, 4),
             "ms_per_pass": round(pre["pass_ms"], 4),
-            "one_stream": {"tflops": round(pre["one_stream_tflops"], 2),
+            "one_stream": {"schedule": "every launch after the previous one, automatic split plan",
+                           "tflops": round(pre["one_stream_tflops"], 2),
                            "frac_of_mfma_f16_peak": round(pre["one_stream_tflops"] / MFMA_F16_PEAK_TFLOPS, 4),
                            "ms_per_pass": round(pre["one_stream_ms"], 4)},
             "flops_per_pass": pre["flops"],
             "ubatches": pre["ubatches"],
             "reps": pre["reps"],
         }
-        if "schedules_bitwise_equal" in pre:
-            result["prefill"]["schedules_bitwise_equal"] = pre["schedules_bitwise_equal"]
+        result["prefill"]["last_ubatch_bitwise_equal_eager"] = pre["last_ubatch_bitwise_equal_eager"]
+        result["prefill"]["last_ubatch_max_abs_diff_vs_auto_plan"] = pre["last_ubatch_max_abs_diff_vs_auto_plan"]
     if uni is not None:
         result["unified_vs_paged"] = uni
     if swp is not None:

@@ -197,3 +197,68 @@ def test_workspace_reused_across_calls_and_shapes():
                 assert np.array_equal(out, first[i]), f"prefill reuse {i} rep {rep}"
     torch.cuda.synchronize()
     assert int(ws[:65536].count_nonzero()) == 0
+
+
+@pytest.mark.parametrize("kv_splits", [1, 2])
+def test_chunked_prefill_concurrent_streams_bitwise(kv_splits):
+    """Sequences prefilled concurrently, sequence s on stream s (its chunks in
+    order on that stream, each stream with its own workspace), give bitwise
+    the outputs of the same launches run one after another; sampled tokens of
+    the last ubatch of each sequence are checked against the oracle."""
+    import torch
+    cp = W.chunked_prefill(n_seqs=4, seq_len=2048, chunk=512, num_pages=160)
+    P, Hkv, D = cp.page_size, cp.n_kv_heads, cp.head_dim
+    pool = pa.Pool(cp.num_pages, P, cp.free_order)
+    seqs = [pool.seq_new() for _ in range(cp.n_seqs)]
+    k_pool, v_pool = W.nan_pools(cp.num_pages, Hkv, P, D)
+    max_pages = cp.seq_len // P
+    ubs = []
+    for s, p0 in cp.ubatches():
+        n = cp.chunk
+        slots, cow = pool.seq_append(seqs[s], n)
+        assert cow is None
+        bt, _ = pool.block_tables(seqs, max_pages)
+        row = np.full(n, s, dtype=np.int32)
+        kvl = np.full(n, p0 + n, dtype=np.int32)
+        pos = np.arange(p0, p0 + n, dtype=np.int32)
+        ubs.append(dict(s=s, p0=p0, slots=slots, bt=bt, row=row, kvl=kvl, pos=pos,
+                        dev=[to_dev(x) for x in (slots, bt, row, kvl, pos)]))
+    q = to_dev(cp.q)
+    kn, vn = to_dev(cp.k), to_dev(cp.v)
+
+    def run(streams):
+        kd, vd = to_dev(k_pool), to_dev(v_pool)
+        need = max(pa.pa_prefill_workspace_bytes(pa.cache_desc(kd, vd), cp.n_q_heads, u["row"], u["kvl"],
+                                                 u["pos"], kv_splits) for u in ubs)
+        ws = [torch.zeros(max(need, 1), dtype=torch.uint8, device="cuda") for _ in streams]
+        outs = []
+        for u in ubs:
+            s, p0, n = u["s"], u["p0"], cp.chunk
+            j = s % len(streams)
+            slots, bt, row, kvl, pos = u["dev"]
+            pa.pa_reshape_and_cache(kd, vd, kn[s, p0:p0 + n], vn[s, p0:p0 + n], slots, stream=streams[j])
+            out = torch.empty(n, cp.n_q_heads, D, dtype=torch.float32, device="cuda")
+            pa.pa_prefill(q[s, p0:p0 + n], kd, vd, bt, row, kvl, pos, float(cp.scale),
+                          token_row_host=u["row"], token_kv_len_host=u["kvl"], token_pos_host=u["pos"],
+                          kv_splits=kv_splits, out=out, workspace=ws[j], stream=streams[j])
+            outs.append(out)
+        torch.cuda.synchronize()
+        return [to_host(o) for o in outs], to_host(kd)
+
+    seq_outs, kseq = run([torch.cuda.current_stream()])
+    conc_outs, kconc = run([torch.cuda.Stream() for _ in range(cp.n_seqs)])
+    assert np.array_equal(bits16(kseq), bits16(kconc))
+    for j, (a, b) in enumerate(zip(seq_outs, conc_outs)):
+        assert np.array_equal(a, b), f"ubatch {j}"
+    kh, vh = k_pool, v_pool
+    for u in ubs:
+        s, p0, n = u["s"], u["p0"], cp.chunk
+        kh, vh = oracle.reshape_and_cache(kh, vh, cp.k[s, p0:p0 + n], cp.v[s, p0:p0 + n], u["slots"])
+    pick = np.array([0, 17, 255, 256, 511])
+    for j, u in enumerate(ubs):
+        if u["p0"] + cp.chunk != cp.seq_len:
+            continue
+        s, p0 = u["s"], u["p0"]
+        ref = oracle.paged_attention(cp.q[s, p0:p0 + cp.chunk][pick], kh, vh, u["bt"], u["row"][pick],
+                                     u["kvl"][pick], u["pos"][pick], cp.scale)
+        assert_attention_close(conc_outs[j][pick], ref, f"sequence {s} last ubatch")
