@@ -108,7 +108,7 @@ pa_status plan_decode(const pa_cache_desc* d, int32_t n_seqs, int32_t n_q_heads,
             return fail(PA_ERR_INVALID, "pa_decode: partition_tokens must be a multiple of 256");
         T = partition_tokens;
     } else if (partition_tokens == 0) {
-        // about one workgroup (4 waves streaming one partition) per compute
+        // about one workgroup (8 waves streaming one partition) per compute
         // unit: measured faster on the 256-CU part than more, shorter
         // partitions, and it keeps the split partials small
         const int64_t work = total * d->n_kv_heads;

@@ -44,9 +44,10 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;   // two per SIMD: one wave's compute overlaps the other's load waits
 constexpr int kChunk = 32;
 constexpr int kDecodeBuffers = 2;   // chunk register sets per wave
+constexpr int kThreads = 64 * kWaves;
 
 __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
@@ -73,7 +74,7 @@ struct ChunkRegs {
 };
 
 template <int D>
-__global__ __launch_bounds__(256, 2) void decode_partition_kernel(DecodeArgs a, DecodeItems items) {
+__global__ __launch_bounds__(kThreads, 1) void decode_partition_kernel(DecodeArgs a, DecodeItems items) {
     constexpr int KS = D / 32;
     constexpr int NB = D / 16;
     // Workgroups are numbered KV-head fastest: the dispatcher deals
@@ -258,7 +259,7 @@ __global__ __launch_bounds__(256, 2) void decode_partition_kernel(DecodeArgs a, 
         }
     };
 
-    // ---- stream the wave's chunks (wave w takes chunks w, w+4, ...) through
+    // ---- stream the wave's chunks (wave w takes chunks w, w+kWaves, ...) through
     // kDecodeBuffers register sets, kDecodeBuffers-1 chunks of loads in flight
     // during each compute.  Loads are issued unconditionally (a chunk past the
     // wave's last one reloads the last one, an L2 hit whose data is unused), so
@@ -425,9 +426,9 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodeItems& items, int64_t 
     const dim3 grid((unsigned)n_workgroups);
     const size_t lds = sizeof(int32_t) * (size_t)decode_page_table_entries(a.partition_tokens, a.page_size);
     if (a.head_dim == 128)
-        hipLaunchKernelGGL(decode_partition_kernel<128>, grid, dim3(256), lds, stream, a, items);
+        hipLaunchKernelGGL(decode_partition_kernel<128>, grid, dim3(kThreads), lds, stream, a, items);
     else
-        hipLaunchKernelGGL(decode_partition_kernel<64>, grid, dim3(256), lds, stream, a, items);
+        hipLaunchKernelGGL(decode_partition_kernel<64>, grid, dim3(kThreads), lds, stream, a, items);
     return hipGetLastError();
 }
 

@@ -27,7 +27,8 @@ hipError_t launch_copy_blocks(void* const* k_caches, void* const* v_caches, int3
 
 // ---- decode ---------------------------------------------------------------
 
-// Tokens per partition are a multiple of this (waves per workgroup x chunk x 2).
+// Tokens per partition are a multiple of this (the tokens one round of the
+// decode workgroup's 8 waves streams: 8 x 32-token chunks).
 constexpr int kDecodePartitionQuantum = 256;
 
 struct DecodeArgs {
