@@ -146,23 +146,28 @@ __global__ __launch_bounds__(kThreads, 1) void decode_partition_kernel(DecodeArg
     const int tk = 8 * (m16 >> 2) + (m16 & 3);
 
     // chunk c0's K rows (tokens clamped to L-1) and V^T rows; page_of maps a
-    // token to its physical page
-    auto load_chunk_with = [&](int c0, ChunkRegs<D>& r, auto page_of) __attribute__((always_inline)) {
+    // token to its physical page.  `idle` (uniform) issues the same loads
+    // with every lane aimed at the first cell of the pools instead: a few
+    // cache-resident lines whose data is never used
+    auto load_chunk_with = [&](int c0, ChunkRegs<D>& r, auto page_of, bool idle) __attribute__((always_inline)) {
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
             const int t = min(c0 + tk + 4 * b, L - 1);
             const uint16_t* row = kc + page_of(t) * page_elems + ((kvh * P + (t & (P - 1))) * D + 8 * g);
+            if (idle) row = kc;
 #pragma unroll
             for (int s = 0; s < KS; ++s) r.k[b][s] = ld16(row + 32 * s);
         }
         int tv = c0 + 8 * g;
         if (tv > L - 1) tv = (L - 1) & ~7;
         const uint16_t* vrow = vc + page_of(tv) * page_elems + ((kvh * D + m16) * P + (tv & (P - 1)));
+        const int64_t vstep = idle ? 0 : (int64_t)16 * P;
+        if (idle) vrow = vc;
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) r.v[nb] = ld16(vrow + (int64_t)16 * nb * P);
+        for (int nb = 0; nb < NB; ++nb) r.v[nb] = ld16(vrow + nb * vstep);
     };
-    auto load_chunk = [&](int c0, ChunkRegs<D>& r) __attribute__((always_inline)) {
-        load_chunk_with(c0, r, [&](int t) { return sm_pages[(t >> sh) - page_base]; });
+    auto load_chunk = [&](int c0, ChunkRegs<D>& r, bool idle) __attribute__((always_inline)) {
+        load_chunk_with(c0, r, [&](int t) { return sm_pages[(t >> sh) - page_base]; }, idle);
     };
 
     constexpr int NBUF = kDecodeBuffers;
@@ -172,7 +177,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_partition_kernel(DecodeArg
     const bool chunk_in_page = P >= kChunk;
     if (chunk_in_page && cfirst < t1) {
         const int page0 = bt[cfirst >> sh];
-        load_chunk_with(cfirst, r[0], [&](int) { return page0; });
+        load_chunk_with(cfirst, r[0], [&](int) { return page0; }, false);
     }
     if ((int)threadIdx.x < n_pages) sm_pages[threadIdx.x] = pt0;
     for (int i = threadIdx.x + blockDim.x; i < n_pages; i += blockDim.x) sm_pages[i] = bt[page_base + i];
@@ -261,15 +266,18 @@ __global__ __launch_bounds__(kThreads, 1) void decode_partition_kernel(DecodeArg
 
     // ---- stream the wave's chunks (wave w takes chunks w, w+kWaves, ...) through
     // kDecodeBuffers register sets, kDecodeBuffers-1 chunks of loads in flight
-    // during each compute.  Loads are issued unconditionally (a chunk past the
-    // wave's last one reloads the last one, an L2 hit whose data is unused), so
+    // during each compute.  Loads are issued unconditionally (for a chunk past
+    // the wave's last one they are idle loads of one cache-resident line), so
     // every path issues the same loads and the in-order vmcnt accounting lets a
     // chunk's compute wait for its own loads only.
     if (cfirst < t1) {
         const int last_c = cfirst + ((t1 - 1 - cfirst) / stride) * stride;
-        if (!chunk_in_page) load_chunk(cfirst, r[0]);
+        auto load_next = [&](int c, ChunkRegs<D>& r) __attribute__((always_inline)) {
+            load_chunk(min(c, last_c), r, c > last_c);
+        };
+        if (!chunk_in_page) load_chunk(cfirst, r[0], false);
 #pragma unroll
-        for (int j = 1; j < NBUF - 1; ++j) load_chunk(min(cfirst + j * stride, last_c), r[j]);
+        for (int j = 1; j < NBUF - 1; ++j) load_next(cfirst + j * stride, r[j]);
         for (int it = 0;; it += NBUF) {
             bool done = false;
 #pragma unroll
@@ -279,7 +287,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_partition_kernel(DecodeArg
                     done = true;
                     break;
                 }
-                load_chunk(min(cj + (NBUF - 1) * stride, last_c), r[(j + NBUF - 1) % NBUF]);
+                load_next(cj + (NBUF - 1) * stride, r[(j + NBUF - 1) % NBUF]);
                 compute_chunk(cj, r[j]);
             }
             if (done) break;
