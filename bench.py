@@ -388,14 +388,14 @@ def bench_swap_compact(args, pa, torch, W):
     P, H, D, N = 128, 8, 128, 2048
     rng = np.random.default_rng(185009)
     kd = torch.empty((N, H, P, D), dtype=torch.float16, device=dev).normal_()
-    vd = torch.empty((N, H, D, P), dtype=torch.float16, device=dev).normal_()
+    vd = torch.empty(pa.v_cache_shape(N, H, P, D), dtype=torch.float16, device=dev).normal_()
     pool = pa.Pool(N, P, rng.permutation(N))
     pool.host_reserve(256)
     seqs = [pool.seq_new() for _ in range(8)]
     for s in seqs:
         pool.seq_append(s, 16384)
     kh = torch.empty((256, H, P, D), dtype=torch.float16, pin_memory=True)
-    vh = torch.empty((256, H, D, P), dtype=torch.float16, pin_memory=True)
+    vh = torch.empty(pa.v_cache_shape(256, H, P, D), dtype=torch.float16, pin_memory=True)
     page_bytes = 2 * H * P * D * 2
     stream = torch.cuda.current_stream()
     ev = lambda: torch.cuda.Event(enable_timing=True)   # noqa: E731
@@ -476,7 +476,7 @@ def bench_prefix(args, pa, torch, W):
     gen.manual_seed(185012)
     qd = torch.randn((n_req, L, Hq, D), generator=gen, device=dev, dtype=torch.float32)
     kd = torch.full((N, Hkv, P, D), float("nan"), dtype=torch.float16, device=dev)
-    vd = torch.full((N, Hkv, D, P), float("nan"), dtype=torch.float16, device=dev)
+    vd = torch.full(pa.v_cache_shape(N, Hkv, P, D), float("nan"), dtype=torch.float16, device=dev)
     desc = pa.cache_desc(kd, vd)
     free_order = rng.permutation(N)
     scale = float(W.fp32_scale(D))

@@ -22,10 +22,12 @@
  *     exception crosses this boundary.
  *   - Cache storage for one layer is two device arrays of IEEE binary16:
  *       K cache  [num_pages][n_kv_heads][page_size][head_dim]
- *       V cache  [num_pages][n_kv_heads][head_dim][page_size]
+ *       V cache  [num_pages][n_kv_heads][page_size / T][head_dim][T],
+ *                T = min(page_size, 32)
  *     Cell (page p, slot s) of KV head h holds one token's key row
- *     K[p][h][s][:] and value column V[p][h][:][s].  A slot id is
- *     page * page_size + slot.
+ *     K[p][h][s][:] and value column V[p][h][s / T][:][s % T]: a V page keeps
+ *     its slots in blocks of T, each block slot-innermost (for page_size <= 32
+ *     this is V[p][h][:][s]).  A slot id is page * page_size + slot.
  *   - Query head h reads KV head h / (n_q_heads / n_kv_heads).
  *   - Device pointers are pa_dev pointers; the caller allocates and owns every
  *     device buffer.  Device calls are asynchronous on `stream` (a hipStream_t;

@@ -11,14 +11,31 @@ pages of each query's own sequence:
     out_{i,h}  = sum_t exp(z_t - max z) V_t[h // G]  /  sum_t exp(z_t - max z)
 
 with G = Hq / Hkv (query head h reads KV head h // G).  Pool storage: K is
-``[N][Hkv][P][D]`` and V is ``[N][Hkv][D][P]``; logical cell t of a sequence is
-page ``table[t // P]``, slot ``t % P``.
+``[N][Hkv][P][D]`` and V is ``[N][Hkv][P // B][D][B]`` with B = min(P, 32): the
+value column of slot s of page p, KV head h, is ``V[p, h, s // B, :, s % B]``.
+Logical cell t of a sequence is page ``table[t // P]``, slot ``t % P``.
 """
 from __future__ import annotations
 
 import math
 
 import numpy as np
+
+
+def v_block(page_size: int) -> int:
+    """Slots per block of a V page: the V storage convention above."""
+    return min(int(page_size), 32)
+
+
+def check_v_pool(k_pool: np.ndarray, v_pool: np.ndarray) -> int:
+    """Check that ``v_pool`` has the V storage shape that goes with ``k_pool``;
+    return the block size B."""
+    num_pages, n_kv, page_size, head_dim = k_pool.shape
+    B = v_block(page_size)
+    want = (num_pages, n_kv, page_size // B, head_dim, B)
+    if tuple(v_pool.shape) != want:
+        raise ValueError(f"V pool shape {tuple(v_pool.shape)} is not {want}")
+    return B
 
 
 def expand_per_token(block_tables: np.ndarray, token_row: np.ndarray) -> np.ndarray:
@@ -40,14 +57,16 @@ def gather_logical(k_pool: np.ndarray, v_pool: np.ndarray, pages: np.ndarray, n:
     Only the ceil(n / P) pages that hold those cells are read; each page id must be
     a real page of the pool."""
     num_pages, n_kv, page_size, head_dim = k_pool.shape
+    check_v_pool(k_pool, v_pool)
     n_pages = (n + page_size - 1) // page_size
     ids = np.asarray(pages[:n_pages], dtype=np.int64)
     if ids.shape[0] != n_pages or np.any(ids < 0) or np.any(ids >= num_pages):
         raise ValueError("block table does not cover the requested cells")
     k = k_pool[ids]                                  # [np][Hkv][P][D]
-    v = v_pool[ids]                                  # [np][Hkv][D][P]
+    v = v_pool[ids]                                  # [np][Hkv][P/B][D][B]
     k = k.transpose(0, 2, 1, 3).reshape(n_pages * page_size, n_kv, head_dim)[:n]
-    v = v.transpose(0, 3, 1, 2).reshape(n_pages * page_size, n_kv, head_dim)[:n]
+    # cell order: page, then slot block, then slot in the block
+    v = v.transpose(0, 2, 4, 1, 3).reshape(n_pages * page_size, n_kv, head_dim)[:n]
     return k.astype(np.float64), v.astype(np.float64)
 
 
@@ -173,6 +192,7 @@ def unified_attention(q, k_pool, v_pool, span, cell_seq, cell_pos, token_seq, to
     q = np.asarray(q)
     T, n_q, head_dim = q.shape
     num_pages, n_kv, page_size, _ = k_pool.shape
+    B = check_v_pool(k_pool, v_pool)
     G = n_q // n_kv
     span = int(span)
     if span > num_pages * page_size:
@@ -191,7 +211,8 @@ def unified_attention(q, k_pool, v_pool, span, cell_seq, cell_pos, token_seq, to
         if vis.size == 0:
             continue
         K = k_pool[vis // page_size, :, vis % page_size, :].astype(np.float64)   # [n][Hkv][D]
-        V = v_pool[vis // page_size, :, :, vis % page_size].astype(np.float64)   # [n][Hkv][D]
+        slot = vis % page_size
+        V = v_pool[vis // page_size, :, slot // B, :, slot % B].astype(np.float64)   # [n][Hkv][D]
         for g in range(n_kv):
             Qg = q64[i, g * G:(g + 1) * G, :]
             z = scale64 * (Qg @ K[:, g, :].T)

@@ -21,6 +21,9 @@ def reshape_and_cache(k_pool, v_pool, k_new, v_new, slot_mapping):
     k_out = np.array(k_pool, copy=True)
     v_out = np.array(v_pool, copy=True)
     page_size = k_out.shape[2]
+    B = min(page_size, 32)   # V pages hold their slots in blocks of B, slot innermost
+    if tuple(v_out.shape) != (k_out.shape[0], k_out.shape[1], page_size // B, k_out.shape[3], B):
+        raise ValueError("V pool shape does not match the K pool")
     kn = np.asarray(k_new)
     vn = np.asarray(v_new)
     if kn.dtype != np.float16:
@@ -36,7 +39,7 @@ def reshape_and_cache(k_pool, v_pool, k_new, v_new, slot_mapping):
             continue
         page, off = int(s) // page_size, int(s) % page_size
         k_out[page, :, off, :] = kn[i]
-        v_out[page, :, :, off] = vn[i]
+        v_out[page, :, off // B, :, off % B] = vn[i]
     return k_out, v_out
 
 

@@ -8,7 +8,8 @@ is missing, every call raises.
 
 Cache layout (one layer), binary16:
     K cache [num_pages][n_kv_heads][page_size][head_dim]
-    V cache [num_pages][n_kv_heads][head_dim][page_size]
+    V cache [num_pages][n_kv_heads][page_size // T][head_dim][T], T = min(page_size, 32)
+            (v_slot_tile(page_size)): slots in blocks of T, each block slot-innermost
 """
 from __future__ import annotations
 
@@ -121,11 +122,23 @@ def _dev(t, dtype, name, ndim=None):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def v_slot_tile(page_size: int) -> int:
+    """Slots per block of a V page (the library's kVSlotTile, 32, or the page)."""
+    return min(int(page_size), 32)
+
+
+def v_cache_shape(num_pages: int, n_kv_heads: int, page_size: int, head_dim: int):
+    """Shape of a V cache for a K cache [num_pages][n_kv_heads][page_size][head_dim]."""
+    T = v_slot_tile(page_size)
+    return (int(num_pages), int(n_kv_heads), int(page_size) // T, int(head_dim), T)
+
+
 def cache_desc(k_cache, v_cache=None) -> CacheDesc:
-    """Descriptor of a K cache [N][Hkv][P][D] (checked against V [N][Hkv][D][P])."""
+    """Descriptor of a K cache [N][Hkv][P][D] (checked against V [N][Hkv][P/T][D][T])."""
     N, H, P, D = (int(x) for x in k_cache.shape)
-    if v_cache is not None and tuple(v_cache.shape) != (N, H, D, P):
-        raise ValueError(f"V cache shape {tuple(v_cache.shape)} does not match K cache {N, H, P, D}")
+    if v_cache is not None and tuple(v_cache.shape) != v_cache_shape(N, H, P, D):
+        raise ValueError(f"V cache shape {tuple(v_cache.shape)} does not match K cache {N, H, P, D}: "
+                         f"expected {v_cache_shape(N, H, P, D)}")
     return CacheDesc(N, P, H, D)
 
 
@@ -256,7 +269,7 @@ def pa_reshape_and_cache(k_cache, v_cache, k_new, v_new, slot_mapping, stream=No
     import torch
     desc = cache_desc(k_cache, v_cache)
     _dev(k_cache, torch.float16, "k_cache", 4)
-    _dev(v_cache, torch.float16, "v_cache", 4)
+    _dev(v_cache, torch.float16, "v_cache", 5)
     T = int(slot_mapping.shape[0])
     if k_new.dtype not in (torch.float16, torch.float32) or v_new.dtype != k_new.dtype:
         raise TypeError("k_new/v_new must both be float16 or both float32")
@@ -280,7 +293,7 @@ def pa_copy_blocks(k_caches, v_caches, pairs, stream=None) -> None:
         if tuple(k.shape) != tuple(k_caches[0].shape) or tuple(v.shape) != tuple(v_caches[0].shape):
             raise ValueError("all layers must have the same cache shape")
         _dev(k, torch.float16, "k_cache", 4)
-        _dev(v, torch.float16, "v_cache", 4)
+        _dev(v, torch.float16, "v_cache", 5)
     p = _host_i32(pairs).reshape(-1, 2)
     n_layers = len(k_caches)
     kp = (ctypes.c_void_p * n_layers)(*[k.data_ptr() for k in k_caches])
@@ -300,7 +313,7 @@ def pa_swap_blocks(k_caches, v_caches, k_host, v_host, pairs, to_host: bool, str
     n_host = int(k_host[0].shape[0])
     for k, v, kh, vh in zip(k_caches, v_caches, k_host, v_host):
         _dev(k, torch.float16, "k_cache", 4)
-        _dev(v, torch.float16, "v_cache", 4)
+        _dev(v, torch.float16, "v_cache", 5)
         for h, d in ((kh, k), (vh, v)):
             if not h.is_pinned() or h.dtype != torch.float16 or tuple(h.shape[1:]) != tuple(d.shape[1:]) \
                     or int(h.shape[0]) != n_host or not h.is_contiguous():
@@ -344,7 +357,7 @@ def pa_decode(q, k_cache, v_cache, block_tables, kv_lens, scale: float, kv_lens_
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(_L().pa_decode(
         ctypes.byref(desc), _dev(k_cache, torch.float16, "k_cache", 4),
-        _dev(v_cache, torch.float16, "v_cache", 4), _dev(q, torch.float32, "q", 3),
+        _dev(v_cache, torch.float16, "v_cache", 5), _dev(q, torch.float32, "q", 3),
         _dev(out, torch.float32, "out", 3), _dev(block_tables, torch.int32, "block_tables", 2),
         _dev(kv_lens, torch.int32, "kv_lens", 1), _i32p(kl), S, max_pages, Hq, float(scale),
         int(partition_tokens), ws_ptr, ws_bytes, _stream_ptr(stream)))
@@ -387,7 +400,7 @@ def pa_prefill(q, k_cache, v_cache, block_tables, token_row, token_kv_len, token
     n_rows, max_pages = (int(x) for x in block_tables.shape)
     _check(_L().pa_prefill(
         ctypes.byref(desc), _dev(k_cache, torch.float16, "k_cache", 4),
-        _dev(v_cache, torch.float16, "v_cache", 4), _dev(q, torch.float32, "q", 3),
+        _dev(v_cache, torch.float16, "v_cache", 5), _dev(q, torch.float32, "q", 3),
         _dev(out, torch.float32, "out", 3), _dev(block_tables, torch.int32, "block_tables", 2),
         _dev(token_row, torch.int32, "token_row", 1), _dev(token_kv_len, torch.int32, "token_kv_len", 1),
         _dev(token_pos, torch.int32, "token_pos", 1), _i32p(rh), _i32p(kh), _i32p(ph), T, n_rows,
@@ -420,7 +433,7 @@ def pa_unified_attention(q, k_cache, v_cache, span: int, cell_seq, cell_pos, tok
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(_L().pa_unified_attention(
         ctypes.byref(desc), _dev(k_cache, torch.float16, "k_cache", 4),
-        _dev(v_cache, torch.float16, "v_cache", 4), _dev(q, torch.float32, "q", 3),
+        _dev(v_cache, torch.float16, "v_cache", 5), _dev(q, torch.float32, "q", 3),
         _dev(out, torch.float32, "out", 3), int(span), _dev(cell_seq, torch.int32, "cell_seq", 1),
         _dev(cell_pos, torch.int32, "cell_pos", 1), _dev(token_seq, torch.int32, "token_seq", 1),
         _dev(token_pos, torch.int32, "token_pos", 1), T, Hq, float(scale), int(kv_splits), ws_ptr,

@@ -93,7 +93,8 @@ __global__ __launch_bounds__(kRcThreads) void reshape_and_cache_kernel(
         if (run) {
             const int64_t page = s0 >> page_shift;
             const int off = s0 & (P - 1);
-            *reinterpret_cast<u32x4*>(v_cache + ((page * n_kv_heads + h) * D + d) * P + off) =
+            // 8 consecutive slots from an 8-aligned one lie in one slot block
+            *reinterpret_cast<u32x4*>(v_cache + v_elem_offset(page, h, d, off, n_kv_heads, P, D)) =
                 *reinterpret_cast<const u32x4*>(&sv[d * kRow + 8 * g]);
         } else {
 #pragma unroll
@@ -101,7 +102,7 @@ __global__ __launch_bounds__(kRcThreads) void reshape_and_cache_kernel(
                 const int32_t sj = sslot[8 * g + j];
                 if (sj < 0) continue;
                 const int64_t page = sj >> page_shift;
-                v_cache[((page * n_kv_heads + h) * D + d) * P + (sj & (P - 1))] = sv[d * kRow + 8 * g + j];
+                v_cache[v_elem_offset(page, h, d, sj & (P - 1), n_kv_heads, P, D)] = sv[d * kRow + 8 * g + j];
             }
         }
     }

@@ -21,9 +21,10 @@
 //   score registers already in the B-operand layout of the P.V product.
 // * Token-to-row assignment inside a 32-token chunk is chosen so that lane
 //   group g (lanes 16g..16g+15) ends up holding tokens 8g..8g+7 of the chunk.
-//   The V cache keeps the slot innermost, so those 8 tokens of one value
-//   dimension are 16 contiguous bytes: one global_load_dwordx4 per lane per
-//   16 value dimensions, no transposition anywhere.
+//   The V cache keeps the slot innermost (in blocks of 32 slots), so those 8
+//   tokens of one value dimension are 16 contiguous bytes: one
+//   global_load_dwordx4 per lane per 16 value dimensions, no transposition
+//   anywhere, and a chunk's V is one contiguous block.
 // * Q (fp32) enters the score MFMA as a binary16 hi/lo pair (q = hi + lo), two
 //   MFMAs per block, so Q is carried to ~22 bits; P is rounded to binary16 for
 //   the P.V product and the row sum uses the same rounded values.
@@ -140,6 +141,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_partition_kernel(DecodeArg
     }
 
     const int64_t page_elems = (int64_t)Hkv * P * D;   // one page of one cache, all heads
+    const int VT = v_slot_tile(P);                      // slots per V block
     const uint16_t* kc = a.k_cache;
     const uint16_t* vc = a.v_cache;
     // token row of this lane inside a chunk for K block 0 (block 1 is +4)
@@ -160,8 +162,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode_partition_kernel(DecodeArg
         }
         int tv = c0 + 8 * g;
         if (tv > L - 1) tv = (L - 1) & ~7;
-        const uint16_t* vrow = vc + page_of(tv) * page_elems + ((kvh * D + m16) * P + (tv & (P - 1)));
-        const int64_t vstep = idle ? 0 : (int64_t)16 * P;
+        // tokens tv..tv+7 (8-aligned) lie in one V slot block: value dims
+        // m16, m16+16, ... are rows T elements apart
+        const int vslot = tv & (P - 1);
+        const uint16_t* vrow = vc + page_of(tv) * page_elems +
+                               (((int64_t)kvh * P + (vslot & ~(VT - 1))) * D + m16 * VT + (vslot & (VT - 1)));
+        const int64_t vstep = idle ? 0 : (int64_t)16 * VT;
         if (idle) vrow = vc;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) r.v[nb] = ld16(vrow + nb * vstep);

@@ -7,6 +7,27 @@
 
 namespace pa {
 
+// ---- V page layout ----------------------------------------------------------
+// A V page of one KV head holds its slots in blocks of T = min(P, kVSlotTile)
+// consecutive slots, each block a [head_dim][T] array (slot innermost), blocks
+// in slot order.  Every 32-token run that a decode chunk or half a prefill
+// tile reads is then one contiguous 8 KiB block (D = 128), where a [D][P] page
+// would give it 64-byte pieces on a 2P-byte stride.  For P <= 32 this is the
+// [D][P] page.
+constexpr int kVSlotTile = 32;
+
+__host__ __device__ inline int v_slot_tile(int page_size) {
+    return page_size < kVSlotTile ? page_size : kVSlotTile;
+}
+
+// element offset of V(page, KV head h, value dim d, slot) in a V cache
+__host__ __device__ inline int64_t v_elem_offset(int64_t page, int h, int d, int slot, int n_kv_heads,
+                                                 int page_size, int head_dim) {
+    const int T = v_slot_tile(page_size);
+    return ((page * n_kv_heads + h) * page_size + (slot & ~(T - 1))) * head_dim + (int64_t)d * T +
+           (slot & (T - 1));
+}
+
 // ---- reshape_and_cache / copy_blocks -------------------------------------
 
 hipError_t launch_reshape_and_cache(void* k_cache, void* v_cache, const void* k_new,

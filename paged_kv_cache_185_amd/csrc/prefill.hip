@@ -258,10 +258,13 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, Til
         const int id = tid + kThreads * i;
         koff[i] = (id / CPR) * D + 8 * (id % CPR);
     }
+    // (one-page tiles: P is a multiple of 64, so V slot blocks hold 32 slots
+    // and the tile's 64 keys are two consecutive blocks)
 #pragma unroll
     for (int i = 0; i < StagingV<D>::VC; ++i) {
         const int id = tid + kThreads * i;
-        voff[i] = (id >> 3) * P + 8 * (id & 7);
+        const int c = id & 7;
+        voff[i] = (c >> 2) * (kVSlotTile * D) + (id >> 3) * kVSlotTile + 8 * (c & 3);
     }
     auto load_meta_k = [&](int t0, StagingK<D>& st) __attribute__((always_inline)) {
         if constexpr (UNIFIED) {
@@ -300,7 +303,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, Til
     auto load_v_page = [&](int t0, int page, StagingV<D>& st) __attribute__((always_inline)) {
         st.t0 = t0;
         load_meta_v(t0, st);
-        const uint16_t* vb = vc + page * page_elems + (k_head_off + (t0 & (P - 1)));
+        const uint16_t* vb = vc + page * page_elems + (k_head_off + (int64_t)(t0 & (P - 1)) * D);
 #pragma unroll
         for (int i = 0; i < StagingV<D>::VC; ++i) st.v[i] = *reinterpret_cast<const u32x4*>(vb + voff[i]);
     };
@@ -333,11 +336,15 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, Til
             const int tb = t0 + 8 * c;
             const int tv = tb < kv_end ? tb : ((kv_end - 1) & ~7);
             const int vpage = sm_pages[(tv >> sh) - page_base];
-            const uint16_t* vbase = vc + vpage * page_elems + (k_head_off + (tv & (P - 1)));
+            // keys tv..tv+7 (8-aligned) lie in one V slot block of VT slots
+            const int VT = v_slot_tile(P);
+            const int vslot = tv & (P - 1);
+            const uint16_t* vbase = vc + vpage * page_elems +
+                                    (k_head_off + (int64_t)(vslot & ~(VT - 1)) * D + (vslot & (VT - 1)));
 #pragma unroll
             for (int i = 0; i < StagingV<D>::VC; ++i) {
                 const int d = (tid + kThreads * i) >> 3;
-                st.v[i] = *reinterpret_cast<const u32x4*>(vbase + d * P);
+                st.v[i] = *reinterpret_cast<const u32x4*>(vbase + d * VT);
             }
         }
     };

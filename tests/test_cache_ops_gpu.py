@@ -46,7 +46,7 @@ def test_reshape_and_cache_f32_rounding_golden():
     kh, vh = bits16(to_host(kd)), bits16(to_host(vd))
     for i in range(n):
         assert np.all(kh[i, 0, 0, :] == want[i]), (g["cases"][i], hex(kh[i, 0, 0, 0]))
-        assert np.all(vh[i, 0, :, 0] == want[i]), g["cases"][i]
+        assert np.all(vh[i, 0, 0, :, 0] == want[i]), g["cases"][i]   # slot 0: block 0, column 0
     nan_in = np.array([int(x, 16) for x in g["nan"]], dtype=np.uint32).view(np.float32)
     src = np.repeat(nan_in[:, None, None], D, axis=2).astype(np.float32)
     k, v = W.nan_pools(len(nan_in), 1, 16, D)
@@ -55,7 +55,7 @@ def test_reshape_and_cache_f32_rounding_golden():
     kd, vd = to_dev(k), to_dev(v)
     pa.pa_reshape_and_cache(kd, vd, to_dev(src), to_dev(src),
                             to_dev(np.arange(len(nan_in), dtype=np.int32) * 16))
-    assert np.all(np.isnan(to_host(kd)[:, 0, 0, :])) and np.all(np.isnan(to_host(vd)[:, 0, :, 0]))
+    assert np.all(np.isnan(to_host(kd)[:, 0, 0, :])) and np.all(np.isnan(to_host(vd)[:, 0, 0, :, 0]))
 
 
 def test_reshape_and_cache_f32_random_matches_numpy_rounding():
@@ -118,7 +118,7 @@ def test_copy_blocks_bitwise(n_layers):
     rng = np.random.default_rng(n_layers)
     N, H, P, D = 40, 8, 128, 128
     ks = [rng.standard_normal((N, H, P, D)).astype(np.float16) for _ in range(n_layers)]
-    vs = [rng.standard_normal((N, H, D, P)).astype(np.float16) for _ in range(n_layers)]
+    vs = [W.v_blocks_from_columns(rng.standard_normal((N, H, D, P)).astype(np.float16)) for _ in range(n_layers)]
     for k in ks:
         k.view(np.uint16)[3] = W.NAN_F16_BITS      # NaN payloads must survive
     pairs = np.array([[3, 10], [5, 11], [5, 12], [39, 0]], dtype=np.int32)
@@ -137,7 +137,7 @@ def test_copy_blocks_many_pairs_and_layers():
     N, H, P, D = 400, 1, 16, 64
     L = 40
     ks = [rng.standard_normal((N, H, P, D)).astype(np.float16) for _ in range(L)]
-    vs = [rng.standard_normal((N, H, D, P)).astype(np.float16) for _ in range(L)]
+    vs = [W.v_blocks_from_columns(rng.standard_normal((N, H, D, P)).astype(np.float16)) for _ in range(L)]
     perm = rng.permutation(N)
     pairs = np.stack([perm[:150], perm[150:300]], axis=1).astype(np.int32)
     kd = [to_dev(k) for k in ks]

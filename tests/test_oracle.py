@@ -22,6 +22,22 @@ GOLD = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
 # ----------------------------------------------------------------- brute force
 
+def vcol(v_pool, page, h, slot):
+    """Value column of (page, KV head h, slot) read from V storage
+    [N][Hkv][P // B][D][B], B = min(P, 32), written out independently of the
+    oracle's gather."""
+    P = v_pool.shape[2] * v_pool.shape[4]
+    B = min(P, 32)
+    assert v_pool.shape[4] == B
+    return v_pool[page, h, slot // B, :, slot % B]
+
+
+def vcols(v_pool):
+    """V storage [N][Hkv][P // B][D][B] as value columns [N][Hkv][D][P] (a copy)."""
+    N, H, nb, D, B = v_pool.shape
+    return v_pool.transpose(0, 1, 3, 2, 4).reshape(N, H, D, nb * B)
+
+
 def brute_force(q, k_pool, v_pool, block_tables, token_row, token_kv_len, token_pos, scale):
     """Scalar definition.  Inverts the block tables (physical cell -> (row, logical
     position)) instead of gathering, then loops with math.fsum / math.exp."""
@@ -53,7 +69,7 @@ def brute_force(q, k_pool, v_pool, block_tables, token_row, token_kv_len, token_
             w = [math.exp(x - m) for x in z]
             den = math.fsum(w)
             for d in range(D):
-                out[i, h, d] = math.fsum(w[c] * float(v_pool[cells[c][1], g, d, cells[c][2]])
+                out[i, h, d] = math.fsum(w[c] * float(vcol(v_pool, cells[c][1], g, cells[c][2])[d])
                                          for c in range(n)) / den
     return out
 
@@ -86,12 +102,47 @@ def test_brute_force_small_prefill(order):
     np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-13)
 
 
+@pytest.mark.parametrize("P", [64, 128])
+def test_brute_force_multi_block_v_pages(P):
+    """Pages of more than one V slot block (P > 32), with ragged last pages and
+    NaN in their unused cells: the oracle's gather of blocked V storage against
+    the brute force's own cell-by-cell reading."""
+    rng = np.random.default_rng(12 + P)
+    c = W.make_decode_case(rng, "blocks", 4, 2, 8, P, [P + 37, 2 * P - 5, 33], 9)
+    got = oracle.paged_decode(c.q, c.k_pool, c.v_pool, c.block_tables, c.kv_lens, c.scale)
+    ref = brute_force(c.q, c.k_pool, c.v_pool, c.block_tables, np.arange(3), c.kv_lens,
+                      c.kv_lens - 1, c.scale)
+    assert np.all(np.isfinite(got))
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-13)
+
+
+def test_reshape_then_gather_round_trip_multi_block():
+    """Tokens scattered by reshape_and_cache into 128-slot pages come back in
+    order from the oracle's gather (both read the blocked V storage, each in
+    its own code), and the V cell of slot s holds token s's value column."""
+    rng = np.random.default_rng(13)
+    N, Hkv, P, D = 5, 2, 128, 8
+    k, v = W.nan_pools(N, Hkv, P, D)
+    T = 300
+    kn = rng.standard_normal((T, Hkv, D)).astype(np.float16)
+    vn = rng.standard_normal((T, Hkv, D)).astype(np.float16)
+    pages = np.array([3, 0, 4])
+    slots = (pages[np.arange(T) // P] * P + np.arange(T) % P).astype(np.int32)
+    k2, v2 = oracle.reshape_and_cache(k, v, kn, vn, slots)
+    K, V = oracle.gather_logical(k2, v2, pages, T)
+    np.testing.assert_array_equal(K, kn.astype(np.float64))
+    np.testing.assert_array_equal(V, vn.astype(np.float64))
+    for t in (0, 31, 32, 63, 64, 127, 128, 200, 299):
+        for h in range(Hkv):
+            np.testing.assert_array_equal(vcol(v2, pages[t // P], h, t % P), vn[t, h])
+
+
 def test_brute_force_shared_pages():
     """Two rows whose tables share their first page (a forked prefix)."""
     rng = np.random.default_rng(11)
     N, Hkv, P, D = 8, 1, 4, 16
     k = rng.standard_normal((N, Hkv, P, D)).astype(np.float16)
-    v = rng.standard_normal((N, Hkv, D, P)).astype(np.float16)
+    v = W.v_blocks_from_columns(rng.standard_normal((N, Hkv, D, P)).astype(np.float16))
     bt = np.array([[6, 1, -1], [6, 3, 0]], dtype=np.int32)
     q = rng.standard_normal((2, 2, D)).astype(np.float32)
     lens = np.array([7, 10], dtype=np.int32)
@@ -108,7 +159,7 @@ def _hand_pool(g):
     for c in pool["cells"]:
         for h in range(pool["n_kv_heads"]):
             k[c["page"], h, c["slot"], :] = c["k"][h]
-            v[c["page"], h, :, c["slot"]] = c["v"][h]
+            vcol(v, c["page"], h, c["slot"])[:] = c["v"][h]
     return k, v, np.array(pool["block_table"], dtype=np.int32)
 
 
@@ -142,7 +193,8 @@ def test_sdpa_single_page(Hq, Hkv, D, L):
     rng = np.random.default_rng(L)
     P = 128
     k = rng.standard_normal((3, Hkv, P, D)).astype(np.float16)
-    v = rng.standard_normal((3, Hkv, D, P)).astype(np.float16)
+    v_cols = rng.standard_normal((3, Hkv, D, P)).astype(np.float16)   # value columns per slot
+    v = W.v_blocks_from_columns(v_cols)
     bt = np.array([[2]], dtype=np.int32)
     T = 5
     q = rng.standard_normal((T, Hq, D)).astype(np.float32)
@@ -150,7 +202,7 @@ def test_sdpa_single_page(Hq, Hkv, D, L):
     got = oracle.paged_attention(q, k, v, bt, np.zeros(T, np.int32), np.full(T, L, np.int32),
                                  pos, 1.0 / math.sqrt(D))
     K = k[2, :, :L, :].transpose(1, 0, 2).astype(np.float64)
-    V = v[2, :, :, :L].transpose(2, 0, 1).astype(np.float64)
+    V = v_cols[2, :, :, :L].transpose(2, 0, 1).astype(np.float64)
     mask = np.arange(L)[None, :] <= pos[:, None]
     ref = _sdpa(q, K, V, Hq // Hkv, 1.0 / math.sqrt(D), mask)
     np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-13)
@@ -168,7 +220,7 @@ def test_closed_form_single_key():
     out = oracle.paged_decode(c.q, c.k_pool, c.v_pool, c.block_tables, c.kv_lens, c.scale)
     page = c.block_tables[0, 0]
     for h in range(4):
-        np.testing.assert_array_equal(out[0, h], c.v_pool[page, h // 2, :, 0].astype(np.float64))
+        np.testing.assert_array_equal(out[0, h], vcol(c.v_pool, page, h // 2, 0).astype(np.float64))
 
 
 def test_closed_form_zero_query_is_mean():
@@ -177,7 +229,8 @@ def test_closed_form_zero_query_is_mean():
     out = oracle.paged_decode(q, c.k_pool, c.v_pool, c.block_tables, c.kv_lens, c.scale)
     # independent computation of the mean from the physical pool
     P = 8
-    vals = np.stack([c.v_pool[c.block_tables[0, t // P], :, :, t % P] for t in range(29)])
+    vals = np.stack([[vcol(c.v_pool, c.block_tables[0, t // P], g, t % P) for g in range(2)]
+                     for t in range(29)])
     for h in range(4):
         np.testing.assert_allclose(out[0, h], vals[:, h // 2, :].astype(np.float64).mean(0),
                                    rtol=1e-13, atol=1e-14)
@@ -194,15 +247,16 @@ def test_closed_form_identical_keys_is_mean_and_constant_v():
         kg = k[:, g]                                        # [N][P][D]
         kg[valid] = row
     out = oracle.paged_decode(c.q, k, c.v_pool, c.block_tables, c.kv_lens, c.scale)
-    vals = np.stack([c.v_pool[c.block_tables[0, t // 8], :, :, t % 8] for t in range(21)])
+    vals = np.stack([[vcol(c.v_pool, c.block_tables[0, t // 8], g, t % 8) for g in range(2)]
+                     for t in range(21)])
     for h in range(4):
         np.testing.assert_allclose(out[0, h], vals[:, h // 2].astype(np.float64).mean(0),
                                    rtol=1e-13, atol=1e-14)
     # constant V (value depends on the KV head) -> that constant, whatever the keys
     v = c.v_pool.copy()
     for g in range(2):
-        vg = v[:, g].transpose(0, 2, 1)                     # view [N][P][D]
-        vg[valid] = np.float16(0.5 * (g + 1))
+        for page, slot in zip(*np.nonzero(valid)):
+            vcol(v, page, g, slot)[:] = np.float16(0.5 * (g + 1))
     out = oracle.paged_decode(c.q, c.k_pool, v, c.block_tables, c.kv_lens, c.scale)
     for h in range(4):
         np.testing.assert_allclose(out[0, h], 0.5 * (h // 2 + 1), rtol=1e-14)
@@ -314,14 +368,14 @@ def test_reshape_and_cache_touches_only_addressed_cells():
     rng = np.random.default_rng(8)
     N, Hkv, P, D = 10, 3, 8, 16
     k = rng.standard_normal((N, Hkv, P, D)).astype(np.float16)
-    v = rng.standard_normal((N, Hkv, D, P)).astype(np.float16)
+    v = W.v_blocks_from_columns(rng.standard_normal((N, Hkv, D, P)).astype(np.float16))
     T = 7
     kn = rng.standard_normal((T, Hkv, D)).astype(np.float16)
     vn = rng.standard_normal((T, Hkv, D)).astype(np.float16)
     slots = np.array([3, 17, -1, 79, 40, -5, 8], dtype=np.int32)
     k2, v2 = oracle.reshape_and_cache(k, v, kn, vn, slots)
     kb, k2b = k.view(np.uint16), k2.view(np.uint16)
-    vb, v2b = v.view(np.uint16), v2.view(np.uint16)
+    vb, v2b = vcols(v).view(np.uint16), vcols(v2).view(np.uint16)
     touched = np.zeros((N, P), dtype=bool)
     for i, s in enumerate(slots):
         if s < 0:
@@ -475,7 +529,8 @@ def brute_force_unified(q, k_pool, v_pool, span, cell_seq, cell_pos, token_seq, 
             w = [math.exp(x - m) for x in z]
             den = math.fsum(w)
             for d in range(D):
-                out[i, h, d] = math.fsum(wt * float(v_pool[c // P, g, d, c % P]) for wt, c in zip(w, cells)) / den
+                out[i, h, d] = math.fsum(wt * float(vcol(v_pool, c // P, g, c % P)[d])
+                                         for wt, c in zip(w, cells)) / den
     return out
 
 
@@ -506,7 +561,7 @@ def test_unified_brute_force_with_padding_and_free_cells():
     rng = np.random.default_rng(31)
     N, Hkv, P, D, Hq = 6, 2, 4, 8, 4
     k = rng.standard_normal((N, Hkv, P, D)).astype(np.float16)
-    v = rng.standard_normal((N, Hkv, D, P)).astype(np.float16)
+    v_cols = rng.standard_normal((N, Hkv, D, P)).astype(np.float16)   # value columns per slot
     span = 22
     cs = rng.integers(-1, 3, size=span).astype(np.int32)   # three sequences and free cells
     cp = np.zeros(span, dtype=np.int32)
@@ -515,7 +570,8 @@ def test_unified_brute_force_with_padding_and_free_cells():
         cp[idx] = rng.permutation(len(idx))                # positions scattered over the span
     for c in np.nonzero(cs < 0)[0]:
         k[c // P, :, c % P, :] = np.nan
-        v[c // P, :, :, c % P] = np.nan
+        v_cols[c // P, :, :, c % P] = np.nan
+    v = W.v_blocks_from_columns(v_cols)
     T = 7
     ts = np.array([0, 1, 2, -1, 0, 2, 1], dtype=np.int32)
     tp = np.array([int((cs == s).sum()) - 1 if s >= 0 else 0 for s in ts], dtype=np.int32)

@@ -97,7 +97,8 @@ class Server:
 
 def logical_pools(tkv, toks_list, P):
     """Each request's K/V from its tokens alone, in private pages 0.. of a host
-    pool, with the identity block table (the oracle's view)."""
+    pool, with the identity block table (the oracle's view).  V is filled as
+    value columns [N][Hkv][D][P] and returned in V storage order."""
     n_pages = [-(-len(t) // P) for t in toks_list]
     N = sum(n_pages)
     k = np.zeros((N, HKV, P, D), np.float16)
@@ -112,7 +113,7 @@ def logical_pools(tkv, toks_list, P):
             v[base + j, :, :, :len(c)] = vv[j * P:(j + 1) * P].transpose(1, 2, 0)
             bt[i, j] = base + j
         base += n_pages[i]
-    return k, v, bt
+    return k, W.v_blocks_from_columns(v), bt
 
 
 @pytest.mark.parametrize("P", [16, 128])

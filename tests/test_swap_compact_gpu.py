@@ -25,7 +25,7 @@ def test_swap_blocks_bitwise_round_trip(n_layers):
     rng = np.random.default_rng(70 + n_layers)
     N, H, P, D, NH = 24, 4, 32, 128, 10
     ks = [rng.standard_normal((N, H, P, D)).astype(np.float16) for _ in range(n_layers)]
-    vs = [rng.standard_normal((N, H, D, P)).astype(np.float16) for _ in range(n_layers)]
+    vs = [W.v_blocks_from_columns(rng.standard_normal((N, H, D, P)).astype(np.float16)) for _ in range(n_layers)]
     kd, vd = [to_dev(k) for k in ks], [to_dev(v) for v in vs]
     kh = [pinned_like(k, NH) for k in kd]
     vh = [pinned_like(v, NH) for v in vd]

@@ -27,7 +27,7 @@ NAN_F16_BITS = np.uint16(0x7E00)
 
 __all__ = [
     "NAN_F16_BITS", "DecodeCase", "PrefillCase", "ChunkedPrefill", "SharingCase",
-    "rng_for", "poison_pools", "make_decode_case", "make_prefill_case",
+    "rng_for", "poison_pools", "v_block", "v_blocks_from_columns", "make_decode_case", "make_prefill_case",
     "tiny_decode", "qwen3_decode", "ua_prefill", "varlen_decode", "sharing_case",
     "chunked_prefill", "decode_valid_bytes", "attention_flops", "prefill_pairs",
     "fp32_scale",
@@ -63,18 +63,35 @@ def poison_pools(k_pool: np.ndarray, v_pool: np.ndarray, valid_cells: np.ndarray
     kb = k_pool.view(np.uint16)
     vb = v_pool.view(np.uint16)
     kb[np.broadcast_to(bad[:, None, :, None], kb.shape)] = NAN_F16_BITS
-    vb[np.broadcast_to(bad[:, None, None, :], vb.shape)] = NAN_F16_BITS
+    n, _, nblk, _, blk = vb.shape
+    vbad = bad.reshape(n, nblk, blk)   # slot s -> (block s // B, s % B)
+    vb[np.broadcast_to(vbad[:, None, :, None, :], vb.shape)] = NAN_F16_BITS
+
+
+def v_block(page_size: int) -> int:
+    """Slots per block of a V page: V storage is [N][Hkv][P // B][D][B], B = min(P, 32)."""
+    return min(int(page_size), 32)
 
 
 def _pool_shapes(n_pages, n_kv_heads, page_size, head_dim):
+    B = v_block(page_size)
     return ((n_pages, n_kv_heads, page_size, head_dim),
-            (n_pages, n_kv_heads, head_dim, page_size))
+            (n_pages, n_kv_heads, page_size // B, head_dim, B))
+
+
+def v_blocks_from_columns(v: np.ndarray) -> np.ndarray:
+    """V pages given as value columns ``[N][Hkv][D][P]`` in V storage order
+    ``[N][Hkv][P // B][D][B]``."""
+    n, h, d, p = v.shape
+    B = v_block(p)
+    return np.ascontiguousarray(v.reshape(n, h, d, p // B, B).transpose(0, 1, 3, 2, 4))
 
 
 def _draw_pools(rng, n_pages, n_kv_heads, page_size, head_dim, std):
-    ks, vs = _pool_shapes(n_pages, n_kv_heads, page_size, head_dim)
+    ks, _ = _pool_shapes(n_pages, n_kv_heads, page_size, head_dim)
     k = _normal_f16(rng, ks, std)
-    v = _normal_f16(rng, vs, std)
+    # drawn as value columns [N][Hkv][D][P], then stored in V page order
+    v = v_blocks_from_columns(_normal_f16(rng, (n_pages, n_kv_heads, head_dim, page_size), std))
     return k, v
 
 
@@ -109,7 +126,7 @@ class DecodeCase:
     num_pages: int
     q: np.ndarray             # float32 [S][Hq][D]
     k_pool: np.ndarray        # float16 [N][Hkv][P][D]
-    v_pool: np.ndarray        # float16 [N][Hkv][D][P]
+    v_pool: np.ndarray        # float16 [N][Hkv][P // B][D][B], B = min(P, 32)
     block_tables: np.ndarray  # int32 [S][max_pages], -1 padded
     kv_lens: np.ndarray       # int32 [S]
     scale: np.float32
