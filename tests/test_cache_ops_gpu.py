@@ -15,7 +15,7 @@ pytestmark = pytest.mark.gpu
 GOLD = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
 
-@pytest.mark.parametrize("P,D,H", [(16, 64, 2), (128, 128, 8), (32, 128, 1)])
+@pytest.mark.parametrize("P,D,H", [(16, 64, 2), (128, 128, 8), (32, 128, 1), (1024, 64, 2)])
 def test_reshape_and_cache_f16_bitwise(P, D, H):
     rng = np.random.default_rng(P + D + H)
     N = 24

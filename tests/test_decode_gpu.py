@@ -38,6 +38,9 @@ CASES = [
     (16, 1, 128, 32, [700, 31, 32, 96]),
     (16, 2, 64, 64, [5, 511, 513, 2100]),
     (8, 4, 128, 256, [257, 1, 600]),
+    # pages of 16 and 32 V slot blocks: lengths around block and page edges
+    (4, 4, 64, 512, [700, 513, 31]),
+    (8, 2, 128, 1024, [1, 32, 33, 1500, 2049]),
 ]
 
 

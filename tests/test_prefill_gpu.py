@@ -36,6 +36,8 @@ CASES = [
     (16, 1, 64, 32, [100], [20], "grouped"),
     (16, 2, 128, 128, [700, 5], [33, 61], "round_robin"),
     (32, 4, 64, 16, [64, 65], [31, 2], "grouped"),
+    (16, 4, 128, 256, [300, 0], [100, 37], "round_robin"),
+    (8, 2, 64, 1024, [1100, 5], [40, 70], "grouped"),
 ]
 
 
