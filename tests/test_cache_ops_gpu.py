@@ -153,3 +153,39 @@ def test_copy_blocks_rejects_overlap():
     k, v = W.nan_pools(8, 1, 16, 64)
     with pytest.raises(pa.InvalidError):
         pa.pa_copy_blocks([to_dev(k)], [to_dev(v)], [[1, 2], [2, 3]])
+
+
+def test_empty_inputs_are_noops():
+    """Zero sequences, zero tokens and zero pairs return without launching and
+    leave every buffer as it was; a ubatch made only of padding tokens gives
+    zero rows."""
+    rng = np.random.default_rng(77)
+    c = W.make_decode_case(rng, "empty", 8, 2, 64, 16, [40, 3], 12)
+    kd, vd = to_dev(c.k_pool), to_dev(c.v_pool)
+    D, Hq = c.head_dim, c.n_q_heads
+    q0 = torch.zeros((0, Hq, D), dtype=torch.float32, device="cuda")
+    bt0 = torch.zeros((0, c.block_tables.shape[1]), dtype=torch.int32, device="cuda")
+    i0 = torch.zeros(0, dtype=torch.int32, device="cuda")
+    out = pa.pa_decode(q0, kd, vd, bt0, i0, float(c.scale), kv_lens_host=np.zeros(0, np.int32))
+    assert out.shape == (0, Hq, D)
+    out = pa.pa_prefill(q0, kd, vd, to_dev(c.block_tables), i0, i0, i0, float(c.scale),
+                        token_row_host=np.zeros(0, np.int32), token_kv_len_host=np.zeros(0, np.int32),
+                        token_pos_host=np.zeros(0, np.int32))
+    assert out.shape == (0, Hq, D)
+    kn0 = torch.zeros((0, c.n_kv_heads, D), dtype=torch.float16, device="cuda")
+    pa.pa_reshape_and_cache(kd, vd, kn0, kn0, i0)
+    pa.pa_copy_blocks([kd], [vd], np.zeros((0, 2), np.int32))
+    torch.cuda.synchronize()
+    assert np.array_equal(bits16(to_host(kd)), bits16(c.k_pool))
+    assert np.array_equal(bits16(to_host(vd)), bits16(c.v_pool))
+    # every token of the ubatch is padding (row -1): all rows zero, finite
+    T = 7
+    q = torch.from_numpy(rng.standard_normal((T, Hq, D)).astype(np.float32)).cuda()
+    row = np.full(T, -1, np.int32)
+    kvl = np.full(T, 40, np.int32)
+    pos = np.arange(T, dtype=np.int32)
+    for splits in (0, 1, 2):
+        got = to_host(pa.pa_prefill(q, kd, vd, to_dev(c.block_tables), to_dev(row), to_dev(kvl), to_dev(pos),
+                                    float(c.scale), token_row_host=row, token_kv_len_host=kvl,
+                                    token_pos_host=pos, kv_splits=splits))
+        assert np.all(got == 0), splits
