@@ -545,32 +545,45 @@ def bench_prefix(args, pa, torch, W):
     return res
 
 
-def cpu_baseline_decode(c, oracle):
-    t0 = time.perf_counter()
-    oracle.paged_decode(c.q, c.k_pool, c.v_pool, c.block_tables, c.kv_lens, c.scale)
-    return time.perf_counter() - t0
+def cpu_baseline_decode(c, oracle, min_seconds=8.0, max_steps=20):
+    """The oracle on whole decode steps of the batch, repeated until about
+    `min_seconds` of CPU work; returns (seconds, steps)."""
+    total, steps = 0.0, 0
+    while steps < max_steps and (steps == 0 or total < min_seconds):
+        t0 = time.perf_counter()
+        oracle.paged_decode(c.q, c.k_pool, c.v_pool, c.block_tables, c.kv_lens, c.scale)
+        total += time.perf_counter() - t0
+        steps += 1
+    return total, steps
 
 
-def cpu_baseline_prefill(cp, oracle, W, ubatch_index=None):
-    """The oracle on one prefill ubatch (sequence 0, chunk 8 by default), with the
-    pool filled on the host by the oracle's own reshape_and_cache."""
+def cpu_baseline_prefill(cp, oracle, W, ubatch_indices=(3, 11, 19, 27)):
+    """The oracle on a few ubatches of sequence 0 spread over the pass (contexts
+    of 2K to 14K tokens, like the pass's mix), each with the pool filled on the
+    host by the oracle's own reshape_and_cache (untimed); returns (seconds,
+    algorithmic flop, description)."""
     chunk = cp.chunk
-    j = min(8, cp.seq_len // chunk - 1) if ubatch_index is None else ubatch_index
-    p0 = j * chunk
-    n_ctx = p0 + chunk
-    n_pages = n_ctx // cp.page_size
-    k, v = W.nan_pools(n_pages, cp.n_kv_heads, cp.page_size, cp.head_dim)
-    slots = np.arange(n_ctx, dtype=np.int32)
-    k, v = oracle.reshape_and_cache(k, v, cp.k[0, :n_ctx], cp.v[0, :n_ctx], slots)
-    bt = np.arange(n_pages, dtype=np.int32)[None, :]
-    row = np.zeros(chunk, np.int32)
-    kvl = np.full(chunk, n_ctx, np.int32)
-    pos = np.arange(p0, p0 + chunk, dtype=np.int32)
-    t0 = time.perf_counter()
-    oracle.paged_attention(cp.q[0, p0:p0 + chunk], k, v, bt, row, kvl, pos, cp.scale)
-    dt = time.perf_counter() - t0
-    flops = W.attention_flops(W.prefill_pairs(kvl, pos), cp.n_q_heads, cp.head_dim)
-    return dt, flops, f"sequence 0, ubatch {j} ({chunk} tokens at positions {p0}..{p0 + chunk - 1})"
+    last = cp.seq_len // chunk - 1
+    js = sorted({min(j, last) for j in ubatch_indices})
+    total, flops = 0.0, 0
+    for j in js:
+        p0 = j * chunk
+        n_ctx = p0 + chunk
+        n_pages = n_ctx // cp.page_size
+        k, v = W.nan_pools(n_pages, cp.n_kv_heads, cp.page_size, cp.head_dim)
+        slots = np.arange(n_ctx, dtype=np.int32)
+        k, v = oracle.reshape_and_cache(k, v, cp.k[0, :n_ctx], cp.v[0, :n_ctx], slots)
+        bt = np.arange(n_pages, dtype=np.int32)[None, :]
+        row = np.zeros(chunk, np.int32)
+        kvl = np.full(chunk, n_ctx, np.int32)
+        pos = np.arange(p0, p0 + chunk, dtype=np.int32)
+        t0 = time.perf_counter()
+        oracle.paged_attention(cp.q[0, p0:p0 + chunk], k, v, bt, row, kvl, pos, cp.scale)
+        total += time.perf_counter() - t0
+        flops += W.attention_flops(W.prefill_pairs(kvl, pos), cp.n_q_heads, cp.head_dim)
+    what = (f"sequence 0, ubatches {', '.join(str(j) for j in js)} ({chunk} tokens each, contexts "
+            f"{(js[0] + 1) * chunk}..{(js[-1] + 1) * chunk})")
+    return total, flops, what
 
 
 def main():
@@ -657,14 +670,15 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
-        log("cpu baseline: oracle decode on the full batch")
-        dt = cpu_baseline_decode(c, oracle)
-        cpu = {"value": dec["valid_bytes"] / dt / 1e9, "unit": "GB/s", "kind": "oracle",
+        log("cpu baseline: oracle decode steps on the full batch")
+        dt, nsteps = cpu_baseline_decode(c, oracle)
+        cpu = {"value": dec["valid_bytes"] * nsteps / dt / 1e9, "unit": "GB/s", "kind": "oracle",
                "cores": blas_threads() or os.cpu_count(),
                "host_cpus": os.cpu_count(), "affinity": len(os.sched_getaffinity(0)),
-               "sample": "one decode step over all 8 sequences x 16384 tokens (the full batch)",
+               "sample": f"{nsteps} decode steps over all 8 sequences x 16384 tokens (the full batch)",
                "seconds": dt}
         if cp is not None:
+            log("cpu baseline: oracle prefill ubatches")
             dtp, fl, what = cpu_baseline_prefill(cp, oracle, W)
             cpu["prefill_tflops"] = fl / dtp / 1e12
             cpu["prefill_sample"] = what
