@@ -264,3 +264,68 @@ def test_chunked_prefill_concurrent_streams_bitwise(kv_splits):
         ref = oracle.paged_attention(cp.q[s, p0:p0 + cp.chunk][pick], kh, vh, u["bt"], u["row"][pick],
                                      u["kvl"][pick], u["pos"][pick], cp.scale)
         assert_attention_close(conc_outs[j][pick], ref, f"sequence {s} last ubatch")
+
+
+def test_chunked_prefill_full_size_in_the_benchmark_schedule():
+    """The timed prefill pass at full size (8 sequences x 16384 tokens, 512-token
+    ubatches) in the launch configuration the benchmark times: sequence s on
+    stream s, unsplit launches (kv_splits = 1), captured in one HIP graph and
+    replayed.  Sampled tokens of the first, a middle and the last ubatch are
+    checked against the oracle over a private host pool of their sequence."""
+    import torch
+    cp = W.chunked_prefill()
+    P, Hkv, D = cp.page_size, cp.n_kv_heads, cp.head_dim
+    pool = pa.Pool(cp.num_pages, P, cp.free_order)
+    seqs = [pool.seq_new() for _ in range(cp.n_seqs)]
+    k_pool, v_pool = W.nan_pools(cp.num_pages, Hkv, P, D)
+    kd, vd = to_dev(k_pool), to_dev(v_pool)
+    del k_pool, v_pool
+    qd, knd, vnd = to_dev(cp.q), to_dev(cp.k), to_dev(cp.v)
+    max_pages = cp.seq_len // P
+    ubs = []
+    for s, p0 in cp.ubatches():
+        n = cp.chunk
+        slots, cow = pool.seq_append(seqs[s], n)
+        assert cow is None
+        bt, _ = pool.block_tables(seqs, max_pages)
+        row = np.full(n, s, np.int32)
+        kvl = np.full(n, p0 + n, np.int32)
+        pos = np.arange(p0, p0 + n, dtype=np.int32)
+        ubs.append(dict(s=s, p0=p0, row=row, kvl=kvl, pos=pos,
+                        dev=[to_dev(x) for x in (slots, bt, row, kvl, pos)]))
+    check = {0: None, len(ubs) // 2 + 3: None, len(ubs) - 1: None}
+    outs = {j: torch.empty(cp.chunk, cp.n_q_heads, D, dtype=torch.float32, device="cuda") for j in check}
+    scratch = [torch.empty(cp.chunk, cp.n_q_heads, D, dtype=torch.float32, device="cuda")
+               for _ in range(cp.n_seqs)]
+    streams = [torch.cuda.Stream() for _ in range(cp.n_seqs)]
+    g = torch.cuda.CUDAGraph()
+    s0 = streams[0]
+    s0.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s0):
+        with torch.cuda.graph(g, stream=s0):
+            for st in streams[1:]:
+                st.wait_stream(s0)
+            for j, u in enumerate(ubs):
+                s, p0, n = u["s"], u["p0"], cp.chunk
+                slots, bt, row, kvl, pos = u["dev"]
+                pa.pa_reshape_and_cache(kd, vd, knd[s, p0:p0 + n], vnd[s, p0:p0 + n], slots, stream=streams[s])
+                pa.pa_prefill(qd[s, p0:p0 + n], kd, vd, bt, row, kvl, pos, float(cp.scale),
+                              token_row_host=u["row"], token_kv_len_host=u["kvl"], token_pos_host=u["pos"],
+                              kv_splits=1, out=outs.get(j, scratch[s]), stream=streams[s])
+            for st in streams[1:]:
+                s0.wait_stream(st)
+    torch.cuda.current_stream().wait_stream(s0)
+    g.replay()
+    torch.cuda.synchronize()
+    pick = np.array([0, 1, 63, 64, 255, 256, 500, 511])
+    for j in check:
+        u = ubs[j]
+        s, p0, n = u["s"], u["p0"], cp.chunk
+        n_ctx = p0 + n
+        kh, vh = W.nan_pools(n_ctx // P, Hkv, P, D)
+        kh, vh = oracle.reshape_and_cache(kh, vh, cp.k[s, :n_ctx], cp.v[s, :n_ctx],
+                                          np.arange(n_ctx, dtype=np.int32))
+        bt_priv = np.arange(n_ctx // P, dtype=np.int32)[None, :]
+        ref = oracle.paged_attention(cp.q[s, p0:p0 + n][pick], kh, vh, bt_priv, np.zeros(len(pick), np.int32),
+                                     u["kvl"][pick], u["pos"][pick], cp.scale)
+        assert_attention_close(to_host(outs[j])[pick], ref, f"ubatch {j} (sequence {s}, tokens {p0}..)")
