@@ -328,8 +328,13 @@ size_t pa_prefill_workspace_bytes(const pa_cache_desc* desc, int32_t n_tokens, i
  *   token_row_host, token_kv_len_host, token_pos_host   host copies of the
  *                same arrays, used to plan the work (grouping tokens by
  *                sequence); they must equal the device arrays
- *   kv_splits    0 = choose; >= 1 = split each tile's KV range into at most
- *                this many parts combined by a log-sum-exp reduce
+ *   kv_splits    0 = choose (splits widened until the launch has about one
+ *                workgroup per compute unit: right when this launch has
+ *                the GPU to itself); >= 1 = split each tile's KV range into
+ *                at most this many parts combined by a log-sum-exp reduce.
+ *                1 (no split, no partials, no combine) suits callers that
+ *                keep several launches in flight on separate streams, whose
+ *                workgroups then fill the GPU together
  * Each row's tokens are grouped into tiles in ubatch order; a tile's work
  * ends at its last token's visible length, so tokens of a row should appear
  * in increasing position for efficiency (not for correctness). */
