@@ -77,6 +77,25 @@ def decode_sources_sha256():
     return h.hexdigest()
 
 
+PREFILL_MFMA_FILE = os.path.join(ROOT, "profiles", "prefill_kernel_mfma_busy_8x16k.txt")
+
+
+def prefill_mfma_busy():
+    """MFMA busy fractions of the prefill kernel from the committed counter
+    summary (per-launch, one dispatch at a time), or None without one."""
+    import re
+    try:
+        with open(PREFILL_MFMA_FILE) as fh:
+            text = fh.read()
+        fr = [float(x) for x in re.findall(r"MFMA busy fraction\s+([0-9.]+)", text)]
+        own = re.search(r"so ([0-9.]+) of the cycles of the SIMDs it runs on", text)
+        return {"automatic_split_launch_all_simds": fr[0], "unsplit_launch_all_simds": fr[1],
+                "unsplit_launch_own_simds": float(own.group(1)) if own else None,
+                "source": "profiles/prefill_kernel_mfma_busy_8x16k.txt"}
+    except (OSError, IndexError, ValueError):
+        return None
+
+
 def decode_traffic():
     """Calibrated HBM bytes per decode launch (FETCH_SIZE + WRITE_SIZE) from the
     committed counter summary, or None when the decode sources have changed
@@ -728,6 +747,11 @@ def main():
             "tflops": round(pre["tflops"], 2),
             "frac_of_mfma_f16_peak": round(pre["tflops"] / MFMA_F16_PEAK_TFLOPS, 4),
             "ms_per_pass": round(pre["pass_ms"], 4),
+            "roofline": {"kernel": "prefill_kernel (pa_prefill)", "bound": "mfma",
+                         "achieved": round(pre["tflops"], 1), "peak": MFMA_F16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(pre["tflops"] / MFMA_F16_PEAK_TFLOPS, 4),
+                         "basis": "algorithmic flop per pass / pass time (the schedule's launches overlap)",
+                         "mfma_busy": prefill_mfma_busy()},
             "one_stream": {"schedule": "every launch after the previous one, automatic split plan",
                            "tflops": round(pre["one_stream_tflops"], 2),
                            "frac_of_mfma_f16_peak": round(pre["one_stream_tflops"] / MFMA_F16_PEAK_TFLOPS, 4),
