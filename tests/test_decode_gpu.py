@@ -267,3 +267,15 @@ def test_mixed_lengths_many_partitions_combine():
     # the live-only grid and the fixed fold order make repeats bitwise equal
     again = run_decode(c, 0)
     assert np.array_equal(got.view(np.uint32), again.view(np.uint32))
+
+
+def test_sequence_longer_than_one_partition_page_table():
+    """A 140000-token sequence at P = 16 is 8750 pages, beyond the 8191 page ids
+    one workgroup stages: a one-pass request (partition_tokens = -1) becomes a
+    split, and the automatic plan agrees with the oracle too."""
+    rng = np.random.default_rng(140000)
+    L = 140000
+    c = W.make_decode_case(rng, "long", 4, 1, 64, 16, [L, 300], (L + 300) // 16 + 64)
+    ref = ref_decode(c)
+    for mode in (-1, 0):
+        assert_attention_close(run_decode(c, mode), ref, f"long sequence mode {mode}")

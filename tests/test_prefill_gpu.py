@@ -329,3 +329,20 @@ def test_chunked_prefill_full_size_in_the_benchmark_schedule():
         ref = oracle.paged_attention(cp.q[s, p0:p0 + n][pick], kh, vh, bt_priv, np.zeros(len(pick), np.int32),
                                      u["kvl"][pick], u["pos"][pick], cp.scale)
         assert_attention_close(to_host(outs[j])[pick], ref, f"ubatch {j} (sequence {s}, tokens {p0}..)")
+
+
+@pytest.mark.parametrize("kv_splits", [1, 0])
+def test_prefill_range_longer_than_one_split_page_table(kv_splits):
+    """Tokens whose visible range (about 140000 keys at P = 16, 8750 pages) is
+    more than one workgroup stages: even an unsplit request is cut at the
+    staged-table limit and combined."""
+    rng = np.random.default_rng(140001)
+    pre, new = [140000 - 40], [40]
+    N = (140000 + 15) // 16 + 64
+    c = W.make_prefill_case(rng, "long", 8, 2, 64, 16, N, pre, new, "grouped")
+    kd, vd, k2, v2 = write_new_tokens(c)
+    got = run_prefill(c, kd, vd, kv_splits)
+    pick = np.array([0, 1, 17, 38, 39])
+    ref = oracle.paged_attention(c.q[pick], k2, v2, c.block_tables, c.token_row[pick],
+                                 c.token_kv_len[pick], c.token_pos[pick], c.scale)
+    assert_attention_close(got[pick], ref, f"long range splits {kv_splits}")
