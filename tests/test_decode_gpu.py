@@ -41,6 +41,7 @@ CASES = [
     # pages of 16 and 32 V slot blocks: lengths around block and page edges
     (4, 4, 64, 512, [700, 513, 31]),
     (8, 2, 128, 1024, [1, 32, 33, 1500, 2049]),
+    (16, 1, 128, 128, [129, 4000, 31]),
 ]
 
 

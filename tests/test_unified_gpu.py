@@ -42,6 +42,7 @@ CASES = [
     (32, 8, 128, 128, [300, 1000], [70, 33], "round_robin"),
     (32, 8, 128, 64, [0, 130], [200, 64], "grouped"),
     (16, 2, 128, 32, [700, 5], [33, 61], "round_robin"),
+    (8, 2, 64, 256, [600, 40], [50, 20], "round_robin"),
 ]
 
 
