@@ -38,10 +38,17 @@
  *     [16, 1024]; n_q_heads a multiple of n_kv_heads with group size
  *     G = n_q_heads / n_kv_heads in {1, 2, 4, 8, 16}.  Other shapes return
  *     PA_ERR_UNSUPPORTED before anything is launched.
- *   - Block-table entries and slots are not range-checked on the device: an
- *     out-of-range page id is undefined behaviour.  Setting the environment
- *     variable PA_VALIDATE=1 makes the host check every host-visible table
- *     first (decode: kv_lens_host; prefill: all host copies).
+ *   - Block-table entries and slots are not range-checked on the device.
+ *     pa_decode, pa_prefill and pa_reshape_and_cache take optional host
+ *     copies of the tables they address through (block_tables_host,
+ *     slot_mapping_host); when one is passed, every entry the launch would
+ *     read is checked on the host first and a bad one returns PA_ERR_INVALID
+ *     before anything is launched: page ids must lie in [0, num_pages), live
+ *     slots in [0, num_pages*page_size) with none repeated.  Setting the
+ *     environment variable PA_VALIDATE=1 (any value but "0") makes those host
+ *     copies mandatory (PA_ERR_INVALID when one is NULL).  Without a host
+ *     copy, an out-of-range page id or slot on the device is undefined
+ *     behaviour.  Host copies must hold the same values as the device arrays.
  */
 #ifndef PA_H
 #define PA_H
@@ -223,11 +230,14 @@ typedef struct {
  * their cells.  k_new, v_new: device [n_tokens][n_kv_heads][head_dim], binary16
  * (src_is_f32 = 0) or IEEE binary32 (src_is_f32 = 1, rounded to nearest even
  * on store).  slot_mapping: device int32 [n_tokens]; a negative slot skips the
- * token.  Live slots must be distinct and < num_pages*page_size.  Bits are
- * copied exactly for binary16 input. */
+ * token.  Live slots must be distinct and < num_pages*page_size.
+ * slot_mapping_host: NULL or a host copy of slot_mapping, checked against those
+ * rules before the launch (mandatory under PA_VALIDATE=1).  Bits are copied
+ * exactly for binary16 input. */
 pa_status pa_reshape_and_cache(const pa_cache_desc* desc, void* k_cache, void* v_cache,
                                const void* k_new, const void* v_new, int32_t src_is_f32,
-                               const int32_t* slot_mapping, int32_t n_tokens, pa_stream stream);
+                               const int32_t* slot_mapping, const int32_t* slot_mapping_host,
+                               int32_t n_tokens, pa_stream stream);
 
 /* Block copy for copy-on-write ([CF] sections 2 and 3): for every layer l and
  * pair i, copy page pairs_host[2i] onto page pairs_host[2i+1] in both
@@ -281,7 +291,12 @@ size_t pa_decode_workspace_bytes(const pa_cache_desc* desc, int32_t n_seqs, int3
  *   block_tables device int32 [n_seqs][max_pages]; only the first
  *                ceil(kv_len/page_size) entries of a row are read
  *   kv_lens      device int32 [n_seqs]; each in [1, max_pages*page_size]
- *   kv_lens_host host copy of kv_lens or NULL; used only to size the split
+ *   block_tables_host  host copy of block_tables or NULL; when given (it
+ *                needs kv_lens_host), the entries each sequence reads are
+ *                checked to be page ids in [0, num_pages) before the launch
+ *   kv_lens_host host copy of kv_lens or NULL; sizes the split and bounds the
+ *                table check (both host copies are mandatory under
+ *                PA_VALIDATE=1)
  *   scale        softmax scale (e.g. 1/sqrt(head_dim))
  *   partition_tokens  0 = choose (about one workgroup per compute unit
  *                when all lengths are equal, partitions of at most 2048
@@ -293,7 +308,8 @@ size_t pa_decode_workspace_bytes(const pa_cache_desc* desc, int32_t n_seqs, int3
  * sequence's length are never used, whatever they hold. */
 pa_status pa_decode(const pa_cache_desc* desc, const void* k_cache, const void* v_cache,
                     const float* q, float* out, const int32_t* block_tables,
-                    const int32_t* kv_lens, const int32_t* kv_lens_host, int32_t n_seqs,
+                    const int32_t* kv_lens, const int32_t* block_tables_host,
+                    const int32_t* kv_lens_host, int32_t n_seqs,
                     int32_t max_pages, int32_t n_q_heads, float scale, int32_t partition_tokens,
                     void* workspace, size_t workspace_bytes, pa_stream stream);
 
@@ -328,6 +344,11 @@ size_t pa_prefill_workspace_bytes(const pa_cache_desc* desc, int32_t n_tokens, i
  *   token_row_host, token_kv_len_host, token_pos_host   host copies of the
  *                same arrays, used to plan the work (grouping tokens by
  *                sequence); they must equal the device arrays
+ *   block_tables_host  host copy of block_tables or NULL; when given, the
+ *                entries every row's tokens read (up to the row's longest
+ *                visible range) are checked to be page ids in
+ *                [0, num_pages) before the launch (mandatory under
+ *                PA_VALIDATE=1)
  *   kv_splits    0 = choose (splits widened until the launch has about one
  *                workgroup per compute unit: right when this launch has
  *                the GPU to itself); >= 1 = split each tile's KV range into
@@ -343,9 +364,9 @@ pa_status pa_prefill(const pa_cache_desc* desc, const void* k_cache, const void*
                      const int32_t* token_row, const int32_t* token_kv_len,
                      const int32_t* token_pos, const int32_t* token_row_host,
                      const int32_t* token_kv_len_host, const int32_t* token_pos_host,
-                     int32_t n_tokens, int32_t n_rows, int32_t max_pages, int32_t n_q_heads,
-                     float scale, int32_t kv_splits, void* workspace, size_t workspace_bytes,
-                     pa_stream stream);
+                     const int32_t* block_tables_host, int32_t n_tokens, int32_t n_rows,
+                     int32_t max_pages, int32_t n_q_heads, float scale, int32_t kv_splits,
+                     void* workspace, size_t workspace_bytes, pa_stream stream);
 
 /* ---------------------------------------------------------------------------
  * Unified-span attention: the baseline UA-PagedAttention replaces ([UA]

@@ -14,6 +14,7 @@ Cache layout (one layer), binary16:
 from __future__ import annotations
 
 import ctypes
+import os
 from typing import Optional, Sequence
 
 import numpy as np
@@ -264,23 +265,79 @@ class Pool:
 
 # ---------------------------------------------------------------- device ops
 
-def pa_reshape_and_cache(k_cache, v_cache, k_new, v_new, slot_mapping, stream=None) -> None:
-    """Write new tokens' K/V ([T][Hkv][D], float16 or float32) into their cells."""
+def _validate_env() -> bool:
+    """PA_VALIDATE as the library reads it: set and not "0"."""
+    v = os.environ.get("PA_VALIDATE", "")
+    return bool(v) and v[0] != "0"
+
+
+def _host_copy(given, device_tensor):
+    """The caller's host copy of a device table, or (under PA_VALIDATE) one
+    taken from the device (a synchronizing copy), else None."""
+    if given is not None:
+        return _host_i32(given)
+    if _validate_env():
+        return _host_i32(device_tensor.cpu().numpy())
+    return None
+
+
+def _launch_stream(stream):
+    import torch
+    return torch.cuda.current_stream() if stream is None else stream
+
+
+def _alloc_out_ws(q, out, workspace, need, stream):
+    """The output (like q) and a zero-filled workspace of `need` bytes when the
+    caller gave none, allocated on the launch stream: the zero fill is then
+    ordered before the kernel, and the caching allocator does not hand the
+    blocks to another stream's work while the kernel may still use them."""
+    import torch
+    if out is not None and (workspace is not None or need <= 0):
+        return out, workspace
+    with torch.cuda.stream(stream):
+        if out is None:
+            out = torch.empty_like(q)
+        if workspace is None and need > 0:
+            workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+    return out, workspace
+
+
+def _ws_args(workspace):
+    if workspace is None:
+        return None, 0
+    return ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size()
+
+
+def _need(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def pa_reshape_and_cache(k_cache, v_cache, k_new, v_new, slot_mapping, stream=None,
+                         slot_mapping_host=None) -> None:
+    """Write new tokens' K/V ([T][Hkv][D], float16 or float32) into their cells.
+
+    ``slot_mapping_host`` (a host copy of ``slot_mapping``) lets the library
+    check the slots before the launch; under PA_VALIDATE=1 it is taken from the
+    device when not given."""
     import torch
     desc = cache_desc(k_cache, v_cache)
     _dev(k_cache, torch.float16, "k_cache", 4)
     _dev(v_cache, torch.float16, "v_cache", 5)
+    _dev(slot_mapping, torch.int32, "slot_mapping", 1)
     T = int(slot_mapping.shape[0])
     if k_new.dtype not in (torch.float16, torch.float32) or v_new.dtype != k_new.dtype:
         raise TypeError("k_new/v_new must both be float16 or both float32")
     for name, t in (("k_new", k_new), ("v_new", v_new)):
         if tuple(t.shape) != (T, desc.n_kv_heads, desc.head_dim):
             raise ValueError(f"{name} must be [{T}][{desc.n_kv_heads}][{desc.head_dim}]")
+    sh = _host_copy(slot_mapping_host, slot_mapping)
+    _need(sh is None or sh.shape == (T,), f"slot_mapping_host must hold {T} entries")
     _check(_L().pa_reshape_and_cache(
         ctypes.byref(desc), _dev(k_cache, torch.float16, "k_cache"),
         _dev(v_cache, torch.float16, "v_cache"), _dev(k_new, k_new.dtype, "k_new"),
         _dev(v_new, v_new.dtype, "v_new"), 1 if k_new.dtype == torch.float32 else 0,
-        _dev(slot_mapping, torch.int32, "slot_mapping", 1), T, _stream_ptr(stream)))
+        _dev(slot_mapping, torch.int32, "slot_mapping", 1), _i32p(sh), T, _stream_ptr(stream)))
 
 
 def pa_copy_blocks(k_caches, v_caches, pairs, stream=None) -> None:
@@ -335,32 +392,39 @@ def pa_decode_workspace_bytes(desc: CacheDesc, n_seqs: int, n_q_heads: int, max_
 
 
 def pa_decode(q, k_cache, v_cache, block_tables, kv_lens, scale: float, kv_lens_host=None,
-              partition_tokens: int = 0, out=None, workspace=None, stream=None):
+              partition_tokens: int = 0, out=None, workspace=None, stream=None,
+              block_tables_host=None):
     """Paged decode attention; q fp32 [S][Hq][D] -> out fp32 [S][Hq][D].
 
     A caller-supplied ``workspace`` must be zero-filled before its first use;
-    pa_decode leaves its counter region zero-filled again."""
+    pa_decode leaves its counter region zero-filled again.  ``block_tables_host``
+    (with ``kv_lens_host``) lets the library check the page ids before the
+    launch; under PA_VALIDATE=1 both are taken from the device when not given."""
     import torch
     desc = cache_desc(k_cache, v_cache)
+    _dev(q, torch.float32, "q", 3)
+    _dev(block_tables, torch.int32, "block_tables", 2)
+    _dev(kv_lens, torch.int32, "kv_lens", 1)
     S, Hq, D = (int(x) for x in q.shape)
-    if D != desc.head_dim:
-        raise ValueError("q head_dim does not match the cache")
+    _need(D == desc.head_dim, "q head_dim does not match the cache")
+    _need(int(block_tables.shape[0]) >= S, f"block_tables needs at least {S} rows")
+    _need(int(kv_lens.shape[0]) == S, f"kv_lens must hold {S} entries")
+    _need(out is None or tuple(out.shape) == tuple(q.shape), "out must have q's shape")
     max_pages = int(block_tables.shape[1])
-    kl = None if kv_lens_host is None else _host_i32(kv_lens_host)
-    if out is None:
-        out = torch.empty_like(q)
+    kl = _host_copy(kv_lens_host, kv_lens)
+    bh = _host_copy(block_tables_host, block_tables)
+    _need(kl is None or kl.shape == (S,), f"kv_lens_host must hold {S} entries")
+    _need(bh is None or bh.shape == tuple(block_tables.shape), "block_tables_host must have block_tables' shape")
     need = pa_decode_workspace_bytes(desc, S, Hq, max_pages, kl, partition_tokens)
-    if workspace is None and need > 0:
-        # zero-filled: the split's completion counters start at zero
-        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
-    ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = _launch_stream(stream)
+    out, workspace = _alloc_out_ws(q, out, workspace, need, st)
+    ws_ptr, ws_bytes = _ws_args(workspace)
     _check(_L().pa_decode(
         ctypes.byref(desc), _dev(k_cache, torch.float16, "k_cache", 4),
         _dev(v_cache, torch.float16, "v_cache", 5), _dev(q, torch.float32, "q", 3),
         _dev(out, torch.float32, "out", 3), _dev(block_tables, torch.int32, "block_tables", 2),
-        _dev(kv_lens, torch.int32, "kv_lens", 1), _i32p(kl), S, max_pages, Hq, float(scale),
-        int(partition_tokens), ws_ptr, ws_bytes, _stream_ptr(stream)))
+        _dev(kv_lens, torch.int32, "kv_lens", 1), _i32p(bh), _i32p(kl), S, max_pages, Hq, float(scale),
+        int(partition_tokens), ws_ptr, ws_bytes, ctypes.c_void_p(st.cuda_stream)))
     return out
 
 
@@ -369,42 +433,51 @@ def pa_prefill_workspace_bytes(desc: CacheDesc, n_q_heads: int, token_row_host, 
     r = _host_i32(token_row_host)
     k = _host_i32(token_kv_len_host)
     p = _host_i32(token_pos_host)
+    _need(r.shape == k.shape == p.shape and r.ndim == 1, "token arrays must be 1-D of one length")
     return int(_L().pa_prefill_workspace_bytes(ctypes.byref(desc), len(r), int(n_q_heads), _i32p(r),
                                                _i32p(k), _i32p(p), int(kv_splits)))
 
 
 def pa_prefill(q, k_cache, v_cache, block_tables, token_row, token_kv_len, token_pos,
                scale: float, token_row_host=None, token_kv_len_host=None, token_pos_host=None,
-               kv_splits: int = 0, out=None, workspace=None, stream=None):
+               kv_splits: int = 0, out=None, workspace=None, stream=None, block_tables_host=None):
     """UA paged prefill; q fp32 [T][Hq][D] -> out fp32 [T][Hq][D].
 
     The host copies of the token arrays are taken from the device tensors if
     not given (a synchronizing copy; pass them to avoid it).  A caller-supplied
     ``workspace`` must be zero-filled before its first use (each call leaves
-    its counter region zeroed again)."""
+    its counter region zeroed again).  ``block_tables_host`` lets the library
+    check the page ids before the launch; under PA_VALIDATE=1 it is taken from
+    the device when not given."""
     import torch
     desc = cache_desc(k_cache, v_cache)
+    _dev(q, torch.float32, "q", 3)
+    _dev(block_tables, torch.int32, "block_tables", 2)
     T, Hq, D = (int(x) for x in q.shape)
-    if D != desc.head_dim:
-        raise ValueError("q head_dim does not match the cache")
+    _need(D == desc.head_dim, "q head_dim does not match the cache")
+    for name, t in (("token_row", token_row), ("token_kv_len", token_kv_len), ("token_pos", token_pos)):
+        _dev(t, torch.int32, name, 1)
+        _need(int(t.shape[0]) == T, f"{name} must hold {T} entries")
+    _need(out is None or tuple(out.shape) == tuple(q.shape), "out must have q's shape")
     rh = _host_i32(token_row.cpu().numpy() if token_row_host is None else token_row_host)
     kh = _host_i32(token_kv_len.cpu().numpy() if token_kv_len_host is None else token_kv_len_host)
     ph = _host_i32(token_pos.cpu().numpy() if token_pos_host is None else token_pos_host)
-    if out is None:
-        out = torch.empty_like(q)
+    for name, h in (("token_row_host", rh), ("token_kv_len_host", kh), ("token_pos_host", ph)):
+        _need(h.shape == (T,), f"{name} must hold {T} entries")
+    bh = _host_copy(block_tables_host, block_tables)
+    _need(bh is None or bh.shape == tuple(block_tables.shape), "block_tables_host must have block_tables' shape")
     need = pa_prefill_workspace_bytes(desc, Hq, rh, kh, ph, kv_splits)
-    if workspace is None and need > 0:
-        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
-    ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = _launch_stream(stream)
+    out, workspace = _alloc_out_ws(q, out, workspace, need, st)
+    ws_ptr, ws_bytes = _ws_args(workspace)
     n_rows, max_pages = (int(x) for x in block_tables.shape)
     _check(_L().pa_prefill(
         ctypes.byref(desc), _dev(k_cache, torch.float16, "k_cache", 4),
         _dev(v_cache, torch.float16, "v_cache", 5), _dev(q, torch.float32, "q", 3),
         _dev(out, torch.float32, "out", 3), _dev(block_tables, torch.int32, "block_tables", 2),
         _dev(token_row, torch.int32, "token_row", 1), _dev(token_kv_len, torch.int32, "token_kv_len", 1),
-        _dev(token_pos, torch.int32, "token_pos", 1), _i32p(rh), _i32p(kh), _i32p(ph), T, n_rows,
-        max_pages, Hq, float(scale), int(kv_splits), ws_ptr, ws_bytes, _stream_ptr(stream)))
+        _dev(token_pos, torch.int32, "token_pos", 1), _i32p(rh), _i32p(kh), _i32p(ph), _i32p(bh), T,
+        n_rows, max_pages, Hq, float(scale), int(kv_splits), ws_ptr, ws_bytes, ctypes.c_void_p(st.cuda_stream)))
     return out
 
 
@@ -421,21 +494,26 @@ def pa_unified_attention(q, k_cache, v_cache, span: int, cell_seq, cell_pos, tok
     q fp32 [T][Hq][D] -> out fp32 [T][Hq][D].  Workspace rules as pa_prefill."""
     import torch
     desc = cache_desc(k_cache, v_cache)
+    _dev(q, torch.float32, "q", 3)
     T, Hq, D = (int(x) for x in q.shape)
-    if D != desc.head_dim:
-        raise ValueError("q head_dim does not match the cache")
-    if out is None:
-        out = torch.empty_like(q)
+    _need(D == desc.head_dim, "q head_dim does not match the cache")
+    for name, t, n in (("cell_seq", cell_seq, None), ("cell_pos", cell_pos, None), ("token_seq", token_seq, T),
+                       ("token_pos", token_pos, T)):
+        _dev(t, torch.int32, name, 1)
+        if n is None:
+            _need(int(t.shape[0]) >= int(span), f"{name} must hold at least span = {span} entries")
+        else:
+            _need(int(t.shape[0]) == n, f"{name} must hold {n} entries")
+    _need(out is None or tuple(out.shape) == tuple(q.shape), "out must have q's shape")
     need = pa_unified_workspace_bytes(desc, T, Hq, span, kv_splits)
-    if workspace is None and need > 0:
-        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
-    ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = _launch_stream(stream)
+    out, workspace = _alloc_out_ws(q, out, workspace, need, st)
+    ws_ptr, ws_bytes = _ws_args(workspace)
     _check(_L().pa_unified_attention(
         ctypes.byref(desc), _dev(k_cache, torch.float16, "k_cache", 4),
         _dev(v_cache, torch.float16, "v_cache", 5), _dev(q, torch.float32, "q", 3),
         _dev(out, torch.float32, "out", 3), int(span), _dev(cell_seq, torch.int32, "cell_seq", 1),
         _dev(cell_pos, torch.int32, "cell_pos", 1), _dev(token_seq, torch.int32, "token_seq", 1),
         _dev(token_pos, torch.int32, "token_pos", 1), T, Hq, float(scale), int(kv_splits), ws_ptr,
-        ws_bytes, _stream_ptr(stream)))
+        ws_bytes, ctypes.c_void_p(st.cuda_stream)))
     return out

@@ -8,7 +8,9 @@ import ctypes
 import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libpa.so")
+# PA_LIB_PATH selects another build of the same library (the host-sanitizer
+# build used by the CPU tests); the default is the in-tree libpa.so
+LIB_PATH = os.environ.get("PA_LIB_PATH") or os.path.join(PKG, "libpa.so")
 
 c_i32 = ctypes.c_int32
 c_i32_p = ctypes.POINTER(ctypes.c_int32)
@@ -48,7 +50,7 @@ SIGNATURES = {
     "pa_prefix_capacity": (c_i32, [c_void_p, c_i32, c_i32_p]),
     "pa_prefix_stats": (c_i32, [c_void_p, c_i32_p]),
     "pa_reshape_and_cache": (c_i32, [CacheDesc_p, c_void_p, c_void_p, c_void_p, c_void_p, c_i32,
-                                     c_void_p, c_i32, c_void_p]),
+                                     c_void_p, c_i32_p, c_i32, c_void_p]),
     "pa_copy_blocks": (c_i32, [CacheDesc_p, ctypes.POINTER(c_void_p), ctypes.POINTER(c_void_p),
                                c_i32, c_i32_p, c_i32, c_void_p]),
     "pa_swap_blocks": (c_i32, [CacheDesc_p, ctypes.POINTER(c_void_p), ctypes.POINTER(c_void_p),
@@ -56,13 +58,13 @@ SIGNATURES = {
                                c_i32_p, c_i32, c_i32, c_void_p]),
     "pa_decode_workspace_bytes": (c_size_t, [CacheDesc_p, c_i32, c_i32, c_i32, c_i32_p, c_i32]),
     "pa_decode": (c_i32, [CacheDesc_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
-                          c_i32_p, c_i32, c_i32, c_i32, c_float, c_i32, c_void_p, c_size_t,
+                          c_i32_p, c_i32_p, c_i32, c_i32, c_i32, c_float, c_i32, c_void_p, c_size_t,
                           c_void_p]),
     "pa_prefill_workspace_bytes": (c_size_t, [CacheDesc_p, c_i32, c_i32, c_i32_p, c_i32_p, c_i32_p,
                                               c_i32]),
     "pa_prefill": (c_i32, [CacheDesc_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
-                           c_void_p, c_void_p, c_void_p, c_i32_p, c_i32_p, c_i32_p, c_i32, c_i32,
-                           c_i32, c_i32, c_float, c_i32, c_void_p, c_size_t, c_void_p]),
+                           c_void_p, c_void_p, c_void_p, c_i32_p, c_i32_p, c_i32_p, c_i32_p, c_i32,
+                           c_i32, c_i32, c_i32, c_float, c_i32, c_void_p, c_size_t, c_void_p]),
     "pa_unified_workspace_bytes": (c_size_t, [CacheDesc_p, c_i32, c_i32, c_i32, c_i32]),
     "pa_unified_attention": (c_i32, [CacheDesc_p, c_void_p, c_void_p, c_void_p, c_void_p, c_i32,
                                      c_void_p, c_void_p, c_void_p, c_void_p, c_i32, c_i32, c_float,

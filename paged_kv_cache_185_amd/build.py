@@ -68,5 +68,75 @@ def build_library(verbose: bool = False) -> str:
     return LIB
 
 
+# ---- host sanitizer build ---------------------------------------------------
+#
+# The host code (page pool, argument checks, work planning) compiled with
+# AddressSanitizer and UndefinedBehaviorSanitizer into a CPU-only test build of
+# the library.  Only host code is instrumented: pool.cpp and api.cpp are
+# compiled as plain C++ by clang, with no device pass, and linked with the
+# kernels' objects from the normal build (never launched by the CPU tests).
+# The library needs the sanitizer runtime loaded first in the process
+# (sanitizer_runtime(), e.g. through LD_PRELOAD of a child process).
+
+SANITIZE = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-shared-libasan"]
+SAN_BUILD = os.path.join(BUILD, "host_sanitize")
+SAN_LIB = os.path.join(SAN_BUILD, "libpa_host_sanitize.so")
+
+
+def host_clang() -> str:
+    for cand in (os.environ.get("PA_HOST_CLANG"), "/opt/rocm/llvm/bin/clang++", shutil.which("clang++")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("clang++ not found: the host sanitizer build needs it")
+
+
+def sanitizer_runtime() -> str:
+    """Path of the shared ASan runtime (which carries UBSan) of host_clang()."""
+    r = subprocess.run([host_clang(), "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    path = r.stdout.strip()
+    if not os.path.isabs(path) or not os.path.exists(path):
+        r = subprocess.run([host_clang(), "-print-runtime-dir"], capture_output=True, text=True)
+        path = os.path.join(r.stdout.strip(), "libclang_rt.asan-x86_64.so")
+    if not os.path.exists(path):
+        raise RuntimeError("shared AddressSanitizer runtime not found")
+    return path
+
+
+def build_host_sanitized(verbose: bool = False) -> str:
+    """Build the host-sanitizer test library (SAN_LIB) and return its path."""
+    os.makedirs(SAN_BUILD, exist_ok=True)
+    kernel_objs = [os.path.join(BUILD, s + ".o") for s in SOURCES if s.endswith(".hip")]
+    if not all(os.path.exists(o) for o in kernel_objs):
+        os.makedirs(BUILD, exist_ok=True)
+        with cf.ThreadPoolExecutor(max_workers=3) as ex:
+            list(ex.map(_compile, [s for s in SOURCES if s.endswith(".hip")]))
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(hipcc())))
+    flags = ["-O1", "-g", "-fno-omit-frame-pointer", "-std=c++17", "-fPIC", "-x", "c++",
+             "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(rocm, "include"), "-I", INCLUDE, "-I", CSRC] + SANITIZE
+
+    def host_obj(src):
+        obj = os.path.join(SAN_BUILD, src + ".o")
+        r = subprocess.run([host_clang()] + flags + ["-c", os.path.join(CSRC, src), "-o", obj],
+                           capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"sanitizer build of {src} failed:\n{r.stderr}")
+        return obj
+
+    with cf.ThreadPoolExecutor(max_workers=2) as ex:
+        objs = list(ex.map(host_obj, ["pool.cpp", "api.cpp"]))
+    tmp = SAN_LIB + ".tmp"
+    r = subprocess.run([host_clang(), "-shared", "-o", tmp] + objs + kernel_objs + SANITIZE +
+                       ["-L", os.path.join(rocm, "lib"), "-lamdhip64", "-Wl,-rpath," + os.path.join(rocm, "lib")],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("sanitizer link failed:\n" + r.stderr)
+    os.replace(tmp, SAN_LIB)
+    if verbose:
+        print("built", SAN_LIB)
+    return SAN_LIB
+
+
 if __name__ == "__main__":
     build_library(verbose=True)
+    if len(sys.argv) > 1 and sys.argv[1] == "--host-sanitize":
+        build_host_sanitized(verbose=True)

@@ -71,6 +71,28 @@ pa_status check_heads(const char* fn, const pa_cache_desc* d, int32_t n_q_heads)
     return PA_OK;
 }
 
+// ---------------------------------------------------------- host range checks
+//
+// Block-table entries and slots are used as addresses on the device without a
+// check there.  When the caller passes host copies, the entries a launch would
+// read are checked here first; PA_VALIDATE=1 makes the host copies mandatory.
+
+// Entries [0, ceil(n_cells / P)) of `row` must be page ids in [0, num_pages).
+pa_status check_table_row(const char* fn, const pa_cache_desc* d, const int32_t* bt_host, int32_t max_pages,
+                          int64_t row, int64_t n_cells) {
+    const int64_t n = (n_cells + d->page_size - 1) / d->page_size;
+    if (n > max_pages)
+        return fail(PA_ERR_INVALID, std::string(fn) + ": row " + std::to_string(row) +
+                                        " needs more than max_pages entries");
+    const int32_t* r = bt_host + row * (int64_t)max_pages;
+    for (int64_t j = 0; j < n; ++j)
+        if (r[j] < 0 || r[j] >= d->num_pages)
+            return fail(PA_ERR_INVALID, std::string(fn) + ": block_tables[" + std::to_string(row) + "][" +
+                                            std::to_string(j) + "] = " + std::to_string(r[j]) +
+                                            " is not a page id in [0, num_pages)");
+    return PA_OK;
+}
+
 // ---------------------------------------------------------------- decode plan
 
 struct DecodePlan {
@@ -347,11 +369,12 @@ extern "C" {
 
 const char* pa_last_error(void) { return g_error.c_str(); }
 
-int32_t pa_version(void) { return 100; }
+int32_t pa_version(void) { return 200; }
 
 pa_status pa_reshape_and_cache(const pa_cache_desc* desc, void* k_cache, void* v_cache,
                                const void* k_new, const void* v_new, int32_t src_is_f32,
-                               const int32_t* slot_mapping, int32_t n_tokens, pa_stream stream) {
+                               const int32_t* slot_mapping, const int32_t* slot_mapping_host,
+                               int32_t n_tokens, pa_stream stream) {
     pa_status st = check_desc("pa_reshape_and_cache", desc);
     if (st != PA_OK) return st;
     if (n_tokens < 0) return fail(PA_ERR_INVALID, "pa_reshape_and_cache: n_tokens < 0");
@@ -360,6 +383,26 @@ pa_status pa_reshape_and_cache(const pa_cache_desc* desc, void* k_cache, void* v
         return fail(PA_ERR_INVALID, "pa_reshape_and_cache: null pointer");
     if (src_is_f32 != 0 && src_is_f32 != 1)
         return fail(PA_ERR_INVALID, "pa_reshape_and_cache: src_is_f32 must be 0 or 1");
+    if (validate_env() && !slot_mapping_host)
+        return fail(PA_ERR_INVALID, "pa_reshape_and_cache: PA_VALIDATE=1 needs slot_mapping_host");
+    if (slot_mapping_host) {
+        // live slots inside the pool, none written twice (the result would
+        // depend on which write lands last)
+        const int64_t n_slots = (int64_t)desc->num_pages * desc->page_size;
+        std::vector<int32_t> live;
+        live.reserve(n_tokens);
+        for (int32_t i = 0; i < n_tokens; ++i) {
+            const int32_t sl = slot_mapping_host[i];
+            if (sl < 0) continue;
+            if (sl >= n_slots)
+                return fail(PA_ERR_INVALID, "pa_reshape_and_cache: slot_mapping[" + std::to_string(i) + "] = " +
+                                                std::to_string(sl) + " is past the pool");
+            live.push_back(sl);
+        }
+        std::sort(live.begin(), live.end());
+        if (std::adjacent_find(live.begin(), live.end()) != live.end())
+            return fail(PA_ERR_INVALID, "pa_reshape_and_cache: a slot is written twice");
+    }
     hipError_t e = launch_reshape_and_cache(k_cache, v_cache, k_new, v_new, src_is_f32 == 1,
                                             slot_mapping, n_tokens, desc->n_kv_heads,
                                             desc->page_size, desc->head_dim, (hipStream_t)stream);
@@ -455,7 +498,8 @@ size_t pa_decode_workspace_bytes(const pa_cache_desc* desc, int32_t n_seqs, int3
 
 pa_status pa_decode(const pa_cache_desc* desc, const void* k_cache, const void* v_cache,
                     const float* q, float* out, const int32_t* block_tables,
-                    const int32_t* kv_lens, const int32_t* kv_lens_host, int32_t n_seqs,
+                    const int32_t* kv_lens, const int32_t* block_tables_host,
+                    const int32_t* kv_lens_host, int32_t n_seqs,
                     int32_t max_pages, int32_t n_q_heads, float scale, int32_t partition_tokens,
                     void* workspace, size_t workspace_bytes, pa_stream stream) {
     pa_status st = check_desc("pa_decode", desc);
@@ -471,8 +515,15 @@ pa_status pa_decode(const pa_cache_desc* desc, const void* k_cache, const void* 
     if (plan.bytes > 0 && (!workspace || workspace_bytes < plan.bytes))
         return fail(PA_ERR_WORKSPACE, "pa_decode: workspace missing or too small (need " +
                                           std::to_string(plan.bytes) + " bytes)");
-    if (validate_env() && kv_lens_host == nullptr)
-        return fail(PA_ERR_INVALID, "pa_decode: PA_VALIDATE=1 needs kv_lens_host");
+    if (validate_env() && (kv_lens_host == nullptr || block_tables_host == nullptr))
+        return fail(PA_ERR_INVALID, "pa_decode: PA_VALIDATE=1 needs kv_lens_host and block_tables_host");
+    if (block_tables_host) {
+        if (!kv_lens_host)
+            return fail(PA_ERR_INVALID, "pa_decode: checking block_tables_host needs kv_lens_host");
+        for (int32_t i = 0; i < n_seqs; ++i)
+            if ((st = check_table_row("pa_decode", desc, block_tables_host, max_pages, i, kv_lens_host[i])) != PA_OK)
+                return st;
+    }
     DecodeArgs a{};
     a.k_cache = (const uint16_t*)k_cache;
     a.v_cache = (const uint16_t*)v_cache;
@@ -535,9 +586,9 @@ pa_status pa_prefill(const pa_cache_desc* desc, const void* k_cache, const void*
                      const int32_t* token_row, const int32_t* token_kv_len,
                      const int32_t* token_pos, const int32_t* token_row_host,
                      const int32_t* token_kv_len_host, const int32_t* token_pos_host,
-                     int32_t n_tokens, int32_t n_rows, int32_t max_pages, int32_t n_q_heads,
-                     float scale, int32_t kv_splits, void* workspace, size_t workspace_bytes,
-                     pa_stream stream) {
+                     const int32_t* block_tables_host, int32_t n_tokens, int32_t n_rows,
+                     int32_t max_pages, int32_t n_q_heads, float scale, int32_t kv_splits,
+                     void* workspace, size_t workspace_bytes, pa_stream stream) {
     pa_status st = check_desc("pa_prefill", desc);
     if (st != PA_OK) return st;
     if ((st = check_heads("pa_prefill", desc, n_q_heads)) != PA_OK) return st;
@@ -552,6 +603,21 @@ pa_status pa_prefill(const pa_cache_desc* desc, const void* k_cache, const void*
     if ((st = plan_prefill(desc, n_tokens, n_q_heads, n_rows, max_pages, token_row_host,
                            token_kv_len_host, token_pos_host, kv_splits, &plan)) != PA_OK)
         return st;
+    if (validate_env() && !block_tables_host)
+        return fail(PA_ERR_INVALID, "pa_prefill: PA_VALIDATE=1 needs block_tables_host");
+    if (block_tables_host) {
+        // the entries a tile reads: those of its row up to the longest visible
+        // range of its tokens
+        std::vector<int64_t> vis(n_rows, 0);
+        for (int32_t i = 0; i < n_tokens; ++i) {
+            const int32_t r = token_row_host[i];
+            if (r >= 0) vis[r] = std::max<int64_t>(vis[r], std::min(token_kv_len_host[i], token_pos_host[i] + 1));
+        }
+        for (int32_t r = 0; r < n_rows; ++r)
+            if (vis[r] > 0 &&
+                (st = check_table_row("pa_prefill", desc, block_tables_host, max_pages, r, vis[r])) != PA_OK)
+                return st;
+    }
     if (plan.bytes > 0 && (!workspace || workspace_bytes < plan.bytes))
         return fail(PA_ERR_WORKSPACE, "pa_prefill: workspace missing or too small (need " +
                                           std::to_string(plan.bytes) + " bytes)");

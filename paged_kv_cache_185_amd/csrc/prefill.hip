@@ -291,21 +291,43 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, Til
             st.vlive = live;
         }
     };
-    // one-page tiles: keys past kv_end are still inside the tile's
-    // (allocated) page; K there is masked out of the scores and V is zeroed
-    // at store
+    // one-page tiles.  In the tile that crosses the split's visible end (the
+    // split's last), K rows past the end are loaded from the last visible row
+    // and V 8-slot runs past it from the run holding the last visible slot,
+    // so no cell past the end is read except the slots that share that run's
+    // 16-byte vector; those scores are masked and those V halves zeroed at
+    // store.  The branch is uniform and both arms issue the same loads.
     auto load_k_page = [&](int t0, int page, StagingK<D>& st) __attribute__((always_inline)) {
         load_meta_k(t0, st);
         const uint16_t* kb = kc + page * page_elems + (k_head_off + (t0 & (P - 1)) * D);
+        if (t0 + kKvTile <= kv_end) {
 #pragma unroll
-        for (int i = 0; i < StagingK<D>::KC; ++i) st.k[i] = *reinterpret_cast<const u32x4*>(kb + koff[i]);
+            for (int i = 0; i < StagingK<D>::KC; ++i) st.k[i] = *reinterpret_cast<const u32x4*>(kb + koff[i]);
+        } else {
+            const int kmax = kv_end - 1 - t0;
+#pragma unroll
+            for (int i = 0; i < StagingK<D>::KC; ++i) {
+                const int id = tid + kThreads * i;
+                st.k[i] = *reinterpret_cast<const u32x4*>(kb + min(id / CPR, kmax) * D + 8 * (id % CPR));
+            }
+        }
     };
     auto load_v_page = [&](int t0, int page, StagingV<D>& st) __attribute__((always_inline)) {
         st.t0 = t0;
         load_meta_v(t0, st);
         const uint16_t* vb = vc + page * page_elems + (k_head_off + (int64_t)(t0 & (P - 1)) * D);
+        if (t0 + kKvTile <= kv_end) {
 #pragma unroll
-        for (int i = 0; i < StagingV<D>::VC; ++i) st.v[i] = *reinterpret_cast<const u32x4*>(vb + voff[i]);
+            for (int i = 0; i < StagingV<D>::VC; ++i) st.v[i] = *reinterpret_cast<const u32x4*>(vb + voff[i]);
+        } else {
+            const int c = min(tid & 7, (kv_end - 1 - t0) >> 3);
+#pragma unroll
+            for (int i = 0; i < StagingV<D>::VC; ++i) {
+                const int d = (tid + kThreads * i) >> 3;
+                st.v[i] = *reinterpret_cast<const u32x4*>(vb + (c >> 2) * (kVSlotTile * D) + d * kVSlotTile +
+                                                          8 * (c & 3));
+            }
+        }
     };
     auto load_k = [&](int t0_req, StagingK<D>& st) __attribute__((always_inline)) {
         const int t0 = min(t0_req, last_t0);

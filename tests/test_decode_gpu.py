@@ -117,21 +117,20 @@ def test_qwen3_decode_full_size():
     launch configuration (automatic split) and forced one pass."""
     c = W.qwen3_decode()
     ref = ref_decode(c)
-    assert_attention_close(run_decode(c, 0), ref, "qwen3 decode auto")
-    assert_attention_close(run_decode(c, -1), ref, "qwen3 decode one pass")
+    assert_attention_close(run_decode(c, 0), ref, "decode 8 x 16384 auto (benchmark plan)")
+    assert_attention_close(run_decode(c, -1), ref, "decode 8 x 16384 one pass")
 
 
 @pytest.mark.parametrize("P", [16, 128])
 def test_varlen_decode(P):
-    """64 sequences with log-uniform lengths in [256, 32768]; the oracle checks a
-    sample of 12 sequences including the shortest and the longest."""
+    """64 sequences with log-uniform lengths in [256, 32768], every output
+    element against the oracle, in the benchmark's launch configuration (the
+    automatic plan: partitions of at most 2048 tokens, combined in the launch)
+    and forced to one pass per sequence."""
     c = W.varlen_decode(P)
-    got = run_decode(c, 0)
-    order = np.argsort(c.kv_lens)
-    pick = np.unique(np.concatenate([order[:3], order[-3:], np.linspace(0, 63, 6).astype(int)]))
-    ref = oracle.paged_decode(c.q[pick], c.k_pool, c.v_pool, c.block_tables[pick], c.kv_lens[pick],
-                              c.scale)
-    assert_attention_close(got[pick], ref, f"varlen P={P}")
+    ref = ref_decode(c)
+    assert_attention_close(run_decode(c, 0), ref, f"varlen decode P={P} auto (64 sequences)")
+    assert_attention_close(run_decode(c, -1), ref, f"varlen decode P={P} one pass (64 sequences)")
 
 
 def test_sharing_and_copy_on_write():

@@ -44,7 +44,7 @@ def test_every_declared_symbol_is_exported_and_bound():
 
 
 def test_version():
-    assert pa.pa_version() >= 100
+    assert pa.pa_version() >= 200
 
 
 def test_pool_golden_script():
@@ -171,21 +171,21 @@ def test_device_ops_validate_before_launch():
     null = ctypes.c_void_p(0)
     # unsupported head_dim / page size: rejected by the host before any HIP call
     bad = _desc(D=96)
-    assert lib.pa_decode(ctypes.byref(bad), null, null, null, null, null, null, None, 1, 1, 2,
+    assert lib.pa_decode(ctypes.byref(bad), null, null, null, null, null, null, None, None, 1, 1, 2,
                          1.0, 0, null, 0, null) == -2
     bad = _desc(P=24)
     assert lib.pa_prefill(ctypes.byref(bad), null, null, null, null, null, null, null, null, None,
-                          None, None, 1, 1, 1, 2, 1.0, 0, null, 0, null) == -2
+                          None, None, None, 1, 1, 1, 2, 1.0, 0, null, 0, null) == -2
     # GQA group of 3 is unsupported; non-multiple is invalid
-    assert lib.pa_decode(ctypes.byref(d), null, null, null, null, null, null, None, 1, 1, 6,
+    assert lib.pa_decode(ctypes.byref(d), null, null, null, null, null, null, None, None, 1, 1, 6,
                          1.0, 0, null, 0, null) == -2
-    assert lib.pa_decode(ctypes.byref(d), null, null, null, null, null, null, None, 1, 1, 3,
+    assert lib.pa_decode(ctypes.byref(d), null, null, null, null, null, null, None, None, 1, 1, 3,
                          1.0, 0, null, 0, null) == -1
     # null pointers
-    assert lib.pa_decode(ctypes.byref(d), null, null, null, null, null, null, None, 1, 1, 4,
+    assert lib.pa_decode(ctypes.byref(d), null, null, null, null, null, null, None, None, 1, 1, 4,
                          1.0, 0, null, 0, null) == -1
     assert "null" in pa.pa_last_error()
-    assert lib.pa_reshape_and_cache(None, null, null, null, null, 0, null, 1, null) == -1
+    assert lib.pa_reshape_and_cache(None, null, null, null, null, 0, null, None, 1, null) == -1
     # copy_blocks pair validation happens on the host
     dummy = (ctypes.c_void_p * 1)(ctypes.c_void_p(16))
     for pairs in ([1, 2, 3, 2], [1, 2, 2, 3], [1, 9]):
@@ -193,6 +193,66 @@ def test_device_ops_validate_before_launch():
         st = lib.pa_copy_blocks(ctypes.byref(d), dummy, dummy, 1,
                                 arr.ctypes.data_as(_lib.c_i32_p), len(pairs) // 2, null)
         assert st == -1, pairs
+
+
+def _p(a):
+    return None if a is None else np.ascontiguousarray(a, dtype=np.int32).ctypes.data_as(_lib.c_i32_p)
+
+
+@pytest.fixture
+def validate_env(monkeypatch):
+    def set_(on):
+        if on:
+            monkeypatch.setenv("PA_VALIDATE", "1")
+        else:
+            monkeypatch.delenv("PA_VALIDATE", raising=False)
+    return set_
+
+
+@pytest.mark.parametrize("validate", [False, True])
+def test_host_copies_are_range_checked_before_launch(validate, validate_env):
+    """Host copies of block tables and slot mappings are checked before any
+    launch: an out-of-range page id or slot, or a repeated slot, returns
+    PA_ERR_INVALID (the device pointers here are dummies that a launch would
+    fault on, so reaching a launch would not return -1).  Under PA_VALIDATE=1
+    the host copies become mandatory."""
+    validate_env(validate)
+    lib = _lib.load()
+    d = _desc(N=8, P=16, H=2, D=64)
+    dv = ctypes.c_void_p(256)            # never dereferenced on the host
+    # decode: 2 sequences of 20 and 3 tokens read entries [0, 2) and [0, 1)
+    kl = np.array([20, 3], np.int32)
+    for bt, bad in (([[1, 8, -1], [2, -1, -1]], "[0][1]"), ([[1, 7, -1], [-1, 0, 0]], "[1][0]")):
+        st = lib.pa_decode(ctypes.byref(d), dv, dv, dv, dv, dv, dv, _p(bt), _p(kl), 2, 3, 4, 1.0, -1,
+                           None, 0, None)
+        assert st == -1 and bad in pa.pa_last_error(), (bt, pa.pa_last_error())
+    # entries past a sequence's length are never read, so they are not checked
+    # (-1 padding there is fine); a table check needs the lengths
+    st = lib.pa_decode(ctypes.byref(d), dv, dv, dv, dv, dv, dv, _p([[1, 7, 99], [2, -5, 42]]), None, 2, 3, 4,
+                       1.0, -1, None, 0, None)
+    assert st == -1 and "kv_lens_host" in pa.pa_last_error()
+    # prefill: row 1's tokens see up to 17 cells (entries [0, 2)), row 0's 5
+    row = np.array([1, 0, 1, -1], np.int32)
+    kvl = np.array([17, 5, 17, 9], np.int32)
+    pos = np.array([16, 4, 10, 0], np.int32)
+    for bt, bad in (([[3, -1], [4, 8]], "[1][1]"), ([[-2, 0], [4, 5]], "[0][0]")):
+        st = lib.pa_prefill(ctypes.byref(d), dv, dv, dv, dv, dv, dv, dv, dv, _p(row), _p(kvl), _p(pos), _p(bt),
+                            4, 2, 2, 4, 1.0, 1, None, 0, None)
+        assert st == -1 and bad in pa.pa_last_error(), (bt, pa.pa_last_error())
+    # reshape_and_cache: slots past the pool (8 pages x 16) and repeated slots
+    for slots, what in (([0, 128, -1], "past the pool"), ([5, -1, 5], "twice")):
+        st = lib.pa_reshape_and_cache(ctypes.byref(d), dv, dv, dv, dv, 0, dv, _p(slots), 3, None)
+        assert st == -1 and what in pa.pa_last_error(), (slots, pa.pa_last_error())
+    # without host copies: mandatory under PA_VALIDATE=1, else not checked here
+    # (only the rejection is exercised: nothing may be launched on dummies)
+    if validate:
+        st = lib.pa_decode(ctypes.byref(d), dv, dv, dv, dv, dv, dv, None, _p(kl), 2, 3, 4, 1.0, -1, None, 0, None)
+        assert st == -1 and "PA_VALIDATE" in pa.pa_last_error()
+        st = lib.pa_prefill(ctypes.byref(d), dv, dv, dv, dv, dv, dv, dv, dv, _p(row), _p(kvl), _p(pos), None,
+                            4, 2, 2, 4, 1.0, 1, None, 0, None)
+        assert st == -1 and "PA_VALIDATE" in pa.pa_last_error()
+        st = lib.pa_reshape_and_cache(ctypes.byref(d), dv, dv, dv, dv, 0, dv, None, 3, None)
+        assert st == -1 and "PA_VALIDATE" in pa.pa_last_error()
 
 
 def test_workspace_sizes():

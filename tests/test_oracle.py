@@ -413,6 +413,70 @@ def test_copy_blocks():
         oracle.copy_blocks(ks, vs, [(1, 5), (5, 6)])
 
 
+def _labelled_pool(labels, page_shape, nan_at=None):
+    """Pool whose page i holds the binary16 value labels[i] everywhere; if
+    nan_at = (page, bits), one element of that page holds that NaN bit pattern."""
+    pool = np.empty((len(labels),) + page_shape, dtype=np.float16)
+    for i, x in enumerate(labels):
+        pool[i] = x
+    if nan_at is not None:
+        u = pool.view(np.uint16)
+        u[(nan_at[0],) + (0,) * len(page_shape)] = nan_at[1]
+    return pool
+
+
+def test_swap_blocks_hand_worked():
+    """Block swap between a device pool and a host reserve ("CacheFlow：基于
+    llama.cpp 的多请求 LLM 推理优化引擎", section 3, block swap; section
+    抢占与恢复机制, preempted blocks go to a CPU area and come back), worked by
+    hand: two layers, K pages [2][4][8] and V pages [2][1][8][4]; device pages
+    hold labels 10..13 (layer 0) and 20..23 (layer 1), host slots 90..92 and
+    95..97; V labels are the K labels + 0.5.  One NaN payload rides along."""
+    kshape, vshape = (2, 4, 8), (2, 1, 8, 4)
+    dk = [_labelled_pool([10, 11, 12, 13], kshape, nan_at=(2, 0x7E15)), _labelled_pool([20, 21, 22, 23], kshape)]
+    dv = [_labelled_pool([10.5, 11.5, 12.5, 13.5], vshape), _labelled_pool([20.5, 21.5, 22.5, 23.5], vshape)]
+    hk = [_labelled_pool([90, 91, 92], kshape), _labelled_pool([95, 96, 97], kshape)]
+    hv = [_labelled_pool([90.5, 91.5, 92.5], vshape), _labelled_pool([95.5, 96.5, 97.5], vshape)]
+    dev_bits = [x.view(np.uint16).copy() for x in dk + dv]
+    host_bits = [x.view(np.uint16).copy() for x in hk + hv]
+
+    # device -> host: (device page 2 -> host slot 0), (device page 1 -> host slot 2);
+    # with source and destination roles exchanged the host would read [90, 12, 10]
+    nk, nv = oracle.swap_blocks(dk, dv, hk, hv, [(2, 0), (1, 2)])
+    want_k = [[12, 91, 11], [22, 96, 21]]
+    want_v = [[12.5, 91.5, 11.5], [22.5, 96.5, 21.5]]
+    for layer in range(2):
+        for slot in range(3):
+            assert np.all(nv[layer][slot] == want_v[layer][slot])
+            ku = nk[layer][slot].view(np.uint16).ravel()
+            if layer == 0 and slot == 0:
+                # the NaN payload of device page 2, element 0, is copied bit for bit
+                assert ku[0] == 0x7E15 and np.all(nk[layer][slot].ravel()[1:] == 12)
+            else:
+                assert np.all(nk[layer][slot] == want_k[layer][slot])
+    # the sources and the caller's destination arrays are left unchanged
+    for x, b in zip(dk + dv, dev_bits):
+        assert np.array_equal(x.view(np.uint16), b)
+    for x, b in zip(hk + hv, host_bits):
+        assert np.array_equal(x.view(np.uint16), b)
+
+    # host -> device: (host slot 1 -> device page 3), (host slot 0 -> device page 1)
+    bk, bv = oracle.swap_blocks(nk, nv, dk, dv, [(1, 3), (0, 1)])
+    want_k = [[10, 12, 12, 91], [20, 22, 22, 96]]
+    want_v = [[10.5, 12.5, 12.5, 91.5], [20.5, 22.5, 22.5, 96.5]]
+    for layer in range(2):
+        for page in range(4):
+            assert np.all(bv[layer][page] == want_v[layer][page])
+            if layer == 0 and page in (1, 2):
+                # page 1 now holds what page 2 held, NaN payload included
+                assert np.array_equal(bk[layer][page].view(np.uint16), dk[0][2].view(np.uint16))
+            else:
+                assert np.all(bk[layer][page] == want_k[layer][page])
+    # a destination may appear only once
+    with pytest.raises(ValueError):
+        oracle.swap_blocks(dk, dv, hk, hv, [(0, 1), (2, 1)])
+
+
 # ---------------------------------------------------------------- allocator
 
 def test_allocator_golden_script():

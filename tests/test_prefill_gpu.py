@@ -108,16 +108,15 @@ def test_prefill_deterministic_and_permutation_invariant():
 
 
 def test_ua_prefill_full_size():
-    """512 tokens interleaved from 8 sequences after 2K-16K prefixes, in the
-    automatic launch configuration; oracle on every 8th token (64 tokens, all
-    8 sequences)."""
+    """512 tokens interleaved from 8 sequences after 2K-16K prefixes, every
+    output element against the oracle, in the automatic launch configuration
+    (the one the benchmark times) and unsplit."""
     c = W.ua_prefill()
     kd, vd, k2, v2 = write_new_tokens(c)
-    got = run_prefill(c, kd, vd, 0)
-    pick = np.arange(0, 512, 7)
-    ref = oracle.paged_attention(c.q[pick], k2, v2, c.block_tables, c.token_row[pick],
-                                 c.token_kv_len[pick], c.token_pos[pick], c.scale)
-    assert_attention_close(got[pick], ref, "ua prefill")
+    ref = oracle.paged_attention(c.q, k2, v2, c.block_tables, c.token_row, c.token_kv_len,
+                                 c.token_pos, c.scale)
+    assert_attention_close(run_prefill(c, kd, vd, 0), ref, "UA ubatch 512 tokens, automatic splits")
+    assert_attention_close(run_prefill(c, kd, vd, 1), ref, "UA ubatch 512 tokens, unsplit")
 
 
 def test_chunked_prefill_sampled_ubatches():
@@ -233,6 +232,9 @@ def test_chunked_prefill_concurrent_streams_bitwise(kv_splits):
         need = max(pa.pa_prefill_workspace_bytes(pa.cache_desc(kd, vd), cp.n_q_heads, u["row"], u["kvl"],
                                                  u["pos"], kv_splits) for u in ubs)
         ws = [torch.zeros(max(need, 1), dtype=torch.uint8, device="cuda") for _ in streams]
+        # the zero fill (and the pool upload) ran on the current stream
+        for st in streams:
+            st.wait_stream(torch.cuda.current_stream())
         outs = []
         for u in ubs:
             s, p0, n = u["s"], u["p0"], cp.chunk
@@ -266,12 +268,14 @@ def test_chunked_prefill_concurrent_streams_bitwise(kv_splits):
         assert_attention_close(conc_outs[j][pick], ref, f"sequence {s} last ubatch")
 
 
-def test_chunked_prefill_full_size_in_the_benchmark_schedule():
+def test_chunked_prefill_full_size_in_both_benchmark_schedules():
     """The timed prefill pass at full size (8 sequences x 16384 tokens, 512-token
-    ubatches) in the launch configuration the benchmark times: sequence s on
-    stream s, unsplit launches (kv_splits = 1), captured in one HIP graph and
-    replayed.  Sampled tokens of the first, a middle and the last ubatch are
-    checked against the oracle over a private host pool of their sequence."""
+    ubatches) in the two launch configurations the benchmark times: (a) sequence
+    s on stream s, unsplit launches (kv_splits = 1), captured in one HIP graph
+    and replayed; (b) one stream, the library's automatic split plan.  Every
+    output element of the first, a middle and the last ubatch (contexts 512,
+    8704 and 16384) is checked against the oracle, computed over a private host
+    pool of the ubatch's sequence."""
     import torch
     cp = W.chunked_prefill()
     P, Hkv, D = cp.page_size, cp.n_kv_heads, cp.head_dim
@@ -293,10 +297,21 @@ def test_chunked_prefill_full_size_in_the_benchmark_schedule():
         pos = np.arange(p0, p0 + n, dtype=np.int32)
         ubs.append(dict(s=s, p0=p0, row=row, kvl=kvl, pos=pos,
                         dev=[to_dev(x) for x in (slots, bt, row, kvl, pos)]))
-    check = {0: None, len(ubs) // 2 + 3: None, len(ubs) - 1: None}
-    outs = {j: torch.empty(cp.chunk, cp.n_q_heads, D, dtype=torch.float32, device="cuda") for j in check}
-    scratch = [torch.empty(cp.chunk, cp.n_q_heads, D, dtype=torch.float32, device="cuda")
-               for _ in range(cp.n_seqs)]
+    check = [0, len(ubs) // 2 + 3, len(ubs) - 1]
+    new_out = lambda: torch.empty(cp.chunk, cp.n_q_heads, D, dtype=torch.float32, device="cuda")  # noqa: E731
+    outs = {sched: {j: new_out() for j in check} for sched in ("streams", "one")}
+    scratch = [new_out() for _ in range(cp.n_seqs)]
+
+    def launch(j, stream, splits, out, ws=None):
+        u = ubs[j]
+        s, p0, n = u["s"], u["p0"], cp.chunk
+        slots, bt, row, kvl, pos = u["dev"]
+        pa.pa_reshape_and_cache(kd, vd, knd[s, p0:p0 + n], vnd[s, p0:p0 + n], slots, stream=stream)
+        pa.pa_prefill(qd[s, p0:p0 + n], kd, vd, bt, row, kvl, pos, float(cp.scale),
+                      token_row_host=u["row"], token_kv_len_host=u["kvl"], token_pos_host=u["pos"],
+                      kv_splits=splits, out=out, workspace=ws, stream=stream)
+
+    # (a) one stream per sequence, unsplit, one graph
     streams = [torch.cuda.Stream() for _ in range(cp.n_seqs)]
     g = torch.cuda.CUDAGraph()
     s0 = streams[0]
@@ -306,18 +321,21 @@ def test_chunked_prefill_full_size_in_the_benchmark_schedule():
             for st in streams[1:]:
                 st.wait_stream(s0)
             for j, u in enumerate(ubs):
-                s, p0, n = u["s"], u["p0"], cp.chunk
-                slots, bt, row, kvl, pos = u["dev"]
-                pa.pa_reshape_and_cache(kd, vd, knd[s, p0:p0 + n], vnd[s, p0:p0 + n], slots, stream=streams[s])
-                pa.pa_prefill(qd[s, p0:p0 + n], kd, vd, bt, row, kvl, pos, float(cp.scale),
-                              token_row_host=u["row"], token_kv_len_host=u["kvl"], token_pos_host=u["pos"],
-                              kv_splits=1, out=outs.get(j, scratch[s]), stream=streams[s])
+                launch(j, streams[u["s"]], 1, outs["streams"].get(j, scratch[u["s"]]))
             for st in streams[1:]:
                 s0.wait_stream(st)
     torch.cuda.current_stream().wait_stream(s0)
     g.replay()
     torch.cuda.synchronize()
-    pick = np.array([0, 1, 63, 64, 255, 256, 500, 511])
+    del g
+    # (b) one stream, automatic split plan (rewrites the same K/V bits)
+    stream = torch.cuda.current_stream()
+    need = max(pa.pa_prefill_workspace_bytes(pa.cache_desc(kd, vd), cp.n_q_heads, u["row"], u["kvl"], u["pos"], 0)
+               for u in ubs)
+    ws = torch.zeros(max(need, 1), dtype=torch.uint8, device="cuda")
+    for j in range(len(ubs)):
+        launch(j, stream, 0, outs["one"].get(j, scratch[0]), ws)
+    torch.cuda.synchronize()
     for j in check:
         u = ubs[j]
         s, p0, n = u["s"], u["p0"], cp.chunk
@@ -326,9 +344,12 @@ def test_chunked_prefill_full_size_in_the_benchmark_schedule():
         kh, vh = oracle.reshape_and_cache(kh, vh, cp.k[s, :n_ctx], cp.v[s, :n_ctx],
                                           np.arange(n_ctx, dtype=np.int32))
         bt_priv = np.arange(n_ctx // P, dtype=np.int32)[None, :]
-        ref = oracle.paged_attention(cp.q[s, p0:p0 + n][pick], kh, vh, bt_priv, np.zeros(len(pick), np.int32),
-                                     u["kvl"][pick], u["pos"][pick], cp.scale)
-        assert_attention_close(to_host(outs[j])[pick], ref, f"ubatch {j} (sequence {s}, tokens {p0}..)")
+        ref = oracle.paged_attention(cp.q[s, p0:p0 + n], kh, vh, bt_priv, np.zeros(n, np.int32),
+                                     u["kvl"], u["pos"], cp.scale)
+        del kh, vh
+        for sched, what in (("streams", "8 streams, kv_splits=1, graph"), ("one", "one stream, automatic splits")):
+            assert_attention_close(to_host(outs[sched][j]), ref,
+                                   f"8x16384 pass ubatch {j} (sequence {s}, context {n_ctx}), {what}")
 
 
 @pytest.mark.parametrize("kv_splits", [1, 0])

@@ -3,7 +3,12 @@
 Storage format of a cache pool (one layer), shared by every consumer:
 
 * K pool: float16 ``[num_pages][n_kv_heads][page_size][head_dim]``
-* V pool: float16 ``[num_pages][n_kv_heads][head_dim][page_size]``
+* V pool: float16 ``[num_pages][n_kv_heads][page_size // B][head_dim][B]`` with
+  ``B = min(page_size, 32)``: a page's slots in blocks of B, each block slot
+  innermost (for page_size <= 32 this is ``[num_pages][n_kv_heads][head_dim][page_size]``).
+  V values are drawn as columns ``[num_pages][n_kv_heads][head_dim][page_size]``
+  and then laid into this storage (``v_blocks_from_columns``), so what a seed
+  gives does not depend on the storage layout.
 
 A *cell* is one (page, slot) position.  Cells that hold no token of a live
 sequence (free pages, padding after a sequence's last token, cells whose token
