@@ -313,6 +313,28 @@ pa_status pa_decode(const pa_cache_desc* desc, const void* k_cache, const void* 
                     int32_t max_pages, int32_t n_q_heads, float scale, int32_t partition_tokens,
                     void* workspace, size_t workspace_bytes, pa_stream stream);
 
+/* Paged decode that allocates nothing, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation.  Same arguments, meaning, results and errors as
+ * pa_decode, without the workspace: the split partials and completion
+ * counters live in a fixed device array of the library (one per GPU, of
+ * pa_decode_noalloc_scratch_bytes() = 32 MiB, held until the process ends).
+ * The caller still passes every input and output.  Limits, checked before any
+ * launch: pa_decode_workspace_bytes() for the same arguments must not exceed
+ * the scratch size (else PA_ERR_WORKSPACE), and n_seqs * n_kv_heads must not
+ * exceed 16384 (else PA_ERR_UNSUPPORTED).  No call allocates: the first call
+ * on a device looks the array up and clears its counters with one small kernel
+ * on `stream`.  Every call on a GPU uses that GPU's one array, so calls that
+ * overlap in time on one GPU (other streams, other threads) race; calls on
+ * one stream may follow one another in any shapes. */
+pa_status pa_decode_noalloc(const pa_cache_desc* desc, const void* k_cache, const void* v_cache,
+                            const float* q, float* out, const int32_t* block_tables,
+                            const int32_t* kv_lens, const int32_t* block_tables_host,
+                            const int32_t* kv_lens_host, int32_t n_seqs, int32_t max_pages,
+                            int32_t n_q_heads, float scale, int32_t partition_tokens,
+                            pa_stream stream);
+size_t    pa_decode_noalloc_scratch_bytes(void);
+
 /* Workspace bytes pa_prefill needs for these arguments (0 if no tile's KV
  * range is split).  Same meaning of arguments as pa_prefill.  A prefill
  * workspace starts with per-(tile, KV head) completion counters (a region of

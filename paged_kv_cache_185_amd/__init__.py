@@ -26,6 +26,7 @@ __all__ = [
     "PaError", "InvalidError", "UnsupportedError", "NoPagesError", "StateError", "HipError",
     "WorkspaceError", "CacheDesc", "cache_desc", "pa_version", "pa_last_error", "Pool",
     "pa_reshape_and_cache", "pa_copy_blocks", "pa_swap_blocks", "pa_decode_workspace_bytes", "pa_decode",
+    "pa_decode_noalloc", "pa_decode_noalloc_scratch_bytes",
     "pa_prefill_workspace_bytes", "pa_prefill", "pa_unified_workspace_bytes",
     "pa_unified_attention", "library_path",
 ]
@@ -426,6 +427,40 @@ def pa_decode(q, k_cache, v_cache, block_tables, kv_lens, scale: float, kv_lens_
         _dev(kv_lens, torch.int32, "kv_lens", 1), _i32p(bh), _i32p(kl), S, max_pages, Hq, float(scale),
         int(partition_tokens), ws_ptr, ws_bytes, ctypes.c_void_p(st.cuda_stream)))
     return out
+
+
+def pa_decode_noalloc(q, k_cache, v_cache, block_tables, kv_lens, scale: float, kv_lens_host=None,
+                      partition_tokens: int = 0, out=None, stream=None, block_tables_host=None):
+    """pa_decode without a workspace: the split partials live in the library's
+    fixed per-GPU scratch (pa_decode_noalloc_scratch_bytes()).  Allocates
+    nothing when ``out`` is given.  Calls that overlap in time on one GPU race."""
+    import torch
+    desc = cache_desc(k_cache, v_cache)
+    _dev(q, torch.float32, "q", 3)
+    _dev(block_tables, torch.int32, "block_tables", 2)
+    _dev(kv_lens, torch.int32, "kv_lens", 1)
+    S, Hq, D = (int(x) for x in q.shape)
+    _need(D == desc.head_dim, "q head_dim does not match the cache")
+    _need(int(block_tables.shape[0]) >= S, f"block_tables needs at least {S} rows")
+    _need(int(kv_lens.shape[0]) == S, f"kv_lens must hold {S} entries")
+    _need(out is None or tuple(out.shape) == tuple(q.shape), "out must have q's shape")
+    kl = _host_copy(kv_lens_host, kv_lens)
+    bh = _host_copy(block_tables_host, block_tables)
+    _need(kl is None or kl.shape == (S,), f"kv_lens_host must hold {S} entries")
+    _need(bh is None or bh.shape == tuple(block_tables.shape), "block_tables_host must have block_tables' shape")
+    st = _launch_stream(stream)
+    out, _ = _alloc_out_ws(q, out, None, 0, st)
+    _check(_L().pa_decode_noalloc(
+        ctypes.byref(desc), _dev(k_cache, torch.float16, "k_cache", 4),
+        _dev(v_cache, torch.float16, "v_cache", 5), _dev(q, torch.float32, "q", 3),
+        _dev(out, torch.float32, "out", 3), _dev(block_tables, torch.int32, "block_tables", 2),
+        _dev(kv_lens, torch.int32, "kv_lens", 1), _i32p(bh), _i32p(kl), S, int(block_tables.shape[1]), Hq,
+        float(scale), int(partition_tokens), ctypes.c_void_p(st.cuda_stream)))
+    return out
+
+
+def pa_decode_noalloc_scratch_bytes() -> int:
+    return int(_L().pa_decode_noalloc_scratch_bytes())
 
 
 def pa_prefill_workspace_bytes(desc: CacheDesc, n_q_heads: int, token_row_host, token_kv_len_host,

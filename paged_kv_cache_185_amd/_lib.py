@@ -60,6 +60,9 @@ SIGNATURES = {
     "pa_decode": (c_i32, [CacheDesc_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                           c_i32_p, c_i32_p, c_i32, c_i32, c_i32, c_float, c_i32, c_void_p, c_size_t,
                           c_void_p]),
+    "pa_decode_noalloc": (c_i32, [CacheDesc_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                  c_i32_p, c_i32_p, c_i32, c_i32, c_i32, c_float, c_i32, c_void_p]),
+    "pa_decode_noalloc_scratch_bytes": (c_size_t, []),
     "pa_prefill_workspace_bytes": (c_size_t, [CacheDesc_p, c_i32, c_i32, c_i32_p, c_i32_p, c_i32_p,
                                               c_i32]),
     "pa_prefill": (c_i32, [CacheDesc_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,

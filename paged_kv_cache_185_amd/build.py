@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpa.so")
 
-SOURCES = ["api.cpp", "pool.cpp", "cache_ops.hip", "decode.hip", "prefill.hip"]
+SOURCES = ["api.cpp", "pool.cpp", "cache_ops.hip", "decode.hip", "prefill.hip", "noalloc.hip"]
 
 
 def hipcc() -> str:

@@ -502,6 +502,20 @@ pa_status pa_decode(const pa_cache_desc* desc, const void* k_cache, const void* 
                     const int32_t* kv_lens_host, int32_t n_seqs,
                     int32_t max_pages, int32_t n_q_heads, float scale, int32_t partition_tokens,
                     void* workspace, size_t workspace_bytes, pa_stream stream) {
+    return pa::run_decode(desc, k_cache, v_cache, q, out, block_tables, kv_lens, block_tables_host,
+                          kv_lens_host, n_seqs, max_pages, n_q_heads, scale, partition_tokens, workspace,
+                          workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+// Validation, planning and the launch of pa_decode, given the workspace (also
+// the path of pa_decode_noalloc, whose workspace is the library's scratch).
+pa_status pa::run_decode(const pa_cache_desc* desc, const void* k_cache, const void* v_cache, const float* q,
+                         float* out, const int32_t* block_tables, const int32_t* kv_lens,
+                         const int32_t* block_tables_host, const int32_t* kv_lens_host, int32_t n_seqs,
+                         int32_t max_pages, int32_t n_q_heads, float scale, int32_t partition_tokens,
+                         void* workspace, size_t workspace_bytes, pa_stream stream) {
     pa_status st = check_desc("pa_decode", desc);
     if (st != PA_OK) return st;
     if ((st = check_heads("pa_decode", desc, n_q_heads)) != PA_OK) return st;
@@ -568,6 +582,8 @@ pa_status pa_decode(const pa_cache_desc* desc, const void* k_cache, const void* 
     if (e != hipSuccess) return hip_fail("pa_decode", e);
     return PA_OK;
 }
+
+extern "C" {
 
 size_t pa_prefill_workspace_bytes(const pa_cache_desc* desc, int32_t n_tokens, int32_t n_q_heads,
                                   const int32_t* token_row_host, const int32_t* token_kv_len_host,

@@ -5,7 +5,21 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <string>
+
+#include "pa.h"
+
 namespace pa {
+
+// Message for pa_last_error() on the calling thread.
+void set_error(const std::string& msg);
+
+// pa_decode's validation, planning and launch with a given workspace.
+pa_status run_decode(const pa_cache_desc* desc, const void* k_cache, const void* v_cache, const float* q,
+                     float* out, const int32_t* block_tables, const int32_t* kv_lens,
+                     const int32_t* block_tables_host, const int32_t* kv_lens_host, int32_t n_seqs,
+                     int32_t max_pages, int32_t n_q_heads, float scale, int32_t partition_tokens,
+                     void* workspace, size_t workspace_bytes, pa_stream stream);
 
 // ---- V page layout ----------------------------------------------------------
 // A V page of one KV head holds its slots in blocks of T = min(P, kVSlotTile)
