@@ -12,6 +12,18 @@ cache by the previous one.  The K timed steps are one HIP graph replay (as a
 serving engine replays a captured decode step).  value = valid K+V bytes x
 steps / wall time between two device synchronizations; roofline.achieved =
 valid bytes / (HIP-event time of the replay on the launch stream / steps).
+Per-call distributions (median / p10 / p90) come from --samples back-to-back
+replays of one-call graphs with an event between consecutive replays: "cold"
+rotates over the cache copies, "warm" repeats one copy.
+--decode-workload varlen16 / varlen128 makes the 64-sequence log-uniform batch
+the headline instead (config.workload follows).
+
+Also measured (each as per-call distributions):
+* variable-length decode: 64 sequences, lengths log-uniform in [256, 32768],
+  pages of 16 and of 128 tokens (one pass vs split-and-reduce per sequence);
+* the UA ubatch: 512 tokens interleaved from 8 sequences after 2K-16K
+  prefixes, one pa_prefill (automatic plan), against the dense f16 MFMA peak
+  and against min(MFMA peak, intensity x HBM peak).
 
 Prefill workload (reported beside it): 8 fresh sequences x 16384 tokens
 prefilled in 512-token ubatches, chunk-major; each ubatch is one
@@ -30,8 +42,9 @@ must not change a result).  The one-stream pass (every launch after the
 previous one, with the library's automatic split plan, which fills the GPU
 from one launch) is timed and reported beside it.
 
-cpu_baseline: the float64 CPU oracle on the machine's host cores, timed on the full
-decode batch (one step) and on one prefill ubatch.
+cpu_baseline: the float64 CPU oracle on the machine's host cores, timed on whole
+decode steps of the headline batch, on four prefill ubatches spread over the
+chunked pass, and on the full UA ubatch.
 """
 from __future__ import annotations
 
@@ -64,8 +77,23 @@ def blas_threads():
         return None
 
 
+def blas_info():
+    """The BLAS library numpy uses and its thread count (threadpoolctl)."""
+    try:
+        from threadpoolctl import threadpool_info
+        for i in threadpool_info():
+            if i.get("user_api") == "blas":
+                return {"library": i.get("internal_api"), "version": i.get("version"),
+                        "threads": i.get("num_threads"), "file": os.path.basename(i.get("filepath", ""))}
+    except Exception:
+        pass
+    return None
+
+
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_kernel_hbm_traffic_8x16k.txt")
-DECODE_SOURCES = [os.path.join(ROOT, "paged_kv_cache_185_amd", "csrc", "decode.hip")]
+# the decode kernel and the host code that plans its launch (partition sizes, grid)
+DECODE_SOURCES = [os.path.join(ROOT, "paged_kv_cache_185_amd", "csrc", f)
+                  for f in ("decode.hip", "api.cpp", "pa_internal.h")]
 
 
 def decode_sources_sha256():
@@ -98,8 +126,9 @@ def prefill_mfma_busy():
 
 def decode_traffic():
     """Calibrated HBM bytes per decode launch (FETCH_SIZE + WRITE_SIZE) from the
-    committed counter summary, or None when the decode sources have changed
-    since the counters were taken (or there is no summary)."""
+    committed counter summary, or None when the decode kernel or its launch
+    planning (decode.hip, api.cpp, pa_internal.h) has changed since the
+    counters were taken (or there is no summary)."""
     try:
         kv = {}
         with open(TRAFFIC_FILE) as fh:
@@ -114,11 +143,61 @@ def decode_traffic():
         return None
 
 
-def bench_decode(args, pa, torch, W):
-    if args.decode_workload == "qwen3":
-        c = W.qwen3_decode()
-    else:   # "varlen16" / "varlen128": 64 sequences, log-uniform lengths
-        c = W.varlen_decode(int(args.decode_workload[len("varlen"):]))
+def capture_graph(torch, fn, n=1):
+    """fn(i, stream) for i in range(n), captured as one HIP graph on a side stream."""
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            for i in range(n):
+                fn(i, torch.cuda.current_stream())
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    return g
+
+
+def per_call_ms(torch, graph, calls_per_replay, n):
+    """Per-call GPU time from n back-to-back replays of a graph of
+    `calls_per_replay` calls, with an event recorded between consecutive
+    replays on the replay stream: each sample is one replay's time divided by
+    its calls (a replay of a one-call graph adds a launch gap of several
+    microseconds that a serving loop's multi-call graph spreads over its
+    calls).  An untimed replay goes first so the GPU is busy while the timed
+    ones are enqueued."""
+    stream = torch.cuda.current_stream()
+    graph.replay()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    ev[0].record(stream)
+    for i in range(n):
+        graph.replay()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    return np.array([ev[i].elapsed_time(ev[i + 1]) / calls_per_replay for i in range(n)])
+
+
+def stats_us(ms):
+    us = np.asarray(ms) * 1e3
+    return {"n": int(us.size), "mean_us": round(float(us.mean()), 2), "median_us": round(float(np.median(us)), 2),
+            "p10_us": round(float(np.percentile(us, 10)), 2), "p90_us": round(float(np.percentile(us, 90)), 2)}
+
+
+def decode_case(W, name):
+    if name == "qwen3":
+        return W.qwen3_decode()
+    return W.varlen_decode(int(name[len("varlen"):]))   # "varlen16" / "varlen128"
+
+
+def workload_text(name, c):
+    if name == "qwen3":
+        return ("paged decode: 8 sequences x 16384 tokens, 32 query / 8 KV heads, head_dim 128, "
+                "f16 pages of 128 tokens in a 2048-page pool")
+    return (f"paged decode: {len(c.kv_lens)} sequences, lengths log-uniform in [256, 32768] "
+            f"(sum {int(np.sum(c.kv_lens))}), 32 query / 8 KV heads, head_dim 128, f16 pages of "
+            f"{c.page_size} tokens in a {c.num_pages}-page pool")
+
+
+def bench_decode(args, pa, torch, W, c):
     dev = torch.device("cuda:0")
     k0 = torch.from_numpy(c.k_pool).to(dev)
     v0 = torch.from_numpy(c.v_pool).to(dev)
@@ -142,28 +221,15 @@ def bench_decode(args, pa, torch, W):
     # warmup steps are a second graph replayed first.
     call(0, torch.cuda.current_stream())
     torch.cuda.synchronize()
-
-    def capture(n):
-        g = torch.cuda.CUDAGraph()
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            with torch.cuda.graph(g, stream=side):
-                for i in range(n):
-                    call(i % args.layers, torch.cuda.current_stream())
-        torch.cuda.current_stream().wait_stream(side)
-        torch.cuda.synchronize()
-        return g
-
     stream = torch.cuda.current_stream()
     if args.eager:
         run = lambda: [call(i % args.layers, stream) for i in range(args.steps)]   # noqa: E731
         for i in range(args.warmup):
             call(i % args.layers, stream)
     else:
-        timed = capture(args.steps)
+        timed = capture_graph(torch, lambda i, st: call(i % args.layers, st), args.steps)
         if args.warmup:
-            capture(args.warmup).replay()
+            capture_graph(torch, lambda i, st: call(i % args.layers, st), args.warmup).replay()
         run = timed.replay
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -173,19 +239,112 @@ def bench_decode(args, pa, torch, W):
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    call_ms = np.array([e0.elapsed_time(e1) / args.steps])
+    call_ms_mean = e0.elapsed_time(e1) / args.steps
     valid = W.decode_valid_bytes(c.kv_lens, c.n_kv_heads, c.head_dim)
-    res = {
-        "valid_bytes": valid,
-        "wall_s": wall,
-        "ms_per_step": wall * 1e3 / args.steps,
-        "call_ms_mean": float(call_ms.mean()),
-        "call_ms_median": float(np.median(call_ms)),
-        "call_ms_p10": float(np.percentile(call_ms, 10)),
-        "call_ms_p90": float(np.percentile(call_ms, 90)),
-        "workspace_bytes": ws_bytes,
-    }
-    return c, res
+    res = {"valid_bytes": valid, "wall_s": wall, "ms_per_step": wall * 1e3 / args.steps,
+           "call_ms_mean": call_ms_mean, "workspace_bytes": ws_bytes}
+    if args.samples > 0:
+        k = args.calls_per_replay
+        g = capture_graph(torch, lambda i, st: call(i % args.layers, st), k)
+        res["cold"] = stats_us(per_call_ms(torch, g, k, args.samples))
+        g = capture_graph(torch, lambda i, st: call(0, st), k)
+        res["warm"] = stats_us(per_call_ms(torch, g, k, args.samples))
+        del g
+    return res
+
+
+def gbs_block(st, nbytes):
+    """A per-call distribution with the rate and HBM fraction at its median."""
+    out = dict(st)
+    out["GBps_at_median"] = round(nbytes / (st["median_us"] * 1e-6) / 1e9, 1)
+    out["hbm_frac_at_median"] = round(nbytes / (st["median_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+    return out
+
+
+def bench_varlen(args, pa, torch, W, P):
+    """64 sequences, lengths log-uniform in [256, 32768], pages of P tokens: one
+    pa_decode per call on the automatic plan (partitions of at most 2048
+    tokens, combined in the launch).  Every call reads ~1.76 GB, seven times
+    the 256 MB last-level cache, so no rotation is needed to keep it cold."""
+    c = W.varlen_decode(P)
+    dev = torch.device("cuda:0")
+    k = torch.from_numpy(c.k_pool).to(dev)
+    v = torch.from_numpy(c.v_pool).to(dev)
+    q = torch.from_numpy(c.q).to(dev)
+    bt = torch.from_numpy(c.block_tables).to(dev)
+    kl = torch.from_numpy(c.kv_lens).to(dev)
+    out = torch.empty_like(q)
+    desc = pa.cache_desc(k, v)
+    ws_bytes = pa.pa_decode_workspace_bytes(desc, c.n_seqs, c.n_q_heads, c.block_tables.shape[1], c.kv_lens, 0)
+    ws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+
+    def call(i, stream):
+        pa.pa_decode(q, k, v, bt, kl, float(c.scale), kv_lens_host=c.kv_lens, out=out, workspace=ws,
+                     stream=stream)
+
+    call(0, torch.cuda.current_stream())
+    g = capture_graph(torch, call, args.calls_per_replay)
+    st = stats_us(per_call_ms(torch, g, args.calls_per_replay, args.samples))
+    valid = W.decode_valid_bytes(c.kv_lens, c.n_kv_heads, c.head_dim)
+    res = gbs_block(st, valid)
+    res.update(valid_bytes=valid, n_seqs=int(c.n_seqs), kv_len_min=int(c.kv_lens.min()),
+               kv_len_max=int(c.kv_lens.max()), kv_len_sum=int(c.kv_lens.sum()), page_size=P,
+               num_pages=int(c.num_pages))
+    del g, k, v
+    return res
+
+
+def bench_ua_ubatch(args, pa, torch, W, oracle_timer=None):
+    """The UA ubatch: 512 tokens interleaved from 8 sequences (64 new tokens
+    each) after prefixes of 2K-16K tokens, K/V of the new tokens written first;
+    one pa_prefill per call on the automatic plan.  Cold: rotating over
+    --layers copies of the pool; warm: one copy."""
+    c = W.ua_prefill()
+    dev = torch.device("cuda:0")
+    k0, v0 = torch.from_numpy(c.k_pool).to(dev), torch.from_numpy(c.v_pool).to(dev)
+    pa.pa_reshape_and_cache(k0, v0, torch.from_numpy(c.k_new).to(dev), torch.from_numpy(c.v_new).to(dev),
+                            torch.from_numpy(c.slot_mapping).to(dev), slot_mapping_host=c.slot_mapping)
+    ks = [k0] + [k0.clone() for _ in range(args.layers - 1)]
+    vs = [v0] + [v0.clone() for _ in range(args.layers - 1)]
+    q = torch.from_numpy(c.q).to(dev)
+    o = torch.empty_like(q)
+    bt, row = torch.from_numpy(c.block_tables).to(dev), torch.from_numpy(c.token_row).to(dev)
+    kvl, pos = torch.from_numpy(c.token_kv_len).to(dev), torch.from_numpy(c.token_pos).to(dev)
+    desc = pa.cache_desc(k0, v0)
+    ws = torch.zeros(max(1, pa.pa_prefill_workspace_bytes(desc, c.n_q_heads, c.token_row, c.token_kv_len,
+                                                          c.token_pos)), dtype=torch.uint8, device=dev)
+
+    def call(layer, stream):
+        pa.pa_prefill(q, ks[layer], vs[layer], bt, row, kvl, pos, float(c.scale), token_row_host=c.token_row,
+                      token_kv_len_host=c.token_kv_len, token_pos_host=c.token_pos, out=o, workspace=ws,
+                      stream=stream)
+
+    call(0, torch.cuda.current_stream())
+    k = args.calls_per_replay
+    g = capture_graph(torch, lambda i, st: call(i % args.layers, st), k)
+    cold = stats_us(per_call_ms(torch, g, k, args.samples))
+    g = capture_graph(torch, lambda i, st: call(0, st), k)
+    warm = stats_us(per_call_ms(torch, g, k, args.samples))
+    del g
+    pairs = W.prefill_pairs(c.token_kv_len, c.token_pos)
+    flops = W.attention_flops(pairs, c.n_q_heads, c.head_dim)
+    lens = np.zeros(c.block_tables.shape[0], dtype=np.int64)
+    for r, n in zip(c.token_row, c.token_kv_len):
+        lens[r] = max(lens[r], n)
+    kv_bytes = W.decode_valid_bytes(lens, c.n_kv_heads, c.head_dim)
+    intensity = flops / kv_bytes
+    roof_tflops = min(MFMA_F16_PEAK_TFLOPS, intensity * HBM_PEAK_GBS / 1e3)
+
+    def rates(st):
+        tf = flops / (st["median_us"] * 1e-6) / 1e12
+        return dict(st, tflops_at_median=round(tf, 1), frac_of_mfma_peak=round(tf / MFMA_F16_PEAK_TFLOPS, 4),
+                    frac_of_roofline=round(tf / roof_tflops, 4))
+    return {"workload": "512 tokens interleaved round-robin from 8 sequences (64 new each) after prefixes "
+                        f"{int(lens.min()) - 64}..{int(lens.max()) - 64} tokens; one pa_prefill, automatic plan",
+            "flops": flops, "valid_kv_bytes": int(kv_bytes), "intensity_flop_per_byte": round(intensity, 1),
+            "roofline_tflops": round(roof_tflops, 1),
+            "roofline_bound": "hbm" if roof_tflops < MFMA_F16_PEAK_TFLOPS else "mfma",
+            "cold": rates(cold), "warm": rates(warm)}, c
 
 
 def bench_prefill(args, pa, torch, W):
@@ -237,6 +396,12 @@ def bench_prefill(args, pa, torch, W):
                       float(cp.scale), token_row_host=pl["row_h"], token_kv_len_host=pl["kvl_h"],
                       token_pos_host=pl["pos_h"], kv_splits=splits, out=out, workspace=ws, stream=stream)
 
+    def pass_stats(per_ms):
+        return {"n": int(per_ms.size), "median_ms": round(float(np.median(per_ms)), 4),
+                "p10_ms": round(float(np.percentile(per_ms, 10)), 4),
+                "p90_ms": round(float(np.percentile(per_ms, 90)), 4),
+                "tflops_at_median": round(flops / (float(np.median(per_ms)) * 1e-3) / 1e12, 1)}
+
     def one_pass(streams, splits):
         # sequence s runs on stream s % len(streams): a sequence's chunks stay
         # in order, different sequences' ubatches may overlap
@@ -265,33 +430,37 @@ def bench_prefill(args, pa, torch, W):
         return g
 
     def time_pass(g):
+        """Mean ms per pass over --prefill-reps replays (and the wall time), plus
+        the per-pass distribution of those replays (events between them)."""
         g.replay()   # warm replay
         torch.cuda.synchronize()
         stream = torch.cuda.current_stream()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.prefill_reps + 1)]
         t0 = time.perf_counter()
-        e0.record(stream)
-        for _ in range(args.prefill_reps):
+        ev[0].record(stream)
+        for i in range(args.prefill_reps):
             g.replay()
-        e1.record(stream)
+            ev[i + 1].record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        return e0.elapsed_time(e1) / args.prefill_reps, wall * 1e3 / args.prefill_reps
+        per = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(args.prefill_reps)])
+        return ev[0].elapsed_time(ev[-1]) / args.prefill_reps, wall * 1e3 / args.prefill_reps, per
 
     # eager pass once (warms the code paths and fills the cache)
     one_pass([torch.cuda.current_stream()], 0)
     torch.cuda.synchronize()
     # one stream, automatic split plan: every launch waits for the previous one
     g1 = capture(1, 0)
-    ms1, wall1 = time_pass(g1)
+    ms1, wall1, per1 = time_pass(g1)
     last_seq = cp.n_seqs - 1
     ref_auto = outs[0].clone()   # the last ubatch of the pass: the last sequence's last chunk
     del g1
     res = {"ubatches": len(plans), "flops": flops, "pairs": pairs, "reps": args.prefill_reps,
            "streams": n_str, "splits": args.prefill_splits, "one_stream_ms": ms1,
-           "one_stream_tflops": flops / (ms1 * 1e-3) / 1e12}
+           "one_stream_tflops": flops / (ms1 * 1e-3) / 1e12, "one_stream_pass": pass_stats(per1)}
     g = capture(n_str, args.prefill_splits)
-    ms, wall = time_pass(g)
+    ms, wall, per = time_pass(g)
+    res["pass"] = pass_stats(per)
     del g
     # the last ubatch again, alone and eager, with the same plan: concurrency
     # must not change it; against the automatic plan it differs only by the
@@ -605,24 +774,40 @@ def cpu_baseline_prefill(cp, oracle, W, ubatch_indices=(3, 11, 19, 27)):
     return total, flops, what
 
 
+def cpu_baseline_ua(c, oracle):
+    """The oracle on the whole UA ubatch (all 512 tokens), over pools holding
+    the new tokens' K/V (the oracle's own reshape_and_cache, untimed);
+    returns seconds."""
+    k, v = oracle.reshape_and_cache(c.k_pool, c.v_pool, c.k_new, c.v_new, c.slot_mapping)
+    t0 = time.perf_counter()
+    oracle.paged_attention(c.q, k, v, c.block_tables, c.token_row, c.token_kv_len, c.token_pos, c.scale)
+    return time.perf_counter() - t0
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=48)
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--layers", type=int, default=4, help="cache copies rotated over decode steps")
+    ap.add_argument("--samples", type=int, default=60,
+                    help="replays behind each per-call distribution (median / p10 / p90); 0 skips them")
+    ap.add_argument("--calls-per-replay", type=int, default=8,
+                    help="calls in the graph whose replays give the per-call distributions")
     ap.add_argument("--partition-tokens", type=int, default=0)
     ap.add_argument("--eager", action="store_true", help="time decode steps as eager calls, not graph replays")
     ap.add_argument("--decode-workload", default="qwen3", choices=["qwen3", "varlen16", "varlen128"],
                     help="qwen3 = the 8 x 16384 headline batch; varlen* = 64 log-uniform sequences")
     ap.add_argument("--prefill-len", type=int, default=16384)
-    ap.add_argument("--prefill-reps", type=int, default=3)
+    ap.add_argument("--prefill-reps", type=int, default=50)
     ap.add_argument("--prefill-streams", type=int, default=8,
                     help="streams the prefill pass's sequences are spread over (1 = every launch in order)")
     ap.add_argument("--prefill-splits", type=int, default=1,
                     help="kv_splits of the multi-stream prefill schedule (0: the library's plan, which "
                          "fills the GPU from one launch; the one-stream pass always uses it)")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-varlen", action="store_true", help="skip the variable-length decode batches")
+    ap.add_argument("--no-ua", action="store_true", help="skip the UA ubatch")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-unified", action="store_true",
                     help="skip the paged-vs-unified-span comparison")
@@ -654,11 +839,30 @@ def main():
         log(f"copied {args.copy_bytes} bytes 3 times")
         return
     log(f"library {pa.library_path()}")
-    log("decode: generating 8 x 16384 workload")
-    c, dec = bench_decode(args, pa, torch, W)
+    log(f"decode: generating the {args.decode_workload} workload")
+    c = decode_case(W, args.decode_workload)
+    dec = bench_decode(args, pa, torch, W, c)
     gbs = dec["valid_bytes"] * args.steps / dec["wall_s"] / 1e9
     achieved = dec["valid_bytes"] / (dec["call_ms_mean"] * 1e-3) / 1e9
     log(f"decode: {dec['call_ms_mean'] * 1e3:.1f} us/call (events), {gbs:.0f} GB/s wall")
+    if "cold" in dec:
+        log(f"decode per call: cold {json.dumps(dec['cold'])}, warm {json.dumps(dec['warm'])}")
+    torch.cuda.empty_cache()
+
+    varlen = {}
+    if not args.no_varlen and args.samples > 0:
+        for P in (16, 128):
+            log(f"varlen decode P={P}")
+            varlen[f"P{P}"] = bench_varlen(args, pa, torch, W, P)
+            log(f"varlen decode P={P}: {json.dumps(varlen[f'P{P}'])}")
+            torch.cuda.empty_cache()
+
+    ua = ua_case = None
+    if not args.no_ua and args.samples > 0:
+        log("UA ubatch")
+        ua, ua_case = bench_ua_ubatch(args, pa, torch, W)
+        log(f"UA ubatch: {json.dumps(ua)}")
+        torch.cuda.empty_cache()
 
     pre = None
     cp = None
@@ -667,6 +871,7 @@ def main():
         cp, _, pre = bench_prefill(args, pa, torch, W)
         log(f"prefill: {pre['pass_ms']:.2f} ms/pass, {pre['tflops']:.1f} TFLOP/s over {pre['streams']} "
             f"stream(s); one stream {pre['one_stream_ms']:.2f} ms/pass, {pre['one_stream_tflops']:.1f} TFLOP/s")
+        torch.cuda.empty_cache()
 
     uni = None
     if not args.no_unified:
@@ -691,10 +896,12 @@ def main():
         import oracle
         log("cpu baseline: oracle decode steps on the full batch")
         dt, nsteps = cpu_baseline_decode(c, oracle)
+        blas = blas_info()
         cpu = {"value": dec["valid_bytes"] * nsteps / dt / 1e9, "unit": "GB/s", "kind": "oracle",
-               "cores": blas_threads() or os.cpu_count(),
-               "host_cpus": os.cpu_count(), "affinity": len(os.sched_getaffinity(0)),
-               "sample": f"{nsteps} decode steps over all 8 sequences x 16384 tokens (the full batch)",
+               "cores": (blas or {}).get("threads") or os.cpu_count(),
+               "host_cpus": os.cpu_count(), "affinity": len(os.sched_getaffinity(0)), "blas": blas,
+               "sample": f"{nsteps} decode steps over the whole headline batch "
+                         f"({len(c.kv_lens)} sequences, {int(np.sum(c.kv_lens))} tokens)",
                "seconds": dt}
         if cp is not None:
             log("cpu baseline: oracle prefill ubatches")
@@ -702,6 +909,11 @@ def main():
             cpu["prefill_tflops"] = fl / dtp / 1e12
             cpu["prefill_sample"] = what
             cpu["prefill_seconds"] = dtp
+        if ua_case is not None:
+            log("cpu baseline: oracle on the whole UA ubatch")
+            dtu = cpu_baseline_ua(ua_case, oracle)
+            cpu["ua_ubatch_seconds"] = dtu
+            cpu["ua_ubatch_tflops"] = ua["flops"] / dtu / 1e12
         log(f"cpu baseline: {cpu['value']:.2f} GB/s")
 
     result = {
@@ -718,8 +930,7 @@ def main():
         "dtype": "f16",
         "data": "synthetic",
         "config": {
-            "workload": "paged decode: 8 sequences x 16384 tokens, 32 query / 8 KV heads, head_dim 128, "
-                        "f16 pages of 128 tokens in a 2048-page pool",
+            "workload": workload_text(args.decode_workload, c),
             "step": "one pa_decode call over the batch; the timed steps are one HIP graph replay",
             "layers_rotated": args.layers,
             "partition_tokens": args.partition_tokens,
@@ -732,12 +943,26 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": decode_traffic(),
+            "traffic": decode_traffic() if args.decode_workload == "qwen3" else None,
             "bytes_per_launch": dec["valid_bytes"],
             "call_us_mean": round(dec["call_ms_mean"] * 1e3, 2),
         },
         "cpu_baseline": cpu,
     }
+    if "cold" in dec:
+        result["decode_per_call"] = {
+            "method": f"{dec['cold']['n']} back-to-back replays of a graph of {args.calls_per_replay} calls, an "
+                      "event between consecutive replays; each sample is a replay's time / its calls",
+            "cold": gbs_block(dec["cold"], dec["valid_bytes"]),
+            "cold_is": f"rotating over {args.layers} cache copies (no call finds its K/V in the 256 MB "
+                       "last-level cache)",
+            "warm": gbs_block(dec["warm"], dec["valid_bytes"]),
+            "warm_is": "the same cache copy every call",
+        }
+    if varlen:
+        result["varlen_decode"] = varlen
+    if ua is not None:
+        result["ua_ubatch"] = ua
     if pre is not None:
         result["prefill"] = {
             "workload": f"8 fresh sequences x {args.prefill_len} tokens in 512-token ubatches "
@@ -747,6 +972,7 @@ def main():
             "tflops": round(pre["tflops"], 2),
             "frac_of_mfma_f16_peak": round(pre["tflops"] / MFMA_F16_PEAK_TFLOPS, 4),
             "ms_per_pass": round(pre["pass_ms"], 4),
+            "pass": pre["pass"],
             "roofline": {"kernel": "prefill_kernel (pa_prefill)", "bound": "mfma",
                          "achieved": round(pre["tflops"], 1), "peak": MFMA_F16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(pre["tflops"] / MFMA_F16_PEAK_TFLOPS, 4),
@@ -755,7 +981,8 @@ def main():
             "one_stream": {"schedule": "every launch after the previous one, automatic split plan",
                            "tflops": round(pre["one_stream_tflops"], 2),
                            "frac_of_mfma_f16_peak": round(pre["one_stream_tflops"] / MFMA_F16_PEAK_TFLOPS, 4),
-                           "ms_per_pass": round(pre["one_stream_ms"], 4)},
+                           "ms_per_pass": round(pre["one_stream_ms"], 4),
+                           "pass": pre["one_stream_pass"]},
             "flops_per_pass": pre["flops"],
             "ubatches": pre["ubatches"],
             "reps": pre["reps"],
