@@ -14,13 +14,16 @@
 //   Workgroups are numbered KV-head-fastest: on an 8-XCD part with 8 KV heads
 //   every workgroup of one head lands on the same XCD, and the tiles and
 //   splits of that head share its K/V through that XCD's L2.
-// * K and V tiles of 64 keys are staged through LDS (double buffered, XOR
-//   swizzled in 16-byte units so the MFMA operand reads are free of bank
-//   conflicts) and shared by the 8 waves.  Global loads run two tiles ahead
-//   of the MFMA work (two register sets); MFMA operands are read from LDS a
-//   k-step or two ahead of their use.  When the page size is a multiple of 64
-//   a tile never crosses a page, and its addresses are one scalar page base
-//   plus fixed per-thread offsets.
+// * K and V tiles of 64 keys live in LDS (XOR swizzled in 16-byte units so
+//   the MFMA operand reads are free of bank conflicts) and are shared by the
+//   8 waves.  They are loaded global -> LDS directly (global_load_lds, the
+//   swizzle applied on the source side), triple buffered, each tile four
+//   barrier phases before its first use, with no staging registers and no
+//   LDS stores.  MFMA operands are read from LDS a k-step or two ahead of
+//   their use.  When the page size is a multiple of 64 a tile never crosses
+//   a page, and its addresses are one scalar page base plus fixed per-thread
+//   offsets.  (The unified-span mode stages tiles through registers, double
+//   buffered, since its V store zeroes free cells anywhere in a tile.)
 // * Both products run on v_mfma_f32_32x32x16_f16 with fp32 accumulation.
 //   Scores are computed transposed, S^T = K Q^T (rows = keys, columns =
 //   queries): each lane's C registers belong to one query column, so the
@@ -30,20 +33,24 @@
 //   holds for each P.V k-step are contiguous, which lets the V operand be one
 //   16-byte LDS read from the slot-innermost V tile.
 // * Q is multiplied by scale*log2(e) and rounded to binary16 once, so scores
-//   come out of the MFMA already in the log2 domain; P is rounded to binary16
-//   for the P.V product; row sums and accumulators are fp32.
+//   come out of the MFMA already in the log2 domain, and the score chain
+//   starts from -m (the running max), so they come out relative to it; P is
+//   rounded to binary16 for the P.V product; row sums and accumulators are
+//   fp32.
 // * The running maximum is raised only when a new score exceeds it by more
 //   than 8 (log2 units): until then P <= 2^8 stays exact enough in binary16
 //   and the output rescale (a multiply per accumulator) is skipped.
 // * Masking is by select (scores -> -inf), and only on tiles that cross some
-//   token's visible end.  V cells at or past the split's visible end are
-//   zeroed in registers before they reach LDS (only the last tile has any),
-//   so NaN padding never meets a zero weight.
+//   token's visible end.  V cells at or past the split's visible end (only
+//   in its last tile) are zeroed in LDS by the lanes that loaded them before
+//   the tile is published, so NaN padding never meets a zero weight.
 // * Long KV ranges are split across workgroups.  Each split stores its
 //   (m, l, acc) partial; the last split of a (tile, KV head) to finish, found
 //   with a device-scope counter, combines them by log-sum-exp in the same
 //   launch.
 #include <math.h>
+
+#include <type_traits>
 
 #include "pa_internal.h"
 
@@ -105,18 +112,55 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// s_waitcnt on the vector-memory count only (vmcnt in bits 3:0 and 15:14;
+// expcnt, bits 6:4, and lgkmcnt, bits 11:8, left at their maxima)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier of the LDS-direct pipeline.  A release fence on LDS makes
+// the compiler wait for every outstanding LDS-direct load (vmcnt(0)) before
+// the barrier, which would drain the prefetch each phase.  Here the caller
+// waits for exactly the loads the next phase reads (wait_vmcnt), this wave's
+// own LDS accesses complete before the barrier (lgkmcnt(0)), and empty asm
+// statements with a memory clobber keep the compiler from moving memory
+// accesses across it.
+__device__ __forceinline__ void dma_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt at their maxima
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// K or V tile moved by LDS-direct loads: 16-byte chunks per tile and per thread
+template <int D>
+struct DmaTile {
+    static constexpr int CH = kKvTile * D / 8;
+    static constexpr int PER = CH / kThreads;
+    static_assert(PER * kThreads == CH, "a tile is a whole number of chunks per thread");
+};
+
 // score row i of a 32-key block <-> key offset (bits 2 and 3 swapped)
 __device__ __forceinline__ int kappa(int i) {
     return (i & ~0xC) | ((i & 4) << 1) | ((i & 8) >> 1);
 }
 
-template <int D>
-struct Smem {
-    u32x4 k[2][kKvTile * D / 8];   // [buf][key][D/8 chunks], chunk swizzled by key % 8
-    u32x4 v[2][D * kKvTile / 8];   // [buf][d][8 chunks of 8 keys], chunk swizzled by d % 8
+struct SmemMeta {
     int32_t tok[kRows];
     int32_t last;   // this workgroup combines the tile's splits
-    int32_t kcode[2][kKvTile];  // unified span: cell code of each key of a K buffer
+};
+
+// Register-staged K/V tiles (unified span only).  Layout of a K tile:
+// [key][D/8 chunks], chunk swizzled by kswz(key); of a V tile: [d][8 chunks of
+// 8 keys], chunk swizzled by vswz(d).  The paged mode keeps the same tile
+// layout in separate LDS arrays filled by LDS-direct loads.
+template <int D>
+struct SmemStaged {
+    u32x4 k[2][kKvTile * D / 8];
+    u32x4 v[2][D * kKvTile / 8];
+    int32_t kcode[2][kKvTile];  // cell code of each key of a K buffer
 };
 
 template <int D>
@@ -168,7 +212,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, Til
     const int kv_begin = split * tile.split_len;
     const int kv_end = min(tile.kv_end, kv_begin + tile.split_len);
 
-    __shared__ Smem<D> sm;
+    __shared__ SmemMeta sm;
+    __shared__ SmemStaged<D> ss;   // referenced by the unified-span path only
+    // paged mode: triple-buffered K and V tiles, filled by LDS-direct loads
+    constexpr int TCH = DmaTile<D>::CH;
+    __shared__ u32x4 kt0[TCH], kt1[TCH], kt2[TCH], vt0[TCH], vt1[TCH], vt2[TCH];
     extern __shared__ int32_t sm_pages[];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -376,14 +424,14 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, Til
             const int id = tid + kThreads * i;
             const int key = id / CPR;
             const int c = id % CPR;
-            sm.k[buf][key * CPR + (c ^ kswz<D>(key))] = st.k[i];
+            ss.k[buf][key * CPR + (c ^ kswz<D>(key))] = st.k[i];
         }
         if constexpr (UNIFIED) {
-            if (tid < kKvTile) sm.kcode[buf][tid] = st.kcode;
+            if (tid < kKvTile) ss.kcode[buf][tid] = st.kcode;
         }
     };
     auto store_v = [&](int buf, StagingV<D>& st) __attribute__((always_inline)) {
-        if constexpr (UNIFIED) {
+        {
             // zero the V halves of free cells and of keys past the split
             uint32_t mk[4];
 #pragma unroll
@@ -394,25 +442,99 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, Til
             for (int i = 0; i < StagingV<D>::VC; ++i)
 #pragma unroll
                 for (int w = 0; w < 4; ++w) st.v[i][w] &= mk[w];
-        } else if (st.t0 + kKvTile > kv_end) {
-            // zero the V halves of keys at or past the visible end (only the
-            // last tile of a split has any)
-            const int nvalid = max(0, min(8, kv_end - (st.t0 + 8 * (tid & 7))));
-            uint32_t mk[4];
-#pragma unroll
-            for (int w = 0; w < 4; ++w)
-                mk[w] = (2 * w < nvalid ? 0x0000ffffu : 0u) | (2 * w + 1 < nvalid ? 0xffff0000u : 0u);
-#pragma unroll
-            for (int i = 0; i < StagingV<D>::VC; ++i)
-#pragma unroll
-                for (int w = 0; w < 4; ++w) st.v[i][w] &= mk[w];
         }
 #pragma unroll
         for (int i = 0; i < StagingV<D>::VC; ++i) {
             const int id = tid + kThreads * i;
             const int d = id >> 3;
             const int c = id & 7;
-            sm.v[buf][d * 8 + (c ^ vswz(d))] = st.v[i];
+            ss.v[buf][d * 8 + (c ^ vswz(d))] = st.v[i];
+        }
+    };
+
+    // ---- paged mode: LDS-direct tile loads.  One global_load_lds_dwordx4
+    // moves 16 bytes per lane into 64 consecutive 16-byte LDS chunks at a
+    // wave-uniform base, so the swizzle is applied on the source side: LDS
+    // chunk p = tid + kThreads*i of a tile receives the logical chunk that
+    // the swizzled layout keeps at p.  The chunk column a lane fetches is the
+    // same for every i; only the key (K) or value row (V) moves with i.
+    const int ck = (tid % CPR) ^ kswz<D>(tid / CPR);   // K: chunk of the key row
+    const int cv = (tid & 7) ^ vswz(tid >> 3);          // V: 8-key run of the value row
+    const int wbase = __builtin_amdgcn_readfirstlane(wave) * 64;
+    auto dma16 = [&](const uint16_t* src, u32x4* dst) __attribute__((always_inline)) {
+        __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+    };
+    auto dma_k = [&](u32x4* dst, int t0_req) __attribute__((always_inline)) {
+        const int t0 = min(t0_req, last_t0);
+        // rows at or past the visible end are fetched from the last visible
+        // row (their scores are masked)
+        const int kmax = min(kKvTile - 1, kv_end - 1 - t0);
+        if constexpr (ONE_PAGE) {
+            const int page = __builtin_amdgcn_readfirstlane(sm_pages[(t0 >> sh) - page_base]);
+            const uint16_t* kb = kc + page * page_elems + (k_head_off + (t0 & (P - 1)) * D + 8 * ck);
+#pragma unroll
+            for (int i = 0; i < DmaTile<D>::PER; ++i) {
+                const int key = min(tid / CPR + (kThreads / CPR) * i, kmax);
+                dma16(kb + key * D, dst + kThreads * i + wbase);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < DmaTile<D>::PER; ++i) {
+                const int t = t0 + min(tid / CPR + (kThreads / CPR) * i, kmax);
+                const int page = sm_pages[(t >> sh) - page_base];
+                dma16(kc + page * page_elems + (k_head_off + (t & (P - 1)) * D + 8 * ck),
+                      dst + kThreads * i + wbase);
+            }
+        }
+    };
+    auto dma_v = [&](u32x4* dst, int t0_req) __attribute__((always_inline)) {
+        const int t0 = min(t0_req, last_t0);
+        // 8-slot runs at or past the visible end are fetched from the run
+        // holding the last visible slot; fix_v_tail zeroes what lies past it
+        const int c = min(cv, (kv_end - 1 - t0) >> 3);
+        if constexpr (ONE_PAGE) {
+            // V slot blocks of kVSlotTile slots: the tile is two whole blocks
+            const int page = __builtin_amdgcn_readfirstlane(sm_pages[(t0 >> sh) - page_base]);
+            const uint16_t* vb = vc + page * page_elems +
+                                 (k_head_off + (int64_t)(t0 & (P - 1)) * D + (c >> 2) * (kVSlotTile * D) +
+                                  8 * (c & 3));
+#pragma unroll
+            for (int i = 0; i < DmaTile<D>::PER; ++i) {
+                const int d = (tid >> 3) + (kThreads / 8) * i;
+                dma16(vb + d * kVSlotTile, dst + kThreads * i + wbase);
+            }
+        } else {
+            // keys tb..tb+7 (8-aligned, below kv_end) lie in one slot block
+            const int tb = t0 + 8 * c;
+            const int vpage = sm_pages[(tb >> sh) - page_base];
+            const int VT = v_slot_tile(P);
+            const int vslot = tb & (P - 1);
+            const uint16_t* vbase = vc + vpage * page_elems +
+                                    (k_head_off + (int64_t)(vslot & ~(VT - 1)) * D + (vslot & (VT - 1)));
+#pragma unroll
+            for (int i = 0; i < DmaTile<D>::PER; ++i) {
+                const int d = (tid >> 3) + (kThreads / 8) * i;
+                dma16(vbase + d * VT, dst + kThreads * i + wbase);
+            }
+        }
+    };
+    // Zero the V halves of keys at or past the visible end in the chunks this
+    // lane loaded into the split's last V tile, once its own loads are done
+    // and before the barrier that publishes the tile.
+    auto fix_v_tail = [&](u32x4* vt, int t0) __attribute__((always_inline)) {
+        const int nvalid = kv_end - (t0 + 8 * cv);
+        if (nvalid < 8) {
+            uint32_t mk[4];
+#pragma unroll
+            for (int w = 0; w < 4; ++w)
+                mk[w] = (2 * w < nvalid ? 0x0000ffffu : 0u) | (2 * w + 1 < nvalid ? 0xffff0000u : 0u);
+#pragma unroll
+            for (int i = 0; i < DmaTile<D>::PER; ++i) {
+                u32x4 x = vt[kThreads * i + tid];
+#pragma unroll
+                for (int w = 0; w < 4; ++w) x[w] &= mk[w];
+                vt[kThreads * i + tid] = x;
+            }
         }
     };
 
@@ -423,8 +545,15 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, Til
     for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[db][r] = 0.0f;
-    f32x16 s[2];   // scores of the tile between its two phases
-    float m_use_s = 0.0f;   // running max as subtracted before exp2 (0 while none seen)
+    f32x16 s[2];   // scores of the tile between its two phases, minus m_use
+    float m_use = 0.0f;   // running max the scores are taken relative to (0 while none seen)
+    // -m_use in all 16 rows (every row of a lane's accumulator block belongs
+    // to the lane's query column): the score MFMA chain starts from it, so
+    // scores come out already relative to the running max and the softmax
+    // needs no subtraction
+    f32x16 negm;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) negm[r] = 0.0f;
 
     // S^T = K Q^T for the 64 keys t0..t0+63 in K buffer `buf`, then the
     // first half of the online softmax: the mask (`full`, uniform, says every
@@ -434,16 +563,12 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, Til
     // faster than in the softmax half).  K operands are read from LDS two
     // k-steps ahead of their MFMAs, and the two 32-key blocks alternate so
     // consecutive MFMAs are independent.
-    auto qk = [&](int buf, int t0, bool full) __attribute__((always_inline)) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) s[kb][r] = 0.0f;
+    auto qk = [&](const u32x4* kt, const int32_t* kcode, int t0, bool full) __attribute__((always_inline)) {
         const int krow0 = kappa(col);
         const int krow1 = 32 + kappa(col);
         auto kread = [&](int ks, int krow) __attribute__((always_inline)) {
             const int c = 2 * ks + hh;
-            return sm.k[buf][krow * CPR + (c ^ kswz<D>(krow))];
+            return kt[krow * CPR + (c ^ kswz<D>(krow))];
         };
         // ring of kKDepth+1 k-steps of operands, kKDepth in flight
         constexpr int R = kKDepth + 1;
@@ -461,8 +586,13 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, Til
             }
             // keep the scheduler from sinking the reads back to their use
             __builtin_amdgcn_sched_barrier(0);
-            s[0] = mfma32(ka[ks % R], qb[ks], s[0]);
-            s[1] = mfma32(kb1[ks % R], qb[ks], s[1]);
+            if (ks == 0) {
+                s[0] = mfma32(ka[0], qb[0], negm);
+                s[1] = mfma32(kb1[0], qb[0], negm);
+            } else {
+                s[0] = mfma32(ka[ks % R], qb[ks], s[0]);
+                s[1] = mfma32(kb1[ks % R], qb[ks], s[1]);
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
         if constexpr (UNIFIED) {
@@ -476,8 +606,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, Til
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
                     const int k0 = 32 * kb + 16 * j + 8 * hh;
-                    const int4 c0 = *reinterpret_cast<const int4*>(&sm.kcode[buf][k0]);
-                    const int4 c1 = *reinterpret_cast<const int4*>(&sm.kcode[buf][k0 + 4]);
+                    const int4 c0 = *reinterpret_cast<const int4*>(&kcode[k0]);
+                    const int4 c1 = *reinterpret_cast<const int4*>(&kcode[k0 + 4]);
                     const int cd[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
@@ -506,7 +636,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, Til
                                                              false, false);
             mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
         }
-        // raise the running max only when the new one is well above it
+        mx += m_use;   // the tile's maximum in absolute terms
+        // raise the running max only when the new one is well above it; then
+        // rescale the accumulators and re-base this tile's scores and the
+        // chain start on the new max
         const bool raise = mx > m_run + kRescaleSlack;
         if (__ballot(raise)) {
             const float m_new = raise ? mx : m_run;
@@ -515,24 +648,31 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, Til
 #pragma unroll
             for (int db = 0; db < DB; ++db) acc[db] *= alpha;
             m_run = m_new;
+            const float m_use_new = m_run == -INFINITY ? 0.0f : m_run;
+            const float shift = m_use - m_use_new;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) s[kb][r] += shift;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) negm[r] = -m_use_new;
+            m_use = m_use_new;
         }
-        m_use_s = m_run == -INFINITY ? 0.0f : m_run;
     };
 
     // Second half of the online softmax of the scores (P = exp2(s - m), row
     // sums) and O^T += V^T P^T with V buffer `buf`.
-    auto smpv = [&](int buf) __attribute__((always_inline)) {
+    auto smpv = [&](const u32x4* vt) __attribute__((always_inline)) {
         // this wave's softmax and P.V are the phase's longer chain: its
         // instructions go first when both waves of a SIMD can issue (measured
         // 1% faster; priority on the score MFMAs instead is 2.5% slower)
         __builtin_amdgcn_s_setprio(1);
-        const float m_use = m_use_s;
         // 16 keys per k-step: P is made just before its MFMAs and the V
         // operands of the next k-step are read from LDS meanwhile
         auto vread = [&](int ks, int db) __attribute__((always_inline)) {
             const int c = 2 * ks + hh;
             const int d = 32 * db + col;
-            return sm.v[buf][d * 8 + (c ^ vswz(d))];
+            return vt[d * 8 + (c ^ vswz(d))];
         };
         // ring of kVDepth+1 k-steps of V operands, kVDepth in flight
         constexpr int RV = kVDepth + 1;
@@ -553,7 +693,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, Til
             f16x8 p;
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                p[e] = (_Float16)__builtin_amdgcn_exp2f(s[ks >> 1][8 * (ks & 1) + e] - m_use);
+                p[e] = (_Float16)__builtin_amdgcn_exp2f(s[ks >> 1][8 * (ks & 1) + e]);
 #pragma unroll
             for (int e = 0; e < 8; e += 2) {
                 const f16x2 pp = {p[e], p[e + 1]};
@@ -577,28 +717,15 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, Til
     // the score MFMAs, mask and row maximum of a tile while the other runs
     // the exps and P.V MFMAs of the previous one, so matrix and vector work
     // of the two waves on a SIMD overlap.  Tile j: A does QK(j) in phase 2j
-    // and softmax+PV(j) in phase 2j+1, B one phase later.  K(j) is read in
-    // phases 2j and 2j+1, V(j) in 2j+1 and 2j+2; both are double buffered,
-    // K stored in the odd phase before its first use and V in the even one.
-    // Global loads run two phases (one tile) ahead of their LDS stores and
-    // are clamped onto the last tile past the end, so every phase issues the
-    // same loads.
-    // Each group runs its own loop (same loads, stores and barriers per
-    // phase, 2*n_tiles+1 phases in all) so that register lifetimes stay
+    // and softmax+PV(j) in phase 2j+1, B one phase later, so K(j) is read in
+    // phases 2j and 2j+1 and V(j) in phases 2j+1 and 2j+2; 2*n_tiles+1
+    // phases in all, each ended by a barrier.  Each group runs its own loop
+    // (same loads and barriers per phase) so that register lifetimes stay
     // simple for the compiler.
     const int wgroup = __builtin_amdgcn_readfirstlane(wave >> 2);
-    StagingK<D> stk;
-    StagingV<D> stv;
-    if constexpr (ONE_PAGE) {
-        load_k_page(kv_begin, page0, stk);
-        load_v_page(kv_begin, page0, stv);
-    } else {
-        load_k(kv_begin, stk);
-        load_v(kv_begin, stv);
-    }
     // Q times scale*log2(e), rounded to binary16: scores come out of the MFMA
     // in the log2 domain
-    {
+    auto make_q = [&]() __attribute__((always_inline)) {
         const float qs = tok >= 0 ? a.scale_log2 : 0.0f;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
@@ -610,47 +737,165 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, Til
             for (int e = 0; e < 8; ++e) h[e] = (_Float16)(xs[e] * qs);
             qb[ks] = __builtin_bit_cast(u32x4, h);
         }
-    }
+    };
 
-    n_vis = tok >= 0 ? min(tok_kv_len, tok_pos + 1) : 0;
-    store_k(0, stk);
-    load_k(kv_begin + kKvTile, stk);
-    __syncthreads();
-    if (wgroup == 0) {
-        for (int j = 0; j < n_tiles; ++j) {
-            const int tj = kv_begin + j * kKvTile;
-            // phase 2j: V(j) -> LDS; QK(j)
-            store_v(j & 1, stv);
-            load_v(tj + kKvTile, stv);
-            qk(j & 1, tj, tj + kKvTile <= min_vis);
-            lds_barrier();
-            // phase 2j+1: K(j+1) -> LDS; softmax+PV(j)
-            store_k((j + 1) & 1, stk);
-            load_k(tj + 2 * kKvTile, stk);
-            smpv(j & 1);
-            lds_barrier();
+    if constexpr (UNIFIED) {
+        // Unified span: tiles go global -> registers -> LDS (the V store
+        // zeroes free cells), double buffered; global loads run two phases
+        // (one tile) ahead of their LDS stores and are clamped onto the last
+        // tile past the end, so every phase issues the same loads.  K(j) is
+        // stored in the phase before its first use, V(j) likewise.
+        StagingK<D> stk;
+        StagingV<D> stv;
+        if constexpr (ONE_PAGE) {
+            load_k_page(kv_begin, page0, stk);
+            load_v_page(kv_begin, page0, stv);
+        } else {
+            load_k(kv_begin, stk);
+            load_v(kv_begin, stv);
         }
-        // phase 2n: the other group's last softmax+PV
-        store_v(n_tiles & 1, stv);
-        lds_barrier();
-    } else {
-        // phase 0: the other group's first QK
-        store_v(0, stv);
-        load_v(kv_begin + kKvTile, stv);
-        lds_barrier();
-        for (int j = 0; j < n_tiles; ++j) {
-            const int tj = kv_begin + j * kKvTile;
-            // phase 2j+1: K(j+1) -> LDS; QK(j)
-            store_k((j + 1) & 1, stk);
-            load_k(tj + 2 * kKvTile, stk);
-            qk(j & 1, tj, tj + kKvTile <= min_vis);
+        make_q();
+        n_vis = tok >= 0 ? min(tok_kv_len, tok_pos + 1) : 0;
+        store_k(0, stk);
+        load_k(kv_begin + kKvTile, stk);
+        __syncthreads();
+        if (wgroup == 0) {
+            for (int j = 0; j < n_tiles; ++j) {
+                const int tj = kv_begin + j * kKvTile;
+                // phase 2j: V(j) -> LDS; QK(j)
+                store_v(j & 1, stv);
+                load_v(tj + kKvTile, stv);
+                qk(ss.k[j & 1], ss.kcode[j & 1], tj, false);
+                lds_barrier();
+                // phase 2j+1: K(j+1) -> LDS; softmax+PV(j)
+                store_k((j + 1) & 1, stk);
+                load_k(tj + 2 * kKvTile, stk);
+                smpv(ss.v[j & 1]);
+                lds_barrier();
+            }
+            // phase 2n: the other group's last softmax+PV
+            store_v(n_tiles & 1, stv);
             lds_barrier();
-            // phase 2j+2: V(j+1) -> LDS; softmax+PV(j)
-            store_v((j + 1) & 1, stv);
-            load_v(tj + 2 * kKvTile, stv);
-            smpv(j & 1);
+        } else {
+            // phase 0: the other group's first QK
+            store_v(0, stv);
+            load_v(kv_begin + kKvTile, stv);
             lds_barrier();
+            for (int j = 0; j < n_tiles; ++j) {
+                const int tj = kv_begin + j * kKvTile;
+                // phase 2j+1: K(j+1) -> LDS; QK(j)
+                store_k((j + 1) & 1, stk);
+                load_k(tj + 2 * kKvTile, stk);
+                qk(ss.k[j & 1], ss.kcode[j & 1], tj, false);
+                lds_barrier();
+                // phase 2j+2: V(j+1) -> LDS; softmax+PV(j)
+                store_v((j + 1) & 1, stv);
+                load_v(tj + 2 * kKvTile, stv);
+                smpv(ss.v[j & 1]);
+                lds_barrier();
+            }
         }
+    } else if (n_tiles > 0) {
+        // Paged mode: tiles go global -> LDS directly (global_load_lds), K and
+        // V triple buffered, so no staging registers and no LDS stores; a
+        // tile's loads are issued four phases before its first use.  The
+        // loads form one stream of groups, G(2m) = K(m) and G(2m+1) = V(m),
+        // tile m in buffer m % 3; the prologue issues G(0..3), phase p issues
+        // G(p+4) and ends with this wave's G(p+1) complete (three later groups
+        // may stay in flight), then the barrier makes every wave's G(p+1)
+        // visible before phase p+1 reads it.  G(p+4) overwrites the buffer of
+        // tile m-3, whose last reader ran in phase p-1 or earlier.  Loads
+        // past the last tile are clamped onto it (never read), so every phase
+        // issues the same loads and the wait count is the same everywhere.
+        // The loop is unrolled by three so that every buffer is a distinct
+        // LDS variable at every access: the compiler then orders an operand
+        // read only after the loads into its own buffer.  Each pass runs all
+        // three steps (up to two past the last tile only load and take their
+        // barriers): exits inside the unrolled body made the compiler drain
+        // every load (vmcnt(0)) at the top of each pass.
+        auto kt = [&](auto bc) __attribute__((always_inline)) -> u32x4* {
+            if constexpr (decltype(bc)::value == 0) return kt0;
+            else if constexpr (decltype(bc)::value == 1) return kt1;
+            else return kt2;
+        };
+        auto vt = [&](auto bc) __attribute__((always_inline)) -> u32x4* {
+            if constexpr (decltype(bc)::value == 0) return vt0;
+            else if constexpr (decltype(bc)::value == 1) return vt1;
+            else return vt2;
+        };
+        using B0 = std::integral_constant<int, 0>;
+        using B1 = std::integral_constant<int, 1>;
+        using B2 = std::integral_constant<int, 2>;
+        // end of a phase: this wave's loads issued before the last three
+        // groups are complete (and, for the last tile's V, its tail zeroed)
+        auto phase_wait = [&]() __attribute__((always_inline)) {
+            __builtin_amdgcn_sched_barrier(0);
+            wait_vmcnt<3 * DmaTile<D>::PER>();
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        n_vis = tok >= 0 ? min(tok_kv_len, tok_pos + 1) : 0;
+        dma_k(kt0, kv_begin);
+        dma_v(vt0, kv_begin);
+        dma_k(kt1, kv_begin + kKvTile);
+        dma_v(vt1, kv_begin + kKvTile);
+        make_q();
+        phase_wait();   // G(0) = K(0)
+        dma_barrier();
+        if (wgroup == 0) {
+            auto a_tile = [&](auto bc, int j) __attribute__((always_inline)) {
+                constexpr int B = decltype(bc)::value;
+                using Bn2 = std::integral_constant<int, (B + 2) % 3>;
+                const int tj = kv_begin + j * kKvTile;
+                // phase 2j: load K(j+2); QK(j)
+                dma_k(kt(Bn2{}), tj + 2 * kKvTile);
+                if (j < n_tiles) qk(kt(bc), nullptr, tj, tj + kKvTile <= min_vis);
+                phase_wait();   // V(j)
+                if (j == n_tiles - 1) fix_v_tail(vt(bc), tj);
+                dma_barrier();
+                // phase 2j+1: load V(j+2); softmax+PV(j)
+                dma_v(vt(Bn2{}), tj + 2 * kKvTile);
+                if (j < n_tiles) smpv(vt(bc));
+                phase_wait();   // K(j+1)
+                dma_barrier();
+            };
+            for (int j = 0; j < n_tiles; j += 3) {
+                a_tile(B0{}, j);
+                a_tile(B1{}, j + 1);
+                a_tile(B2{}, j + 2);
+            }
+            // phase 2n: the other group's last softmax+PV
+            dma_barrier();
+        } else {
+            // phase 0: the other group's first QK; load K(2)
+            dma_k(kt2, kv_begin + 2 * kKvTile);
+            phase_wait();   // V(0)
+            if (n_tiles == 1) fix_v_tail(vt0, kv_begin);
+            dma_barrier();
+            auto b_tile = [&](auto bc, int j) __attribute__((always_inline)) {
+                constexpr int B = decltype(bc)::value;
+                using Bn1 = std::integral_constant<int, (B + 1) % 3>;
+                using Bn2 = std::integral_constant<int, (B + 2) % 3>;
+                const int tj = kv_begin + j * kKvTile;
+                // phase 2j+1: load V(j+2); QK(j)
+                dma_v(vt(Bn2{}), tj + 2 * kKvTile);
+                if (j < n_tiles) qk(kt(bc), nullptr, tj, tj + kKvTile <= min_vis);
+                phase_wait();   // K(j+1)
+                dma_barrier();
+                // phase 2j+2: load K(j+3) into K(j)'s buffer; softmax+PV(j)
+                dma_k(kt(bc), tj + 3 * kKvTile);
+                if (j < n_tiles) smpv(vt(bc));
+                phase_wait();   // V(j+1)
+                if (j + 1 == n_tiles - 1) fix_v_tail(vt(Bn1{}), tj + kKvTile);
+                dma_barrier();
+            };
+            for (int j = 0; j < n_tiles; j += 3) {
+                b_tile(B0{}, j);
+                b_tile(B1{}, j + 1);
+                b_tile(B2{}, j + 2);
+            }
+        }
+        // no load may still be writing LDS when the workgroup moves on
+        wait_vmcnt<0>();
     }
 
     // ---- epilogue.  l_run holds this half-wave's keys only; the column's
