@@ -265,23 +265,37 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, Til
         tok = ti < tile.count ? tile.first + ti : -1;
         load_token();
     } else if (wave == 0) {
+        // eight 64-entry chunks of token_row in flight per round
         int found = 0;
-        for (int base = tile.first; base <= tile.last && found < tile.count; base += 64) {
-            const int i = base + lane;
-            const bool hit = (i <= tile.last) && a.token_row[i] == tile.row;
-            const uint64_t mask = __ballot(hit);
-            const int before = __popcll(mask & ((1ull << lane) - 1ull));
-            if (hit && found + before < tile.count) sm.tok[found + before] = i;
-            found += __popcll(mask);
+        for (int base = tile.first; base <= tile.last && found < tile.count; base += 512) {
+            int rw[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int i = base + 64 * k + lane;
+                rw[k] = i <= tile.last ? a.token_row[i] : -1;
+            }
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int i = base + 64 * k + lane;
+                const bool hit = i <= tile.last && rw[k] == tile.row;
+                const uint64_t mask = __ballot(hit);
+                const int before = __popcll(mask & ((1ull << lane) - 1ull));
+                if (hit && found + before < tile.count) sm.tok[found + before] = i;
+                found += __popcll(mask);
+            }
         }
     }
     if (tid < n_pages) sm_pages[tid] = pt0;
     for (int i = tid + kThreads; i < n_pages; i += kThreads) sm_pages[i] = UNIFIED ? page_base + i : bt[page_base + i];
     __syncthreads();
-    if (!tile.dense) {
-        tok = ti < tile.count ? sm.tok[ti] : -1;
-        load_token();
-    }
+    // a tile found by the scan: its tokens' metadata and Q are loaded once
+    // the first K/V loads are out
+    auto load_scanned_token = [&]() __attribute__((always_inline)) {
+        if (!tile.dense) {
+            tok = ti < tile.count ? sm.tok[ti] : -1;
+            load_token();
+        }
+    };
 
     u32x4 qb[KS];   // Q operands, made once the first tile's loads are out
 
@@ -745,6 +759,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, Til
         // (one tile) ahead of their LDS stores and are clamped onto the last
         // tile past the end, so every phase issues the same loads.  K(j) is
         // stored in the phase before its first use, V(j) likewise.
+        load_scanned_token();
         StagingK<D> stk;
         StagingV<D> stv;
         if constexpr (ONE_PAGE) {
@@ -833,12 +848,13 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, Til
             wait_vmcnt<3 * DmaTile<D>::PER>();
             __builtin_amdgcn_sched_barrier(0);
         };
-        n_vis = tok >= 0 ? min(tok_kv_len, tok_pos + 1) : 0;
         dma_k(kt0, kv_begin);
         dma_v(vt0, kv_begin);
         dma_k(kt1, kv_begin + kKvTile);
         dma_v(vt1, kv_begin + kKvTile);
+        load_scanned_token();
         make_q();
+        n_vis = tok >= 0 ? min(tok_kv_len, tok_pos + 1) : 0;
         phase_wait();   // G(0) = K(0)
         dma_barrier();
         if (wgroup == 0) {
@@ -896,6 +912,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, Til
         }
         // no load may still be writing LDS when the workgroup moves on
         wait_vmcnt<0>();
+    } else {
+        load_scanned_token();   // no keys: the rows are written as zeros
     }
 
     // ---- epilogue.  l_run holds this half-wave's keys only; the column's
@@ -979,10 +997,23 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, Til
     if (!sm.last) return;
     if (tid == 0) __hip_atomic_store(a.counters + grp, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
+    // Fold the splits in ascending order, two per round trip, this one's own
+    // partial re-read like the others, so the result does not depend on which
+    // split finishes last.  The running maximum M moves up as splits arrive
+    // (acc and L rescaled then), so no separate pass over the splits' m is
+    // needed; a column that no split saw (padding) keeps M = -inf: weights 0.
     float M = -INFINITY;
     float L = 0.0f;
     auto fold = [&](const u32x2& ml, const u32x4 (&x)[NP]) __attribute__((always_inline)) {
-        const float w = M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(__uint_as_float(ml[0]) - M);
+        const float m = __uint_as_float(ml[0]);
+        if (m > M) {
+            const float r = M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(M - m);
+            L *= r;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) acc[db] *= r;
+            M = m;
+        }
+        const float w = M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - M);
         const float wl = w * __uint_as_float(ml[1]);
         L += wl;
 #pragma unroll
@@ -998,20 +1029,6 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, Til
     for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[db][r] = 0.0f;
-    // the maximum over the splits' m (four splits' loads in flight at a
-    // time), then the splits folded in ascending order, two per round trip,
-    // this one's own partial re-read like the others, so the result does not
-    // depend on which split finishes last; a column that no split saw
-    // (padding) keeps M = -inf: weights 0
-#pragma unroll 1
-    for (int sp0 = 0; sp0 < nsp; sp0 += 4) {
-        u32x2 ml[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-            ml[u] = __builtin_amdgcn_raw_buffer_load_b64(rml, ml_off(min(sp0 + u, nsp - 1)), 0, kCoherent);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) M = fmaxf(M, __uint_as_float(ml[u][0]));
-    }
 #pragma unroll 1
     for (int sp = 0; sp < nsp; sp += 2) {
         const int sp1 = min(sp + 1, nsp - 1);
