@@ -17,10 +17,11 @@
 // * K and V tiles of 64 keys live in LDS (XOR swizzled in 16-byte units so
 //   the MFMA operand reads are free of bank conflicts) and are shared by the
 //   8 waves.  They are loaded global -> LDS directly (global_load_lds, the
-//   swizzle applied on the source side), triple buffered, each tile four
-//   barrier phases before its first use, with no staging registers and no
-//   LDS stores.  MFMA operands are read from LDS a k-step or two ahead of
-//   their use.  When the page size is a multiple of 64 a tile never crosses
+//   swizzle applied on the source side), triple buffered, with no staging
+//   registers and no LDS stores; each tile is loaded by the wave group that
+//   runs the (shorter) score half of a phase, three phases before its first
+//   use.  MFMA operands are read from LDS a k-step or two ahead of their
+//   use.  When the page size is a multiple of 64 a tile never crosses
 //   a page, and its addresses are one scalar page base plus fixed per-thread
 //   offsets.  (The unified-span mode stages tiles through registers, double
 //   buffered, since its V store zeroes free cells anywhere in a tile.)
@@ -134,12 +135,14 @@ __device__ __forceinline__ void dma_barrier() {
     asm volatile("" ::: "memory");
 }
 
-// K or V tile moved by LDS-direct loads: 16-byte chunks per tile and per thread
+// K or V tile moved by LDS-direct loads, all of it by one wave group (half
+// the workgroup): 16-byte chunks per tile and per thread of the group
 template <int D>
 struct DmaTile {
+    static constexpr int GT = kThreads / 2;
     static constexpr int CH = kKvTile * D / 8;
-    static constexpr int PER = CH / kThreads;
-    static_assert(PER * kThreads == CH, "a tile is a whole number of chunks per thread");
+    static constexpr int PER = CH / GT;
+    static_assert(PER * GT == CH, "a tile is a whole number of chunks per thread");
 };
 
 // score row i of a 32-key block <-> key offset (bits 2 and 3 swapped)
@@ -466,15 +469,18 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, Til
         }
     };
 
-    // ---- paged mode: LDS-direct tile loads.  One global_load_lds_dwordx4
-    // moves 16 bytes per lane into 64 consecutive 16-byte LDS chunks at a
-    // wave-uniform base, so the swizzle is applied on the source side: LDS
-    // chunk p = tid + kThreads*i of a tile receives the logical chunk that
-    // the swizzled layout keeps at p.  The chunk column a lane fetches is the
-    // same for every i; only the key (K) or value row (V) moves with i.
-    const int ck = (tid % CPR) ^ kswz<D>(tid / CPR);   // K: chunk of the key row
-    const int cv = (tid & 7) ^ vswz(tid >> 3);          // V: 8-key run of the value row
-    const int wbase = __builtin_amdgcn_readfirstlane(wave) * 64;
+    // ---- paged mode: LDS-direct tile loads, each tile by the four waves of
+    // one group.  One global_load_lds_dwordx4 moves 16 bytes per lane into 64
+    // consecutive 16-byte LDS chunks at a wave-uniform base, so the swizzle is
+    // applied on the source side: LDS chunk p = tg + GT*i of a tile (tg = the
+    // thread's index in its group) receives the logical chunk that the
+    // swizzled layout keeps at p.  The chunk column a lane fetches is the same
+    // for every i; only the key (K) or value row (V) moves with i.
+    constexpr int GT = DmaTile<D>::GT;
+    const int tg = tid & (GT - 1);
+    const int ck = (tg % CPR) ^ kswz<D>(tg / CPR);   // K: chunk of the key row
+    const int cv = (tg & 7) ^ vswz(tg >> 3);          // V: 8-key run of the value row
+    const int wbase = (__builtin_amdgcn_readfirstlane(wave) & 3) * 64;
     auto dma16 = [&](const uint16_t* src, u32x4* dst) __attribute__((always_inline)) {
         __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
     };
@@ -488,16 +494,15 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, Til
             const uint16_t* kb = kc + page * page_elems + (k_head_off + (t0 & (P - 1)) * D + 8 * ck);
 #pragma unroll
             for (int i = 0; i < DmaTile<D>::PER; ++i) {
-                const int key = min(tid / CPR + (kThreads / CPR) * i, kmax);
-                dma16(kb + key * D, dst + kThreads * i + wbase);
+                const int key = min(tg / CPR + (GT / CPR) * i, kmax);
+                dma16(kb + key * D, dst + GT * i + wbase);
             }
         } else {
 #pragma unroll
             for (int i = 0; i < DmaTile<D>::PER; ++i) {
-                const int t = t0 + min(tid / CPR + (kThreads / CPR) * i, kmax);
+                const int t = t0 + min(tg / CPR + (GT / CPR) * i, kmax);
                 const int page = sm_pages[(t >> sh) - page_base];
-                dma16(kc + page * page_elems + (k_head_off + (t & (P - 1)) * D + 8 * ck),
-                      dst + kThreads * i + wbase);
+                dma16(kc + page * page_elems + (k_head_off + (t & (P - 1)) * D + 8 * ck), dst + GT * i + wbase);
             }
         }
     };
@@ -514,8 +519,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, Til
                                   8 * (c & 3));
 #pragma unroll
             for (int i = 0; i < DmaTile<D>::PER; ++i) {
-                const int d = (tid >> 3) + (kThreads / 8) * i;
-                dma16(vb + d * kVSlotTile, dst + kThreads * i + wbase);
+                const int d = (tg >> 3) + (GT / 8) * i;
+                dma16(vb + d * kVSlotTile, dst + GT * i + wbase);
             }
         } else {
             // keys tb..tb+7 (8-aligned, below kv_end) lie in one slot block
@@ -527,8 +532,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, Til
                                     (k_head_off + (int64_t)(vslot & ~(VT - 1)) * D + (vslot & (VT - 1)));
 #pragma unroll
             for (int i = 0; i < DmaTile<D>::PER; ++i) {
-                const int d = (tid >> 3) + (kThreads / 8) * i;
-                dma16(vbase + d * VT, dst + kThreads * i + wbase);
+                const int d = (tg >> 3) + (GT / 8) * i;
+                dma16(vbase + d * VT, dst + GT * i + wbase);
             }
         }
     };
@@ -544,10 +549,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, Til
                 mk[w] = (2 * w < nvalid ? 0x0000ffffu : 0u) | (2 * w + 1 < nvalid ? 0xffff0000u : 0u);
 #pragma unroll
             for (int i = 0; i < DmaTile<D>::PER; ++i) {
-                u32x4 x = vt[kThreads * i + tid];
+                u32x4 x = vt[GT * i + tg];
 #pragma unroll
                 for (int w = 0; w < 4; ++w) x[w] &= mk[w];
-                vt[kThreads * i + tid] = x;
+                vt[GT * i + tg] = x;
             }
         }
     };
@@ -812,22 +817,26 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, Til
         }
     } else if (n_tiles > 0) {
         // Paged mode: tiles go global -> LDS directly (global_load_lds), K and
-        // V triple buffered, so no staging registers and no LDS stores; a
-        // tile's loads are issued four phases before its first use.  The
-        // loads form one stream of groups, G(2m) = K(m) and G(2m+1) = V(m),
-        // tile m in buffer m % 3; the prologue issues G(0..3), phase p issues
-        // G(p+4) and ends with this wave's G(p+1) complete (three later groups
-        // may stay in flight), then the barrier makes every wave's G(p+1)
-        // visible before phase p+1 reads it.  G(p+4) overwrites the buffer of
-        // tile m-3, whose last reader ran in phase p-1 or earlier.  Loads
-        // past the last tile are clamped onto it (never read), so every phase
-        // issues the same loads and the wait count is the same everywhere.
-        // The loop is unrolled by three so that every buffer is a distinct
-        // LDS variable at every access: the compiler then orders an operand
-        // read only after the loads into its own buffer.  Each pass runs all
-        // three steps (up to two past the last tile only load and take their
-        // barriers): exits inside the unrolled body made the compiler drain
-        // every load (vmcnt(0)) at the top of each pass.
+        // V triple buffered (tile m in buffer m % 3), so no staging registers
+        // and no LDS stores.  Each group loads one kind of tile during its
+        // score phases, whose waves have slack, so the softmax and P.V waves
+        // issue no loads: group A loads K(j+2) in phase 2j, after QK(j), and
+        // group B loads V(j+2) in phase 2j+1, after its QK(j).  A tile is
+        // first read four phases after its loads are issued.  At the end of
+        // its softmax phase a group waits for its own tile loaded two phases
+        // before the latest (one tile's loads may stay in flight), and the
+        // barrier then publishes it to every wave: A waits for K(j+1) at the
+        // end of phase 2j+1, B for V(j+1) at the end of phase 2j+2.  A load
+        // overwrites the buffer of tile m-3, whose last reader ran in an
+        // earlier phase.  Loads past the last tile are clamped onto it (never
+        // read), so every pass issues the same loads and the wait count is
+        // the same everywhere.  The loop is unrolled by three so that every
+        // buffer is a distinct LDS variable at every access: the compiler
+        // then orders an operand read only after the loads into its own
+        // buffer.  Each pass runs all three steps (up to two past the last
+        // tile only load and take their barriers): exits inside the unrolled
+        // body made the compiler drain every load (vmcnt(0)) at the top of
+        // each pass.
         auto kt = [&](auto bc) __attribute__((always_inline)) -> u32x4* {
             if constexpr (decltype(bc)::value == 0) return kt0;
             else if constexpr (decltype(bc)::value == 1) return kt1;
@@ -841,35 +850,36 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, Til
         using B0 = std::integral_constant<int, 0>;
         using B1 = std::integral_constant<int, 1>;
         using B2 = std::integral_constant<int, 2>;
-        // end of a phase: this wave's loads issued before the last three
-        // groups are complete (and, for the last tile's V, its tail zeroed)
+        // end of a softmax phase: this wave's loads but the latest tile's
+        // are complete
         auto phase_wait = [&]() __attribute__((always_inline)) {
             __builtin_amdgcn_sched_barrier(0);
-            wait_vmcnt<3 * DmaTile<D>::PER>();
+            wait_vmcnt<DmaTile<D>::PER>();
             __builtin_amdgcn_sched_barrier(0);
         };
-        dma_k(kt0, kv_begin);
-        dma_v(vt0, kv_begin);
-        dma_k(kt1, kv_begin + kKvTile);
-        dma_v(vt1, kv_begin + kKvTile);
+        if (wgroup == 0) {
+            dma_k(kt0, kv_begin);
+            dma_k(kt1, kv_begin + kKvTile);
+        } else {
+            dma_v(vt0, kv_begin);
+            dma_v(vt1, kv_begin + kKvTile);
+        }
         load_scanned_token();
         make_q();
         n_vis = tok >= 0 ? min(tok_kv_len, tok_pos + 1) : 0;
-        phase_wait();   // G(0) = K(0)
-        dma_barrier();
         if (wgroup == 0) {
+            phase_wait();   // K(0)
+            dma_barrier();
             auto a_tile = [&](auto bc, int j) __attribute__((always_inline)) {
                 constexpr int B = decltype(bc)::value;
                 using Bn2 = std::integral_constant<int, (B + 2) % 3>;
                 const int tj = kv_begin + j * kKvTile;
-                // phase 2j: load K(j+2); QK(j)
-                dma_k(kt(Bn2{}), tj + 2 * kKvTile);
+                // phase 2j: QK(j); load K(j+2) into K(j-1)'s buffer
                 if (j < n_tiles) qk(kt(bc), nullptr, tj, tj + kKvTile <= min_vis);
-                phase_wait();   // V(j)
-                if (j == n_tiles - 1) fix_v_tail(vt(bc), tj);
+                __builtin_amdgcn_sched_barrier(0);
+                dma_k(kt(Bn2{}), tj + 2 * kKvTile);
                 dma_barrier();
-                // phase 2j+1: load V(j+2); softmax+PV(j)
-                dma_v(vt(Bn2{}), tj + 2 * kKvTile);
+                // phase 2j+1: softmax+PV(j)
                 if (j < n_tiles) smpv(vt(bc));
                 phase_wait();   // K(j+1)
                 dma_barrier();
@@ -882,8 +892,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, Til
             // phase 2n: the other group's last softmax+PV
             dma_barrier();
         } else {
-            // phase 0: the other group's first QK; load K(2)
-            dma_k(kt2, kv_begin + 2 * kKvTile);
+            dma_barrier();
+            // phase 0: the other group's first QK
             phase_wait();   // V(0)
             if (n_tiles == 1) fix_v_tail(vt0, kv_begin);
             dma_barrier();
@@ -892,13 +902,12 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, Til
                 using Bn1 = std::integral_constant<int, (B + 1) % 3>;
                 using Bn2 = std::integral_constant<int, (B + 2) % 3>;
                 const int tj = kv_begin + j * kKvTile;
-                // phase 2j+1: load V(j+2); QK(j)
-                dma_v(vt(Bn2{}), tj + 2 * kKvTile);
+                // phase 2j+1: QK(j); load V(j+2) into V(j-1)'s buffer
                 if (j < n_tiles) qk(kt(bc), nullptr, tj, tj + kKvTile <= min_vis);
-                phase_wait();   // K(j+1)
+                __builtin_amdgcn_sched_barrier(0);
+                dma_v(vt(Bn2{}), tj + 2 * kKvTile);
                 dma_barrier();
-                // phase 2j+2: load K(j+3) into K(j)'s buffer; softmax+PV(j)
-                dma_k(kt(bc), tj + 3 * kKvTile);
+                // phase 2j+2: softmax+PV(j)
                 if (j < n_tiles) smpv(vt(bc));
                 phase_wait();   // V(j+1)
                 if (j + 1 == n_tiles - 1) fix_v_tail(vt(Bn1{}), tj + kKvTile);
