@@ -106,15 +106,31 @@ def decode_sources_sha256():
 
 
 PREFILL_MFMA_FILE = os.path.join(ROOT, "profiles", "prefill_kernel_mfma_busy_8x16k.txt")
+PREFILL_SOURCES = [os.path.join(ROOT, "paged_kv_cache_185_amd", "csrc", f)
+                   for f in ("prefill.hip", "api.cpp", "pa_internal.h")]
+
+
+def prefill_sources_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    for f in PREFILL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
 
 
 def prefill_mfma_busy():
     """MFMA busy fractions of the prefill kernel from the committed counter
-    summary (per-launch, one dispatch at a time), or None without one."""
+    summary (per-launch, one dispatch at a time), or None without one or when
+    the kernel or its launch planning (prefill.hip, api.cpp, pa_internal.h)
+    has changed since the counters were taken."""
     import re
     try:
         with open(PREFILL_MFMA_FILE) as fh:
             text = fh.read()
+        sha = re.search(r"^prefill_sources_sha256:\s*([0-9a-f]+)", text, re.M)
+        if not sha or sha.group(1) != prefill_sources_sha256():
+            return None
         fr = [float(x) for x in re.findall(r"MFMA busy fraction\s+([0-9.]+)", text)]
         own = re.search(r"so ([0-9.]+) of the cycles of the SIMDs it runs on", text)
         return {"automatic_split_launch_all_simds": fr[0], "unsplit_launch_all_simds": fr[1],
