@@ -484,6 +484,25 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, Til
     auto dma16 = [&](const uint16_t* src, u32x4* dst) __attribute__((always_inline)) {
         __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
     };
+    // one-page tiles: the tile's K or V block of this head as a buffer
+    // resource (built once per tile in scalar registers), and one load of it
+    // with a per-lane 32-bit byte offset
+    auto tile_rsrc = [&](const uint16_t* cache, int t0) __attribute__((always_inline)) {
+        const int page = __builtin_amdgcn_readfirstlane(sm_pages[(t0 >> sh) - page_base]);
+        const uint16_t* base = cache + page * page_elems + (k_head_off + (int64_t)(t0 & (P - 1)) * D);
+        return __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, 0x7fffffff, 0x00020000);
+    };
+    auto dma_kb = [&](u32x4* dst, __amdgpu_buffer_rsrc_t r, int t0, int i) __attribute__((always_inline)) {
+        const int key = min(tg / CPR + (GT / CPR) * i, min(kKvTile - 1, kv_end - 1 - t0));
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(dst + GT * i + wbase), 16,
+                                                 (key * D + 8 * ck) * 2, 0, 0, 0);
+    };
+    auto dma_vb = [&](u32x4* dst, __amdgpu_buffer_rsrc_t r, int t0, int i) __attribute__((always_inline)) {
+        const int c = min(cv, (kv_end - 1 - t0) >> 3);
+        const int d = (tg >> 3) + (GT / 8) * i;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(dst + GT * i + wbase), 16,
+                                                 ((c >> 2) * (kVSlotTile * D) + d * kVSlotTile + 8 * (c & 3)) * 2, 0, 0, 0);
+    };
     auto dma_k = [&](u32x4* dst, int t0_req) __attribute__((always_inline)) {
         const int t0 = min(t0_req, last_t0);
         // rows at or past the visible end are fetched from the last visible
@@ -581,8 +600,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, Til
     // half (exp, P.V), which is the longer chain of a phase (measured 1.4%
     // faster than in the softmax half).  K operands are read from LDS two
     // k-steps ahead of their MFMAs, and the two 32-key blocks alternate so
-    // consecutive MFMAs are independent.
-    auto qk = [&](const u32x4* kt, const int32_t* kcode, int t0, bool full) __attribute__((always_inline)) {
+    // consecutive MFMAs are independent.  mid(ks) runs after k-step ks (the
+    // phase's tile loads go there).
+    auto qk = [&](const u32x4* kt, const int32_t* kcode, int t0, bool full, auto&& mid) __attribute__((always_inline)) {
         const int krow0 = kappa(col);
         const int krow1 = 32 + kappa(col);
         auto kread = [&](int ks, int krow) __attribute__((always_inline)) {
@@ -612,6 +632,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, Til
                 s[0] = mfma32(ka[ks % R], qb[ks], s[0]);
                 s[1] = mfma32(kb1[ks % R], qb[ks], s[1]);
             }
+            __builtin_amdgcn_sched_barrier(0);
+            mid(ks);
             __builtin_amdgcn_sched_barrier(0);
         }
         if constexpr (UNIFIED) {
@@ -785,7 +807,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, Til
                 // phase 2j: V(j) -> LDS; QK(j)
                 store_v(j & 1, stv);
                 load_v(tj + kKvTile, stv);
-                qk(ss.k[j & 1], ss.kcode[j & 1], tj, false);
+                qk(ss.k[j & 1], ss.kcode[j & 1], tj, false, [](int) {});
                 lds_barrier();
                 // phase 2j+1: K(j+1) -> LDS; softmax+PV(j)
                 store_k((j + 1) & 1, stk);
@@ -806,7 +828,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, Til
                 // phase 2j+1: K(j+1) -> LDS; QK(j)
                 store_k((j + 1) & 1, stk);
                 load_k(tj + 2 * kKvTile, stk);
-                qk(ss.k[j & 1], ss.kcode[j & 1], tj, false);
+                qk(ss.k[j & 1], ss.kcode[j & 1], tj, false, [](int) {});
                 lds_barrier();
                 // phase 2j+2: V(j+1) -> LDS; softmax+PV(j)
                 store_v((j + 1) & 1, stv);
@@ -819,9 +841,14 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, Til
         // Paged mode: tiles go global -> LDS directly (global_load_lds), K and
         // V triple buffered (tile m in buffer m % 3), so no staging registers
         // and no LDS stores.  Each group loads one kind of tile during its
-        // score phases, whose waves have slack, so the softmax and P.V waves
-        // issue no loads: group A loads K(j+2) in phase 2j, after QK(j), and
-        // group B loads V(j+2) in phase 2j+1, after its QK(j).  A tile is
+        // score phases, so the softmax and P.V waves issue no loads: group A
+        // loads K(j+2) in phase 2j, during QK(j), and group B loads V(j+2) in
+        // phase 2j+1, during its QK(j).  A compute unit's vector-memory path
+        // takes one of these 1 KiB loads every ~15-19 cycles, so a wave that
+        // issues into a burst of its neighbours' loads waits; with one-page
+        // tiles the loads go out one after every other score k-step (a buffer
+        // resource per tile, one 32-bit offset per lane and load), otherwise
+        // after the score MFMAs.  A tile is
         // first read four phases after its loads are issued.  At the end of
         // its softmax phase a group waits for its own tile loaded two phases
         // before the latest (one tile's loads may stay in flight), and the
@@ -875,9 +902,23 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, Til
                 using Bn2 = std::integral_constant<int, (B + 2) % 3>;
                 const int tj = kv_begin + j * kKvTile;
                 // phase 2j: QK(j); load K(j+2) into K(j-1)'s buffer
-                if (j < n_tiles) qk(kt(bc), nullptr, tj, tj + kKvTile <= min_vis);
-                __builtin_amdgcn_sched_barrier(0);
-                dma_k(kt(Bn2{}), tj + 2 * kKvTile);
+                constexpr int STEP = KS / DmaTile<D>::PER;
+                if constexpr (ONE_PAGE) {
+                    const int tq = min(tj + 2 * kKvTile, last_t0);
+                    const auto rk = tile_rsrc(kc, tq);
+                    if (j < n_tiles) {
+                        qk(kt(bc), nullptr, tj, tj + kKvTile <= min_vis, [&](int ks) __attribute__((always_inline)) {
+                            if (ks % STEP == 0) dma_kb(kt(Bn2{}), rk, tq, ks / STEP);
+                        });
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < DmaTile<D>::PER; ++i) dma_kb(kt(Bn2{}), rk, tq, i);
+                    }
+                } else {
+                    if (j < n_tiles) qk(kt(bc), nullptr, tj, tj + kKvTile <= min_vis, [](int) {});
+                    __builtin_amdgcn_sched_barrier(0);
+                    dma_k(kt(Bn2{}), tj + 2 * kKvTile);
+                }
                 dma_barrier();
                 // phase 2j+1: softmax+PV(j)
                 if (j < n_tiles) smpv(vt(bc));
@@ -903,9 +944,23 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, Til
                 using Bn2 = std::integral_constant<int, (B + 2) % 3>;
                 const int tj = kv_begin + j * kKvTile;
                 // phase 2j+1: QK(j); load V(j+2) into V(j-1)'s buffer
-                if (j < n_tiles) qk(kt(bc), nullptr, tj, tj + kKvTile <= min_vis);
-                __builtin_amdgcn_sched_barrier(0);
-                dma_v(vt(Bn2{}), tj + 2 * kKvTile);
+                constexpr int STEP = KS / DmaTile<D>::PER;
+                if constexpr (ONE_PAGE) {
+                    const int tq = min(tj + 2 * kKvTile, last_t0);
+                    const auto rv = tile_rsrc(vc, tq);
+                    if (j < n_tiles) {
+                        qk(kt(bc), nullptr, tj, tj + kKvTile <= min_vis, [&](int ks) __attribute__((always_inline)) {
+                            if (ks % STEP == 0) dma_vb(vt(Bn2{}), rv, tq, ks / STEP);
+                        });
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < DmaTile<D>::PER; ++i) dma_vb(vt(Bn2{}), rv, tq, i);
+                    }
+                } else {
+                    if (j < n_tiles) qk(kt(bc), nullptr, tj, tj + kKvTile <= min_vis, [](int) {});
+                    __builtin_amdgcn_sched_barrier(0);
+                    dma_v(vt(Bn2{}), tj + 2 * kKvTile);
+                }
                 dma_barrier();
                 // phase 2j+2: softmax+PV(j)
                 if (j < n_tiles) smpv(vt(bc));
