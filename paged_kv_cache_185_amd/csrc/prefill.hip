@@ -16,15 +16,16 @@
 //   splits of that head share its K/V through that XCD's L2.
 // * K and V tiles of 64 keys live in LDS (XOR swizzled in 16-byte units so
 //   the MFMA operand reads are free of bank conflicts) and are shared by the
-//   8 waves.  They are loaded global -> LDS directly (global_load_lds, the
+//   8 waves.  They are loaded global -> LDS directly (LDS-direct loads, the
 //   swizzle applied on the source side), triple buffered, with no staging
 //   registers and no LDS stores; each tile is loaded by the wave group that
-//   runs the (shorter) score half of a phase, three phases before its first
-//   use.  MFMA operands are read from LDS a k-step or two ahead of their
-//   use.  When the page size is a multiple of 64 a tile never crosses
-//   a page, and its addresses are one scalar page base plus fixed per-thread
-//   offsets.  (The unified-span mode stages tiles through registers, double
-//   buffered, since its V store zeroes free cells anywhere in a tile.)
+//   runs the score half of a phase, between its score MFMAs, three phases
+//   before the tile's first use.  MFMA operands are read from LDS a k-step
+//   or two ahead of their use.  When the page size is a multiple of 64 a
+//   tile never crosses a page: it is one buffer resource (the page's block
+//   of the head) and fixed per-thread offsets.  (The unified-span mode
+//   stages tiles through registers, double buffered, since its V store
+//   zeroes free cells anywhere in a tile.)
 // * Both products run on v_mfma_f32_32x32x16_f16 with fp32 accumulation.
 //   Scores are computed transposed, S^T = K Q^T (rows = keys, columns =
 //   queries): each lane's C registers belong to one query column, so the
@@ -305,7 +306,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, Til
     const uint16_t* kc = a.k_cache;
     const uint16_t* vc = a.v_cache;
 
-    // ---- global -> registers for one KV tile starting at key t0.  Thread
+    // ---- unified span: global -> registers for one KV tile starting at key
+    // t0 (the paged mode loads tiles straight into LDS, below).  Thread
     // tid moves the K chunks (key, c) = (id / CPR, id % CPR) and the V chunks
     // (d, c) = (id / 8, id % 8) of id = tid + kThreads*i; everything but the
     // page lookup is fixed per thread.  Loads and stores are branch-free
@@ -593,15 +595,16 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, Til
 #pragma unroll
     for (int r = 0; r < 16; ++r) negm[r] = 0.0f;
 
-    // S^T = K Q^T for the 64 keys t0..t0+63 in K buffer `buf`, then the
-    // first half of the online softmax: the mask (`full`, uniform, says every
-    // query column sees all 64 keys), the row maximum and the lazy rescale.
-    // Doing these here, in the score half of the ping-pong, shortens the other
-    // half (exp, P.V), which is the longer chain of a phase (measured 1.4%
-    // faster than in the softmax half).  K operands are read from LDS two
-    // k-steps ahead of their MFMAs, and the two 32-key blocks alternate so
-    // consecutive MFMAs are independent.  mid(ks) runs after k-step ks (the
-    // phase's tile loads go there).
+    // S^T = K Q^T for the 64 keys t0..t0+63 of K tile `kt`, then the first
+    // half of the online softmax: the mask (`full`, uniform, says every query
+    // column sees all 64 keys), the row maximum and the lazy rescale.  These
+    // sit in the score half of the ping-pong (measured 1.4% faster than in the
+    // softmax half when tiles went through registers).  With the tile loads
+    // this half is the longer one of a phase: moving the exps of the first one
+    // or two P.V k-steps into it is 1.5% and 3% slower.  K operands are read
+    // from LDS two k-steps ahead of their MFMAs, and the two 32-key blocks
+    // alternate so consecutive MFMAs are independent.  mid(ks) runs after
+    // k-step ks (the phase's tile loads go there).
     auto qk = [&](const u32x4* kt, const int32_t* kcode, int t0, bool full, auto&& mid) __attribute__((always_inline)) {
         const int krow0 = kappa(col);
         const int krow1 = 32 + kappa(col);
@@ -701,12 +704,14 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, Til
         }
     };
 
-    // Second half of the online softmax of the scores (P = exp2(s - m), row
-    // sums) and O^T += V^T P^T with V buffer `buf`.
+    // Second half of the online softmax of the scores (P = exp2(s), the
+    // scores being relative to the running max already; row sums) and
+    // O^T += V^T P^T with V tile `vt`.
     auto smpv = [&](const u32x4* vt) __attribute__((always_inline)) {
-        // this wave's softmax and P.V are the phase's longer chain: its
-        // instructions go first when both waves of a SIMD can issue (measured
-        // 1% faster; priority on the score MFMAs instead is 2.5% slower)
+        // raised wave priority: this wave's instructions go first when both
+        // waves of a SIMD can issue (measured 1% faster, with register-staged
+        // and with LDS-direct tiles; priority on the score MFMAs instead was
+        // 2.5% slower)
         __builtin_amdgcn_s_setprio(1);
         // 16 keys per k-step: P is made just before its MFMAs and the V
         // operands of the next k-step are read from LDS meanwhile
