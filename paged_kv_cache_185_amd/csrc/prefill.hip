@@ -136,6 +136,11 @@ __device__ __forceinline__ void dma_barrier() {
     asm volatile("" ::: "memory");
 }
 
+// Words 2 and 3 of the raw buffer resources used here: up to 2 GiB of
+// records, and data format 32 bit (bits 18:15 of word 3 = 4), other fields 0.
+constexpr int kRawRecords = 0x7fffffff;
+constexpr int kRawWord3 = 0x00020000;
+
 // K or V tile moved by LDS-direct loads, all of it by one wave group (half
 // the workgroup): 16-byte chunks per tile and per thread of the group
 template <int D>
@@ -492,7 +497,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, Til
     auto tile_rsrc = [&](const uint16_t* cache, int t0) __attribute__((always_inline)) {
         const int page = __builtin_amdgcn_readfirstlane(sm_pages[(t0 >> sh) - page_base]);
         const uint16_t* base = cache + page * page_elems + (k_head_off + (int64_t)(t0 & (P - 1)) * D);
-        return __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, 0x7fffffff, 0x00020000);
+        return __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, kRawRecords, kRawWord3);
     };
     auto dma_kb = [&](u32x4* dst, __amdgpu_buffer_rsrc_t r, int t0, int i) __attribute__((always_inline)) {
         const int key = min(tg / CPR + (GT / CPR) * i, min(kKvTile - 1, kv_end - 1 - t0));
@@ -889,15 +894,26 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, Til
             wait_vmcnt<DmaTile<D>::PER>();
             __builtin_amdgcn_sched_barrier(0);
         };
-        if (wgroup == 0) {
-            dma_k(kt0, kv_begin);
-            dma_k(kt1, kv_begin + kKvTile);
+        // the first tile, the token metadata and Q (a tile found by the scan;
+        // a contiguous tile loaded them before the page table), then the
+        // second tile: the in-order wait for Q in make_q leaves the second
+        // tile's loads in flight.  Each path makes Q on its own, so that the
+        // compiler counts its own loads exactly instead of draining them all
+        // where the paths join.
+        if (wgroup == 0) dma_k(kt0, kv_begin);
+        else dma_v(vt0, kv_begin);
+        auto second_tile = [&]() __attribute__((always_inline)) {
+            if (wgroup == 0) dma_k(kt1, kv_begin + kKvTile);
+            else dma_v(vt1, kv_begin + kKvTile);
+        };
+        if (!tile.dense) {
+            load_scanned_token();
+            second_tile();
+            make_q();
         } else {
-            dma_v(vt0, kv_begin);
-            dma_v(vt1, kv_begin + kKvTile);
+            second_tile();
+            make_q();
         }
-        load_scanned_token();
-        make_q();
         n_vis = tok >= 0 ? min(tok_kv_len, tok_pos + 1) : 0;
         if (wgroup == 0) {
             phase_wait();   // K(0)
@@ -1034,9 +1050,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, Til
     // 16) makes the accesses coherent across the XCDs' L2s
     constexpr int kCoherent = 16;
     const __amdgpu_buffer_rsrc_t racc = __builtin_amdgcn_make_buffer_rsrc(
-        a.part_acc + slot0 * NP * kThreads * 4, 0, 0x7fffffff, 0x00020000);
+        a.part_acc + slot0 * NP * kThreads * 4, 0, kRawRecords, kRawWord3);
     const __amdgpu_buffer_rsrc_t rml = __builtin_amdgcn_make_buffer_rsrc(
-        a.part_ml + slot0 * kThreads * 2, 0, 0x7fffffff, 0x00020000);
+        a.part_ml + slot0 * kThreads * 2, 0, kRawRecords, kRawWord3);
     auto acc_off = [&](int sp, int j) __attribute__((always_inline)) { return ((sp * NP + j) * kThreads + tid) * 16; };
     auto ml_off = [&](int sp) __attribute__((always_inline)) { return (sp * kThreads + tid) * 8; };
     {
